@@ -1,0 +1,70 @@
+"""Build libtwell.so (HIP kernels for gfx950 + the C ABI) in-tree.
+
+Every source is compiled by hipcc for gfx950 only, in parallel, then linked
+into activation_sparse_ffn_03_amd/libtwell.so. Objects go to _build/ at the
+repository root.
+"""
+from __future__ import annotations
+
+import concurrent.futures
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD_DIR = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libtwell.so")
+
+ARCH = "gfx950"
+HIP_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",
+    # keep the compiler from forming packed fp32 (v_pk_*_f32) instructions
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", INCLUDE, "-I", CSRC,
+]
+SOURCES = ["twell_host.cpp", "twell_api.hip", "trace.hip", "scan.hip", "gate_pack.hip", "fused_fwd.hip", "route.hip", "bwd.hip"]
+
+
+def _hipcc() -> str:
+    for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found")
+
+
+def _compile(src: str, verbose: bool) -> str:
+    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+    cmd = [_hipcc(), *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    if src.endswith(".cpp"):
+        cmd = [_hipcc(), "-x", "hip", *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    out = "\n".join(line for line in (r.stdout + r.stderr).splitlines()
+                    if "packed-fp32-ops" not in line)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{out}")
+    if verbose and out.strip():
+        print(out, file=sys.stderr)
+    return obj
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source for gfx950 and link libtwell.so; returns its path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    jobs = min(len(SOURCES), max(1, min(16, os.cpu_count() or 1)))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+    tmp = LIB + ".tmp"
+    r = subprocess.run([_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,103 @@
+// Stage 3a: hybrid row router for training.
+//
+// "Sakana AI and NVIDIA present TwELL" (edge.aivizor.me), second paragraph:
+// for training a hybrid format routes rows dynamically either into a compact
+// ELL matrix (sparse rows) or into a dense backup for overflows; fourth
+// paragraph: the maximum nonzeros per row can far exceed the mean.
+//
+// Readings: row_nnz = sum of the row's true tile counts; a row is dense iff
+// row_nnz > K or it overflowed a TwELL tile; ELL positions follow ascending
+// global column (tile by tile, slot by slot); dense rows are listed in
+// ascending order.
+//
+// Kernels
+//   route_rows     thread per row: row_nnz, is_dense, and the ELL entries of
+//                  ELL rows (vals, global cols, saved a).
+//   launch_compact ascending dense-row list + capacity status.
+//   route_dense_h  thread per (dense row, column): dense activation rows,
+//                  rebuilt from TwELL slots or copied from the overflow rows.
+#include "twell_device.h"
+#include "twell_kernels.h"
+#include "twell_trace.h"
+
+namespace twell {
+namespace {
+
+template <typename TS>
+__global__ __launch_bounds__(256) void route_rows(RouteArgs a) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= a.N) return;
+  const int64_t N = a.N;
+  int32_t nnz = 0;
+  for (int j = 0; j < a.n_tiles; ++j) nnz += a.counts[(size_t)j * N + i];
+  const bool dense = nnz > a.row_cap || a.ovf_flag[i] != 0;
+  a.row_nnz[i] = nnz;
+  a.is_dense[i] = dense ? 1 : 0;
+  if (dense) return;
+  const TS* vals = reinterpret_cast<const TS*>(a.vals);
+  TS* ev = reinterpret_cast<TS*>(a.ell_vals);
+  int k = 0;
+  for (int j = 0; j < a.n_tiles; ++j) {
+    const int cnt = a.counts[(size_t)j * N + i];
+    for (int s = 0; s < cnt; ++s, ++k) {
+      const size_t src = ((size_t)j * a.slots + s) * N + i;
+      const size_t dst = (size_t)k * N + i;
+      ev[dst] = vals[src];
+      a.ell_cols[dst] = j * a.tile_n + a.cols[src];
+      a.ell_a[dst] = a.a_save[src];
+    }
+  }
+}
+
+// Dense row o, column c: from the overflow row copy when the row overflowed
+// (located by binary search in the ascending overflow list), else from the
+// TwELL slots of its tile.
+template <typename TS>
+__global__ __launch_bounds__(256) void route_dense_h(RouteArgs a) {
+  const int cb = (a.F + 255) / 256;
+  const int o = blockIdx.x / cb;
+  if (o >= a.dense_cap || o >= *a.n_dense) return;
+  const int c = (blockIdx.x % cb) * 256 + threadIdx.x;
+  if (c >= a.F) return;
+  const int64_t N = a.N;
+  const int64_t i = a.dense_rows[o];
+  TS* out = reinterpret_cast<TS*>(a.dense_h) + (size_t)o * a.F;
+  const TS* vals = reinterpret_cast<const TS*>(a.vals);
+  TS h = TS(0);
+  if (a.ovf_flag[i]) {
+    const int n = min(*a.n_ovf, a.ovf_cap);
+    int lo = 0, hi = n;  // first position with ovf_rows[pos] >= i
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (a.ovf_rows[mid] < i) lo = mid + 1; else hi = mid;
+    }
+    if (lo < n && a.ovf_rows[lo] == i) h = reinterpret_cast<const TS*>(a.ovf_h)[(size_t)lo * a.F + c];
+  } else {
+    const int j = c / a.tile_n, off = c - j * a.tile_n;
+    const int cnt = min((int)a.counts[(size_t)j * N + i], a.slots);
+    for (int s = 0; s < cnt; ++s) {
+      const size_t src = ((size_t)j * a.slots + s) * N + i;
+      if (a.cols[src] == off) h = vals[src];
+    }
+  }
+  out[c] = h;
+}
+
+template <typename TS>
+hipError_t launch_t(const RouteArgs& a, hipStream_t s) {
+  TWELL_LAUNCH("route_rows", route_rows<TS>, dim3((unsigned)((a.N + 255) / 256)), 256, 0, s, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  err = launch_compact(a.is_dense, a.N, a.dense_rows, a.dense_cap, a.n_dense, a.status, 2u /*TWELL_DEV_DENSE_CAPACITY*/, s);
+  if (err != hipSuccess || a.dense_cap == 0) return err;
+  TWELL_LAUNCH("route_dense_h", route_dense_h<TS>, dim3((unsigned)(((a.F + 255) / 256) * (int64_t)a.dense_cap)), 256, 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
+  return a.is_bf16 ? launch_t<uint16_t>(a, s) : launch_t<float>(a, s);
+}
+
+}  // namespace twell

@@ -1,0 +1,41 @@
+// Host-only shape validation and buffer / workspace size arithmetic.
+// Plain C++17 with no HIP dependency, so it can also be built and tested on
+// its own (and under sanitizers) without a GPU toolchain.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <string>
+
+#include "../../include/twell.h"
+
+namespace twell {
+
+constexpr size_t kWsAlign = 256;
+
+struct Shape {
+  int64_t N;
+  int D, F, tile_n, slots, row_cap, ovf_cap, dense_cap;
+  int n_tiles;
+  int esz;     // bytes per stored element (2 bf16, 4 fp32)
+  int G;       // column chunks of a dense row
+  int nrb;     // row blocks of the column transpose
+  int64_t nnz_max;
+};
+
+// Offsets (bytes from the workspace base) of every backward workspace array.
+struct BwdLayout {
+  size_t row_ptr, dense_pos, pair_col, coef, csc_pair, csc_row, col_ptr, blk_cnt, grp_off, part, total;
+};
+
+// Validate dims/dtype; on failure returns the status and sets *why.
+twell_status check_shape(const twell_dims* dims, int dtype, Shape* out, std::string* why);
+void compute_sizes(const Shape& s, twell_sizes* out);
+BwdLayout bwd_layout(const Shape& s);
+size_t fwd_ws_bytes(const Shape& s);
+
+// Pointer checks: null (when bytes > 0) or not 16-byte aligned.
+bool bad_ptr(const void* p, size_t bytes);
+
+}  // namespace twell

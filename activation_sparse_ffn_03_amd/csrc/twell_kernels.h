@@ -1,0 +1,135 @@
+// Internal launch interface between the C ABI (twell_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace twell {
+
+// Width of the column chunks that dense (overflow / backup) rows are split
+// into so that one long row is spread over many waves.
+constexpr int kDenseChunk = 512;
+// Rows per block of the deterministic column transpose.
+constexpr int kTransposeRows = 64;
+
+// Ascending list of the rows whose flag is set (single-workgroup
+// deterministic scan). Writes rows[0:min(count,cap)], *n_out = count and
+// *status = count > cap ? bit : 0.
+hipError_t launch_compact(const uint8_t* flag, int64_t N, int32_t* rows, int cap, int32_t* n_out,
+                          uint32_t* status, uint32_t bit, hipStream_t s);
+
+struct GateArgs {
+  int64_t N;
+  int D, F, tile_n, slots, n_tiles;
+  int is_bf16;
+  const void* x;       // [N][D]
+  const void* w;       // [F][D]
+  const float* g_in;   // pack_preact: [N][F] fp32 pre-activation (else null)
+  const float* t;      // [N]
+  void* vals;
+  uint16_t* cols;
+  uint16_t* counts;
+  uint8_t* ovf_flag;
+  int32_t* ovf_rows;
+  void* ovf_h;
+  int32_t* n_ovf;
+  uint32_t* status;
+  int ovf_cap;
+  float* g_dump;       // optional
+};
+
+hipError_t launch_gate_pack(const GateArgs& a, hipStream_t s);
+
+struct FwdArgs {
+  int64_t N;
+  int D, F, tile_n, slots, n_tiles;
+  int is_bf16;
+  const void* vals;
+  const uint16_t* cols;
+  const uint16_t* counts;
+  const int32_t* ovf_rows;
+  const void* ovf_h;
+  const int32_t* n_ovf;
+  int ovf_cap;
+  const void* x;
+  const void* w_up;
+  const void* w_down;
+  float* y;
+  float* a_save;
+  float* part;  // [ovf_cap][G][D] fp32 partial outputs of dense-row chunks
+};
+
+hipError_t launch_ffn_fwd(const FwdArgs& a, hipStream_t s);
+
+// out[rows[o]] = sum_g part[o][g] for o < min(*n_rows, cap), part [cap][G][D].
+hipError_t launch_dense_reduce(const float* part, const int32_t* rows, const int32_t* n_rows, int cap, int G,
+                               int D, float* out, hipStream_t s);
+
+struct RouteArgs {
+  int64_t N;
+  int F, tile_n, slots, n_tiles, row_cap, dense_cap;
+  int is_bf16;
+  const void* vals;
+  const uint16_t* cols;
+  const uint16_t* counts;
+  const uint8_t* ovf_flag;
+  const int32_t* ovf_rows;
+  const void* ovf_h;
+  const int32_t* n_ovf;
+  int ovf_cap;
+  const float* a_save;
+  void* ell_vals;
+  int32_t* ell_cols;
+  float* ell_a;
+  int32_t* row_nnz;
+  uint8_t* is_dense;
+  int32_t* dense_rows;
+  void* dense_h;
+  int32_t* n_dense;
+  uint32_t* status;
+};
+
+hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+
+struct BwdWorkspace {
+  int32_t* row_ptr;    // [N+1]
+  int32_t* dense_pos;  // [N] position in dense_rows or -1
+  int32_t* pair_col;   // [nnz_max]
+  float4* coef;        // [nnz_max] (z, da, dg, 0)
+  int32_t* csc_pair;   // [nnz_max]
+  int32_t* csc_row;    // [nnz_max]
+  int32_t* col_ptr;    // [F+1]
+  int32_t* blk_cnt;    // [n_rb][F]
+  int32_t* grp_off;    // [dense_cap][G]
+  float* part;         // [dense_cap][G][D]
+};
+
+struct BwdArgs {
+  int64_t N;
+  int D, F, row_cap, dense_cap;
+  int is_bf16;
+  const void* ell_vals;
+  const int32_t* ell_cols;
+  const float* ell_a;
+  const int32_t* row_nnz;
+  const uint8_t* is_dense;
+  const int32_t* dense_rows;
+  const void* dense_h;
+  const int32_t* n_dense;
+  const void* x;
+  const void* dy;
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+  float lam;
+  float* dx;
+  float* dw_gate;
+  float* dw_up;
+  float* dw_down;
+  BwdWorkspace ws;
+};
+
+hipError_t launch_ffn_bwd(const BwdArgs& a, hipStream_t s);
+
+}  // namespace twell

@@ -1,0 +1,300 @@
+"""Thin Python binding of libtwell (ctypes, argument marshalling only).
+
+Every step of the computation runs in the HIP kernels of libtwell.so; this
+module only turns torch tensors into device pointers, passes the caller's
+current HIP stream, allocates caller-owned buffers with torch, and raises
+TwellError on a non-OK status. There is no fallback: if the library is not
+built, loading it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libtwell.so")
+
+BF16 = 0
+F32 = 1
+DEV_OVF_CAPACITY = 1
+DEV_DENSE_CAPACITY = 2
+
+_STATUS = {0: "TWELL_OK", 1: "TWELL_ERR_INVALID_ARG", 2: "TWELL_ERR_UNSUPPORTED", 3: "TWELL_ERR_WORKSPACE",
+           4: "TWELL_ERR_CAPACITY", 5: "TWELL_ERR_HIP"}
+
+# Every symbol include/twell.h declares.
+EXPORTS = ("twell_status_str", "twell_last_error", "twell_n_tiles", "twell_query_sizes", "twell_gate_pack",
+           "twell_pack_preact", "twell_ffn_fwd", "twell_route_hybrid", "twell_ffn_bwd", "twell_trace_start",
+           "twell_trace_stop", "twell_trace_count", "twell_trace_dropped", "twell_trace_get")
+
+
+class TwellError(RuntimeError):
+    def __init__(self, status: int, where: str, msg: str):
+        super().__init__(f"{where}: {_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("n_tokens", ctypes.c_int64), ("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32),
+                ("tile_n", ctypes.c_int32), ("slots", ctypes.c_int32), ("row_cap", ctypes.c_int32),
+                ("ovf_cap", ctypes.c_int32), ("dense_cap", ctypes.c_int32)]
+
+
+class Pack(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("vals", "cols", "counts", "ovf_flag", "ovf_rows", "ovf_h", "n_ovf", "status")]
+
+
+class Hybrid(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("ell_vals", "ell_cols", "ell_a", "row_nnz", "is_dense", "dense_rows", "dense_h", "n_dense",
+                 "status")]
+
+
+_SIZE_FIELDS = ("vals", "cols", "counts", "ovf_flag", "ovf_rows", "ovf_h", "n_ovf", "status", "ell_vals",
+                "ell_cols", "ell_a", "row_nnz", "is_dense", "dense_rows", "dense_h", "n_dense", "a_save",
+                "ws_fwd", "ws_bwd")
+
+
+class Sizes(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in _SIZE_FIELDS]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libtwell.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libtwell.so is not built at {LIB_PATH}; run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+        pd, pp, ph = ctypes.POINTER(Dims), ctypes.POINTER(Pack), ctypes.POINTER(Hybrid)
+        L.twell_status_str.restype = ctypes.c_char_p
+        L.twell_status_str.argtypes = [ctypes.c_int]
+        L.twell_last_error.restype = ctypes.c_char_p
+        L.twell_last_error.argtypes = []
+        L.twell_n_tiles.restype = i32
+        L.twell_n_tiles.argtypes = [pd]
+        L.twell_query_sizes.restype = ctypes.c_int
+        L.twell_query_sizes.argtypes = [pd, ctypes.c_int, ctypes.POINTER(Sizes)]
+        L.twell_gate_pack.restype = ctypes.c_int
+        L.twell_gate_pack.argtypes = [pd, ctypes.c_int, vp, vp, vp, pp, vp, vp]
+        L.twell_pack_preact.restype = ctypes.c_int
+        L.twell_pack_preact.argtypes = [pd, ctypes.c_int, vp, vp, pp, vp]
+        L.twell_ffn_fwd.restype = ctypes.c_int
+        L.twell_ffn_fwd.argtypes = [pd, ctypes.c_int, pp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.twell_route_hybrid.restype = ctypes.c_int
+        L.twell_route_hybrid.argtypes = [pd, ctypes.c_int, pp, vp, ph, vp]
+        L.twell_ffn_bwd.restype = ctypes.c_int
+        L.twell_ffn_bwd.argtypes = [pd, ctypes.c_int, ph, vp, vp, vp, vp, vp, f32, vp, vp, vp, vp, vp, sz, vp]
+        L.twell_trace_start.restype = ctypes.c_int
+        L.twell_trace_start.argtypes = [i32]
+        L.twell_trace_stop.restype = ctypes.c_int
+        L.twell_trace_stop.argtypes = []
+        L.twell_trace_count.restype = i32
+        L.twell_trace_count.argtypes = []
+        L.twell_trace_dropped.restype = i32
+        L.twell_trace_dropped.argtypes = []
+        L.twell_trace_get.restype = ctypes.c_int
+        L.twell_trace_get.argtypes = [i32, ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float)]
+        _lib = L
+    return _lib
+
+
+def _check(st: int, where: str) -> None:
+    if st != 0:
+        raise TwellError(st, where, lib().twell_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libtwell must be contiguous")
+    return ctypes.c_void_p(t.data_ptr()) if t.numel() else None
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def make_dims(n_tokens: int, d_model: int, d_ff: int, tile_n: int, slots: int, row_cap: int = 0,
+              ovf_cap: int = 0, dense_cap: int = 0) -> Dims:
+    return Dims(int(n_tokens), int(d_model), int(d_ff), int(tile_n), int(slots), int(row_cap), int(ovf_cap),
+                int(dense_cap))
+
+
+def n_tiles(dims: Dims) -> int:
+    return int(lib().twell_n_tiles(ctypes.byref(dims)))
+
+
+def query_sizes(dims: Dims, dtype: int) -> dict:
+    s = Sizes()
+    _check(lib().twell_query_sizes(ctypes.byref(dims), int(dtype), ctypes.byref(s)), "twell_query_sizes")
+    return {n: int(getattr(s, n)) for n in _SIZE_FIELDS}
+
+
+def storage_dtype(dtype: int) -> torch.dtype:
+    return torch.bfloat16 if dtype == BF16 else torch.float32
+
+
+@dataclass
+class TwellPack:
+    vals: torch.Tensor      # [n_t][S][N]
+    cols: torch.Tensor      # [n_t][S][N] int16 storage of uint16
+    counts: torch.Tensor    # [n_t][N]    int16 storage of uint16
+    ovf_flag: torch.Tensor  # [N] uint8
+    ovf_rows: torch.Tensor  # [ovf_cap] int32
+    ovf_h: torch.Tensor     # [ovf_cap][F]
+    n_ovf: torch.Tensor     # [1] int32
+    status: torch.Tensor    # [1] int32 storage of uint32
+
+    def struct(self) -> Pack:
+        return Pack(*[_ptr(getattr(self, n)) for n, _ in Pack._fields_])
+
+
+@dataclass
+class TwellHybrid:
+    ell_vals: torch.Tensor
+    ell_cols: torch.Tensor
+    ell_a: torch.Tensor
+    row_nnz: torch.Tensor
+    is_dense: torch.Tensor
+    dense_rows: torch.Tensor
+    dense_h: torch.Tensor
+    n_dense: torch.Tensor
+    status: torch.Tensor
+
+    def struct(self) -> Hybrid:
+        return Hybrid(*[_ptr(getattr(self, n)) for n, _ in Hybrid._fields_])
+
+
+def alloc_pack(dims: Dims, dtype: int, device="cuda") -> TwellPack:
+    query_sizes(dims, dtype)  # validates
+    N, F, S = dims.n_tokens, dims.d_ff, dims.slots
+    nt = n_tiles(dims)
+    sd = storage_dtype(dtype)
+    e = dict(device=device)
+    return TwellPack(vals=torch.empty((nt, S, N), dtype=sd, **e), cols=torch.empty((nt, S, N), dtype=torch.int16, **e),
+                     counts=torch.empty((nt, N), dtype=torch.int16, **e), ovf_flag=torch.empty(N, dtype=torch.uint8, **e),
+                     ovf_rows=torch.empty(dims.ovf_cap, dtype=torch.int32, **e),
+                     ovf_h=torch.empty((dims.ovf_cap, F), dtype=sd, **e), n_ovf=torch.empty(1, dtype=torch.int32, **e),
+                     status=torch.empty(1, dtype=torch.int32, **e))
+
+
+def alloc_hybrid(dims: Dims, dtype: int, device="cuda") -> TwellHybrid:
+    query_sizes(dims, dtype)
+    N, F, K = dims.n_tokens, dims.d_ff, dims.row_cap
+    sd = storage_dtype(dtype)
+    e = dict(device=device)
+    return TwellHybrid(ell_vals=torch.empty((K, N), dtype=sd, **e), ell_cols=torch.empty((K, N), dtype=torch.int32, **e),
+                       ell_a=torch.empty((K, N), dtype=torch.float32, **e), row_nnz=torch.empty(N, dtype=torch.int32, **e),
+                       is_dense=torch.empty(N, dtype=torch.uint8, **e),
+                       dense_rows=torch.empty(dims.dense_cap, dtype=torch.int32, **e),
+                       dense_h=torch.empty((dims.dense_cap, F), dtype=sd, **e),
+                       n_dense=torch.empty(1, dtype=torch.int32, **e), status=torch.empty(1, dtype=torch.int32, **e))
+
+
+def alloc_workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
+def gate_pack(dims: Dims, dtype: int, x, w_gate_t, t, pack: TwellPack, g_dump=None, stream=None) -> None:
+    p = pack.struct()
+    _check(lib().twell_gate_pack(ctypes.byref(dims), int(dtype), _ptr(x), _ptr(w_gate_t), _ptr(t),
+                                 ctypes.byref(p), _ptr(g_dump), _stream(stream)), "twell_gate_pack")
+
+
+def pack_preact(dims: Dims, dtype: int, g, t, pack: TwellPack, stream=None) -> None:
+    p = pack.struct()
+    _check(lib().twell_pack_preact(ctypes.byref(dims), int(dtype), _ptr(g), _ptr(t), ctypes.byref(p),
+                                   _stream(stream)), "twell_pack_preact")
+
+
+def ffn_fwd(dims: Dims, dtype: int, pack: TwellPack, x, w_up_t, w_down, y, a_save=None, ws=None,
+            stream=None) -> None:
+    p = pack.struct()
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().twell_ffn_fwd(ctypes.byref(dims), int(dtype), ctypes.byref(p), _ptr(x), _ptr(w_up_t),
+                               _ptr(w_down), _ptr(y), _ptr(a_save), _ptr(ws), nbytes, _stream(stream)),
+           "twell_ffn_fwd")
+
+
+def route_hybrid(dims: Dims, dtype: int, pack: TwellPack, a_save, hyb: TwellHybrid, stream=None) -> None:
+    p, h = pack.struct(), hyb.struct()
+    _check(lib().twell_route_hybrid(ctypes.byref(dims), int(dtype), ctypes.byref(p), _ptr(a_save),
+                                    ctypes.byref(h), _stream(stream)), "twell_route_hybrid")
+
+
+def ffn_bwd(dims: Dims, dtype: int, hyb: TwellHybrid, x, dy, w_gate_t, w_up_t, w_down, l1_lambda: float, dx,
+            dw_gate_t, dw_up_t, dw_down, ws, stream=None) -> None:
+    h = hyb.struct()
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().twell_ffn_bwd(ctypes.byref(dims), int(dtype), ctypes.byref(h), _ptr(x), _ptr(dy), _ptr(w_gate_t),
+                               _ptr(w_up_t), _ptr(w_down), ctypes.c_float(l1_lambda), _ptr(dx), _ptr(dw_gate_t),
+                               _ptr(dw_up_t), _ptr(dw_down), _ptr(ws), nbytes, _stream(stream)), "twell_ffn_bwd")
+
+
+def trace_start(capacity: int = 4096) -> None:
+    _check(lib().twell_trace_start(int(capacity)), "twell_trace_start")
+
+
+def trace_stop() -> list:
+    """Stop tracing and return [(kernel_name, ms), ...] for every recorded launch."""
+    L = lib()
+    _check(L.twell_trace_stop(), "twell_trace_stop")
+    out = []
+    for i in range(int(L.twell_trace_count())):
+        name, ms = ctypes.c_char_p(), ctypes.c_float()
+        _check(L.twell_trace_get(i, ctypes.byref(name), ctypes.byref(ms)), "twell_trace_get")
+        out.append((name.value.decode(), float(ms.value)))
+    if L.twell_trace_dropped():
+        raise TwellError(4, "trace_stop", f"{L.twell_trace_dropped()} launches dropped; raise the capacity")
+    return out
+
+
+class TwellFFN:
+    """Buffers for one (dims, dtype) problem, and the whole hot path in order.
+
+    forward(): gate_pack -> ffn_fwd (with a_save when training)
+    backward(): route_hybrid -> ffn_bwd
+    All buffers are allocated once here, with torch, on `device`.
+    """
+
+    def __init__(self, dims: Dims, dtype: int, train: bool = False, device="cuda"):
+        self.dims, self.dtype, self.train = dims, dtype, train
+        self.sizes = query_sizes(dims, dtype)
+        self.pack = alloc_pack(dims, dtype, device)
+        N, D, F = dims.n_tokens, dims.d_model, dims.d_ff
+        self.y = torch.empty((N, D), dtype=torch.float32, device=device)
+        self.ws_fwd = alloc_workspace(self.sizes["ws_fwd"], device)
+        self.a_save = None
+        if train:
+            self.a_save = torch.empty(self.sizes["a_save"] // 4, dtype=torch.float32, device=device)
+            self.hyb = alloc_hybrid(dims, dtype, device)
+            self.ws_bwd = alloc_workspace(self.sizes["ws_bwd"], device)
+            self.dx = torch.empty((N, D), dtype=torch.float32, device=device)
+            self.dw_gate_t = torch.empty((F, D), dtype=torch.float32, device=device)
+            self.dw_up_t = torch.empty((F, D), dtype=torch.float32, device=device)
+            self.dw_down = torch.empty((F, D), dtype=torch.float32, device=device)
+
+    def forward(self, x, w_gate_t, w_up_t, w_down, t, g_dump=None, stream=None):
+        gate_pack(self.dims, self.dtype, x, w_gate_t, t, self.pack, g_dump=g_dump, stream=stream)
+        ffn_fwd(self.dims, self.dtype, self.pack, x, w_up_t, w_down, self.y, a_save=self.a_save, ws=self.ws_fwd,
+                stream=stream)
+        return self.y
+
+    def backward(self, x, dy, w_gate_t, w_up_t, w_down, l1_lambda: float, stream=None):
+        route_hybrid(self.dims, self.dtype, self.pack, self.a_save, self.hyb, stream=stream)
+        ffn_bwd(self.dims, self.dtype, self.hyb, x, dy, w_gate_t, w_up_t, w_down, l1_lambda, self.dx, self.dw_gate_t,
+                self.dw_up_t, self.dw_down, self.ws_bwd, stream=stream)
+        return self.dx, self.dw_gate_t, self.dw_up_t, self.dw_down

@@ -1,0 +1,270 @@
+#!/usr/bin/env python3
+"""Benchmark of the libtwell hot path on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input.
+The default workload is the training step (8192 tokens, d_model 2048, d_ff
+8192, lognormal gate density with mean 1%): gate GEMM with the TwELL pack
+epilogue, overflow rows, fused up/down projection (saving a), hybrid routing
+and the sparse backward. Other workloads (forward only) can be picked with
+--workload.
+
+Prints ONE JSON line: throughput in tokens/s, the dense bf16 FFN on the same
+GPU and inputs as reference, the roofline of the dominant kernel (device time
+from HIP events recorded around each kernel on its own stream through the
+library's trace ABI), and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, published
+METRIC = "sparse FFN tokens/s and speedup vs dense bf16 FFN; HBM GB/s / MFMA % of peak"
+
+WORKLOADS = {
+    # name: (config, density override, train)
+    "c5": ("c5", None, True),
+    "c2": ("c2", None, False),
+    "c3_5": ("c3", 0.05, False),
+    "c3_1": ("c3", 0.01, False),
+    "c3_05": ("c3", 0.005, False),
+    "c4": ("c4", None, False),
+}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="c5", choices=sorted(WORKLOADS))
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-dense", action="store_true")
+    p.add_argument("--cpu-sample", type=int, default=0, help="tokens in the CPU oracle sample (0 = auto)")
+    return p.parse_args()
+
+
+def capacities(w, train):
+    """Overflow / dense-backup capacities the benchmark launches with (rows)."""
+    return max(64, w.N // 8), (max(64, w.N // 8) if train else 0)
+
+
+def describe(w, train):
+    dens = w.density
+    d = f"uniform {dens[1] * 100:g}%" if dens[0] == "uniform" else \
+        f"lognormal mean {dens[1] * 100:g}% sigma {dens[2]:g} clip [{dens[3] * 100:g}%, {dens[4] * 100:g}%]"
+    kind = "training step (fwd + route + bwd)" if train else "forward"
+    return f"{kind}: {w.N} tokens x d_model {w.D} x d_ff {w.F}, T_n {w.tile_n}, S {w.slots}, density {d}"
+
+
+def kernel_work(name, w, st, train):
+    """Algorithmic bytes and flops of one launch of a main kernel (what the method must move / compute)."""
+    N, D, F, e = w.N, w.D, w.F, 2
+    nnz, nnz_ell, n_t = st["nnz"], st["nnz_ell"], w.n_tiles
+    if name == "gate_mfma_bf16":
+        twell = n_t * w.slots * N * (e + 2) + n_t * N * 2
+        return {"flops": 2.0 * N * D * F, "bytes": N * D * e + F * D * e + twell, "bound": "mfma"}
+    if name == "ffn_fwd_kernel":
+        byt = N * D * e + 2 * F * D * e + nnz * (e + 2) + n_t * N * 2 + N * D * 4 + (nnz * 4 if train else 0)
+        return {"flops": 4.0 * D * nnz, "bytes": byt, "bound": "hbm"}
+    if name == "bwd_rows":
+        byt = N * D * e + 3 * F * D * e + nnz_ell * (e + 8) + N * D * 4 + nnz * 20
+        return {"flops": 6.0 * D * nnz, "bytes": byt, "bound": "hbm"}
+    if name == "bwd_dw":
+        byt = 2 * N * D * e + nnz * 24 + 3 * F * D * 4
+        return {"flops": 6.0 * D * nnz, "bytes": byt, "bound": "hbm"}
+    return None
+
+
+def cpu_baseline(w, train, sample):
+    """The oracle, as it stands, on the first `sample` tokens of the workload."""
+    import numpy as np
+    from oracle import twell_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = None
+    cores = len(os.sched_getaffinity(0))
+    n = sample
+    x, t = w.x[:n], w.t[:n]
+    t0 = time.perf_counter()
+    fw = orc.ffn_forward(x, w.w_gate_t, w.w_up_t, w.w_down, t, store=w.dtype)
+    pk = orc.pack(fw["g"], t, w.tile_n, w.slots, store=w.dtype, arith="f32")
+    if train:
+        orc.route(pk, w.row_cap, a=fw["a"], ovf_h=fw["hq"][pk["ovf_rows"]])
+        orc.ffn_backward(x, w.dy[:n], w.w_gate_t, w.w_up_t, w.w_down, fw["mask"], fw["hq"], w.lam)
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": blas_threads or cores, "kind": "oracle",
+            "sample": f"first {n} of {w.N} tokens of the same workload (full d_model/d_ff, fp64 NumPy, "
+                      f"{'forward + pack + route + backward' if train else 'forward + pack'}); {dt:.1f} s wall; "
+                      f"host affinity {cores} cores"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              f"(multi-GPU sharding is design-only).", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from activation_sparse_ffn_03_amd import twell as tw
+    from synth import make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    tw.lib()
+    cfg, dens, train = WORKLOADS[args.workload]
+    w = make_inputs(cfg, density=dens)
+    print(f"[bench] workload {args.workload}: {describe(w, train)}", file=sys.stderr, flush=True)
+    dev = torch.device("cuda:0")
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev).to(torch.bfloat16)
+
+    x, wg, wu, wd = up(w.x), up(w.w_gate_t), up(w.w_up_t), up(w.w_down)
+    t = torch.from_numpy(w.t).to(dev)
+    dy = up(w.dy) if train else None
+    ovf_cap, dense_cap = capacities(w, train)
+    dims = tw.make_dims(w.N, w.D, w.F, w.tile_n, w.slots, w.row_cap if train else 0, ovf_cap, dense_cap)
+    ffn = tw.TwellFFN(dims, tw.BF16, train=train)
+
+    def step():
+        ffn.forward(x, wg, wu, wd, t)
+        if train:
+            ffn.backward(x, dy, wg, wu, wd, w.lam)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = e0.elapsed_time(e1) / args.steps
+    assert int(ffn.pack.status.item()) == 0, "overflow capacity exceeded"
+    if train:
+        assert int(ffn.hyb.status.item()) == 0, "dense-backup capacity exceeded"
+
+    # per-kernel device times: HIP events around every kernel on the stream it runs on
+    tw.trace_start(capacity=64 * args.steps + 64)
+    for _ in range(args.steps):
+        step()
+    recs = tw.trace_stop()
+    per = {}
+    for name, kms in recs:
+        per.setdefault(name, []).append(kms)
+    kernels = {k: {"launches_per_step": len(v) / args.steps, "avg_ms": sum(v) / len(v),
+                   "ms_per_step": sum(v) / args.steps} for k, v in per.items()}
+
+    cnt = ffn.pack.counts.to(torch.int32) & 0xFFFF   # uint16 counts stored in int16
+    nnz = int(cnt.to(torch.int64).sum().item())
+    stats = {"nnz": nnz, "nnz_ell": nnz, "n_ovf": int(ffn.pack.n_ovf.item())}
+    if train:
+        isd = ffn.hyb.is_dense.bool()
+        rn = ffn.hyb.row_nnz.to(torch.int64)
+        stats["nnz_ell"] = int(rn[~isd].sum().item())
+        stats["n_dense"] = int(ffn.hyb.n_dense.item())
+
+    main_k = [k for k in kernels if kernel_work(k, w, stats, train)]
+    dom = max(main_k, key=lambda k: kernels[k]["ms_per_step"])
+    wk = kernel_work(dom, w, stats, train)
+    sec = kernels[dom]["avg_ms"] / 1e3
+    if wk["bound"] == "mfma":
+        ach = wk["flops"] / sec / 1e12
+        roof = {"bound": "mfma", "achieved": ach, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                "frac": ach / MFMA_BF16_PEAK_TFS, "traffic": None, "kernel": dom}
+    else:
+        ach = wk["bytes"] / sec / 1e9
+        roof = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": ach / HBM_PEAK_GBS, "traffic": None, "kernel": dom}
+    for k in main_k:
+        wk_k = kernel_work(k, w, stats, train)
+        s_k = kernels[k]["avg_ms"] / 1e3
+        kernels[k]["GBps_algorithmic"] = wk_k["bytes"] / s_k / 1e9
+        kernels[k]["TFLOPs"] = wk_k["flops"] / s_k / 1e12
+
+    # dense bf16 FFN on the same GPU and inputs (torch / hipBLASLt), same step definition
+    dense = None
+    if not args.no_dense:
+        lam = w.lam
+
+        def dense_step():
+            g = torch.nn.functional.linear(x, wg)
+            a = torch.nn.functional.linear(x, wu)
+            m = g > t[:, None]
+            h = torch.where(m, g - t[:, None].to(g.dtype), torch.zeros((), dtype=g.dtype, device=dev))
+            z = h * a
+            y = torch.mm(z, wd)
+            if train:
+                dz = torch.nn.functional.linear(dy, wd)
+                dwd = torch.mm(z.t(), dy)
+                da = dz * h
+                dg = torch.where(m, dz * a + lam, torch.zeros((), dtype=g.dtype, device=dev))
+                dx = torch.mm(da, wu) + torch.mm(dg, wg)
+                dwu = torch.mm(da.t(), x)
+                dwg = torch.mm(dg.t(), x)
+                return y, dx, dwd, dwu, dwg
+            return y
+
+        for _ in range(args.warmup):
+            dense_step()
+        torch.cuda.synchronize()
+        d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        d0.record(stream)
+        for _ in range(args.steps):
+            dense_step()
+        d1.record(stream)
+        torch.cuda.synchronize()
+        dense = d0.elapsed_time(d1) / args.steps
+
+    flops_dense = 6.0 * w.N * w.D * w.F * (3 if train else 1)
+    out = {
+        "metric": METRIC,
+        "value": w.N / (ms / 1e3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {describe(w, train)}", "n_tokens": w.N, "d_model": w.D,
+                   "d_ff": w.F, "tile_n": w.tile_n, "slots": w.slots, "row_cap": w.row_cap if train else 0,
+                   "parallelism": "none (1 GPU)"},
+        "speedup_vs_dense": (dense / ms) if dense else None,
+        "dense_bf16_ms_per_step": dense,
+        "dense_equivalent_tflops": flops_dense / (ms / 1e3) / 1e12,
+        "roofline": roof,
+        "kernels": kernels,
+        "workload_stats": {**stats, "density": nnz / (w.N * w.F)},
+        "wall_s_timed": wall,
+    }
+    if not args.no_cpu_baseline:
+        sample = args.cpu_sample or 4096
+        out["cpu_baseline"] = cpu_baseline(w, train, min(sample, w.N))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -113,18 +113,31 @@ def gate_preact(x, w_gate_t) -> np.ndarray:
     return _f64(x) @ _f64(w_gate_t).T
 
 
-def ffn_forward(x, w_gate_t, w_up_t, w_down, t, store: str = "bf16") -> dict:
-    """Dense ReLU-gated FFN y = (Q(ReLU(x W_gate - t)) * (x W_up)) W_down, all float64.
+def ffn_forward(x, w_gate_t, w_up_t, w_down, t, store: str = "bf16", arith: str = "f64") -> dict:
+    """Dense ReLU-gated FFN y = (Q(ReLU(x W_gate - t)) * (x W_up)) W_down, float64.
 
     g = x W_gate (gate projection), active mask M = g > t_i (strict),
     h = M * (g - t_i), hq = Q(h) the storage rounding of the activation,
     a = x W_up (up projection), z = hq * a, y = z W_down (down projection).
+
+    arith="f32" forms the stored activation the way the packed format defines
+    it, Q(fl32(g32 - t)) with g32 = fl32(g) and the compare and subtraction in
+    IEEE fp32; everything else stays float64. arith="f64" uses g and g - t in
+    float64.
     """
     x = _f64(x)
     t = _f64(t).reshape(-1)
     g = gate_preact(x, w_gate_t)
-    mask = g > t[:, None]
-    h = np.where(mask, g - t[:, None], 0.0)
+    if arith == "f32":
+        g32 = g.astype(np.float32)
+        t32 = t.astype(np.float32)
+        mask = g32 > t32[:, None]
+        h = np.where(mask, (g32 - t32[:, None]).astype(np.float64), 0.0)
+    elif arith == "f64":
+        mask = g > t[:, None]
+        h = np.where(mask, g - t[:, None], 0.0)
+    else:
+        raise ValueError(f"unknown arith {arith!r}")
     hq = store_round(h, store)
     a = x @ _f64(w_up_t).T
     z = hq * a
@@ -335,6 +348,31 @@ def margin_thresholds(g, p, window: float = 0.25) -> np.ndarray:
             raise ValueError(f"row {i}: gap too narrow for an fp32 threshold")
         t[i] = mid
     return t
+
+
+def bf16_ulp(a) -> np.ndarray:
+    """Spacing of bf16 values at |a| (2^(e-7) for |a| in [2^e, 2^(e+1))); 0 at a == 0."""
+    a = np.abs(_f64(a))
+    _, e = np.frexp(a)
+    return np.where(a > 0, np.ldexp(1.0, e - 8), 0.0)
+
+
+def store_ulp(a, store: str) -> np.ndarray:
+    """Spacing of storage values at |a|: bf16 (8 significant bits) or fp32 (24)."""
+    a = np.abs(_f64(a))
+    _, e = np.frexp(a)
+    bits = {"bf16": 8, "f32": 24}[store]
+    return np.where(a > 0, np.ldexp(1.0, e - bits), 0.0)
+
+
+def rounding_ambiguous(h, delta, store: str = "bf16") -> np.ndarray:
+    """Entries whose stored value Q(v) is not the same for every v within
+    [h - delta, h + delta]: an implementation that evaluates h with an error up
+    to delta may store either neighbour there, and both are correct results."""
+    h = _f64(h)
+    lo = store_round(np.maximum(h - delta, 0.0), store)
+    hi = store_round(h + delta, store)
+    return (h > 0) & (lo != hi)
 
 
 def relative_margin(g, t) -> np.ndarray:

@@ -88,9 +88,21 @@ def _densities(rng, N: int, spec: tuple) -> np.ndarray:
     raise ValueError(f"unknown density spec {spec!r}")
 
 
+def _grid(rng, shape, half: int, scale: float) -> np.ndarray:
+    """Integers uniform in [-half, half] times a power-of-two scale (exact in bf16)."""
+    return (rng.integers(-half, half + 1, size=shape).astype(np.float32) * np.float32(scale))
+
+
 def make_inputs(name: str, seed: int = 0, *, density=None, N=None, D=None, F=None,
-                tile_n=None, slots=None, row_cap=None) -> Workload:
-    """Draw one workload. Keyword overrides shrink a config for quick tests."""
+                tile_n=None, slots=None, row_cap=None, grid: bool = False) -> Workload:
+    """Draw one workload. Keyword overrides shrink a config for quick tests.
+
+    grid=True draws x as multiples of 1/8 in [-2, 2] and the weights as
+    multiples of 1/64 in [-1/8, 1/8] instead of normals: every product is then a
+    multiple of 2^-9 and every dot product over d_model <= 8192 stays below
+    2^21 * 2^-9, so it is exact in fp32 whatever the summation order. Used to
+    make rounding decisions on the gate pre-activation identical on every
+    implementation."""
     cfg = dict(CONFIGS[name])
     for k, v in dict(N=N, D=D, F=F, tile_n=tile_n, slots=slots, row_cap=row_cap).items():
         if v is not None:
@@ -100,16 +112,25 @@ def make_inputs(name: str, seed: int = 0, *, density=None, N=None, D=None, F=Non
     n, d, f = int(cfg["N"]), int(cfg["D"]), int(cfg["F"])
     dt = cfg["dtype"]
     rng = np.random.default_rng(seed)
-    x = _round_storage(rng.standard_normal((n, d), dtype=np.float32), dt)
-    wg = _round_storage(rng.standard_normal((f, d), dtype=np.float32) * np.float32(1.0 / math.sqrt(d)), dt)
-    wu = _round_storage(rng.standard_normal((f, d), dtype=np.float32) * np.float32(1.0 / math.sqrt(d)), dt)
-    wd = _round_storage(rng.standard_normal((f, d), dtype=np.float32) * np.float32(1.0 / math.sqrt(f)), dt)
+    if grid:
+        x = _grid(rng, (n, d), 16, 1.0 / 8)
+        wg = _grid(rng, (f, d), 8, 1.0 / 64)
+        wu = _grid(rng, (f, d), 8, 1.0 / 64)
+        wd = _grid(rng, (f, d), 8, 1.0 / 64)
+        w_std = math.sqrt(sum(k * k for k in range(-8, 9)) / 17.0) / 64.0
+    else:
+        x = _round_storage(rng.standard_normal((n, d), dtype=np.float32), dt)
+        wg = _round_storage(rng.standard_normal((f, d), dtype=np.float32) * np.float32(1.0 / math.sqrt(d)), dt)
+        wu = _round_storage(rng.standard_normal((f, d), dtype=np.float32) * np.float32(1.0 / math.sqrt(d)), dt)
+        wd = _round_storage(rng.standard_normal((f, d), dtype=np.float32) * np.float32(1.0 / math.sqrt(f)), dt)
+        w_std = 1.0 / math.sqrt(d)
     p = _densities(rng, n, cfg["density"])
-    sigma = np.sqrt(np.einsum("ij,ij->i", x.astype(np.float64), x.astype(np.float64)) / d)
+    # std of g_ij given x_i when the gate weights have standard deviation w_std
+    sigma = np.sqrt(np.einsum("ij,ij->i", x.astype(np.float64), x.astype(np.float64))) * w_std
     t = (sigma * scipy.special.ndtri(1.0 - p)).astype(np.float32)
     dy = None
     if cfg["train"]:
-        dy = _round_storage(rng.standard_normal((n, d), dtype=np.float32), dt)
+        dy = _grid(rng, (n, d), 16, 1.0 / 8) if grid else _round_storage(rng.standard_normal((n, d), dtype=np.float32), dt)
     return Workload(name=name, N=n, D=d, F=f, tile_n=int(cfg["tile_n"]), slots=int(cfg["slots"]),
                     row_cap=int(cfg["row_cap"]), dtype=dt, train=bool(cfg["train"]),
                     lam=float(cfg["lam"]), density=tuple(cfg["density"]),

@@ -1,0 +1,75 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every symbol include/twell.h declares, and rejects bad arguments before
+touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from activation_sparse_ffn_03_amd import twell as tw
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "twell.h")
+
+
+def test_library_exports_every_declared_symbol():
+    decl = set(re.findall(r"\b(twell_[a-z_]+)\s*\(", open(HEADER).read()))
+    assert decl == set(tw.EXPORTS), decl ^ set(tw.EXPORTS)
+    L = tw.lib()
+    for name in decl:
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    L = tw.lib()
+    assert L.twell_status_str(0) == b"TWELL_OK"
+    assert L.twell_status_str(3) == b"TWELL_ERR_WORKSPACE"
+    assert L.twell_status_str(99) == b"TWELL_ERR_UNKNOWN"
+
+
+def test_n_tiles_and_sizes():
+    d = tw.make_dims(64, 128, 512, 64, 16, 0, 4, 0)
+    assert tw.n_tiles(d) == 8
+    z = tw.query_sizes(d, tw.F32)
+    assert z["vals"] == 8 * 16 * 64 * 4 and z["cols"] == 8 * 16 * 64 * 2 and z["counts"] == 8 * 64 * 2
+    assert z["ovf_h"] == 4 * 512 * 4 and z["a_save"] == 8 * 16 * 64 * 4
+    d2 = tw.make_dims(8192, 2048, 8192, 128, 16, 512, 1024, 1024)
+    z2 = tw.query_sizes(d2, tw.BF16)
+    assert z2["ell_vals"] == 512 * 8192 * 2 and z2["dense_h"] == 1024 * 8192 * 2
+    assert z2["ws_bwd"] > 8192 * 512 * 28   # pair records of every possible entry
+    assert tw.n_tiles(tw.make_dims(1, 64, 1000, 128, 4)) == 8   # ragged last tile
+
+
+@pytest.mark.parametrize("dims,code", [
+    ((64, 100, 512, 64, 16), tw.UNSUPPORTED if hasattr(tw, "UNSUPPORTED") else 2),  # d_model not /64
+    ((64, 128, 512, 48, 16), 2),      # tile_n not supported
+    ((64, 128, 512, 64, 65), 1),      # slots > tile_n
+    ((-1, 128, 512, 64, 16), 1),      # negative tokens
+    ((64, 128, 70000, 64, 16), 2),    # d_ff too large
+    ((64, 16384, 512, 64, 16), 2),    # d_model too large
+])
+def test_invalid_shapes(dims, code):
+    with pytest.raises(tw.TwellError) as e:
+        tw.query_sizes(tw.make_dims(*dims), tw.BF16)
+    assert e.value.status == code
+
+
+def test_calls_validate_before_touching_the_device():
+    L = tw.lib()
+    d = tw.make_dims(64, 128, 512, 64, 16, 8, 4, 4)
+    p, h = tw.Pack(), tw.Hybrid()
+    assert L.twell_gate_pack(ctypes.byref(d), 0, None, None, None, ctypes.byref(p), None, None) == 1
+    assert b"x" in L.twell_last_error()
+    assert L.twell_pack_preact(ctypes.byref(d), 0, None, None, ctypes.byref(p), None) == 1
+    assert L.twell_ffn_fwd(ctypes.byref(d), 0, None, None, None, None, None, None, None, 0, None) == 1
+    assert L.twell_route_hybrid(ctypes.byref(d), 0, ctypes.byref(p), None, ctypes.byref(h), None) == 1
+    assert L.twell_ffn_bwd(ctypes.byref(d), 0, ctypes.byref(h), None, None, None, None, None, ctypes.c_float(0.0),
+                           None, None, None, None, None, 0, None) == 1
+    # misaligned pointer
+    fake = ctypes.c_void_p(0x1001)
+    assert L.twell_gate_pack(ctypes.byref(d), 0, fake, fake, fake, ctypes.byref(p), None, None) == 1
+    # bad dtype
+    z = tw.Sizes()
+    assert L.twell_query_sizes(ctypes.byref(d), 7, ctypes.byref(z)) == 1
+    assert L.twell_n_tiles(None) == -1
+    assert L.twell_trace_start(0) == 1

@@ -388,3 +388,43 @@ def test_rowwise_rel_err():
     e = orc.rowwise_rel_err(got, ref)
     assert abs(e[0] - 0.1 / math.sqrt(12.5)) < 1e-12 and e[1] == 0
     assert orc.rowwise_rel_err(np.array([[0.0, 1e-9]]), np.zeros((1, 2)))[0] == np.inf
+
+
+# ----------------------------------------------------------------- fp32-formed activation, rounding helpers
+
+def test_forward_f32_arith_equals_f32_pack():
+    # the dense activation formed as Q(fl32(fl32(g) - t)) equals the packed one (same definition, two codes)
+    w = make_inputs("c2", N=50, D=128, F=300, density=0.1)
+    fw = orc.ffn_forward(w.x, w.w_gate_t, w.w_up_t, w.w_down, w.t, store="bf16", arith="f32")
+    pk = orc.pack(fw["g"].astype(np.float32), w.t, 64, 8, store="bf16", arith="f32")
+    np.testing.assert_array_equal(orc.unpack(pk, fw["hq"][pk["ovf_rows"]]), fw["hq"])
+    ys = orc.sparse_forward(pk, w.x, w.w_up_t, w.w_down, fw["hq"][pk["ovf_rows"]])
+    np.testing.assert_array_equal(ys, fw["y"])
+    # the two arithmetics differ only by fp32 rounding of g - t
+    f64 = orc.ffn_forward(w.x, w.w_gate_t, w.w_up_t, w.w_down, w.t, store="exact", arith="f64")
+    f32 = orc.ffn_forward(w.x, w.w_gate_t, w.w_up_t, w.w_down, w.t, store="exact", arith="f32")
+    both = f64["mask"] & f32["mask"]
+    assert np.all(np.abs(f64["h"][both] - f32["h"][both]) <= 2.0 ** -20 * (1 + np.abs(f64["g"][both])))
+
+
+def test_grid_inputs_make_gate_exact_in_fp32():
+    w = make_inputs("c5", N=64, D=8192, F=64, grid=True)
+    g = orc.gate_preact(w.x, w.w_gate_t)
+    # every partial sum is a multiple of 2^-9 below 2^21 in magnitude, so fp32 holds g exactly
+    np.testing.assert_array_equal(g.astype(np.float32).astype(np.float64), g)
+    np.testing.assert_array_equal(np.round(g * 512), g * 512)
+    c = make_inputs("c5", N=4000, D=256, F=512, grid=True)
+    gc = orc.gate_preact(c.x, c.w_gate_t)
+    assert 0.008 < (gc > c.t[:, None]).mean() < 0.012   # thresholds still give ~1% density
+
+
+def test_store_ulp_and_rounding_ambiguity():
+    assert orc.store_ulp(1.0, "bf16") == 2.0 ** -7 and orc.store_ulp(1.5, "bf16") == 2.0 ** -7
+    assert orc.store_ulp(2.0, "bf16") == 2.0 ** -6 and orc.store_ulp(0.75, "bf16") == 2.0 ** -8
+    assert orc.store_ulp(1.0, "f32") == 2.0 ** -23 and orc.store_ulp(0.0, "bf16") == 0.0
+    mid = 1.0 + 2.0 ** -8                        # half way between two bf16 neighbours
+    assert orc.rounding_ambiguous(np.array([mid]), 1e-9)[0]
+    assert not orc.rounding_ambiguous(np.array([1.0 + 2.0 ** -7]), 1e-9)[0]
+    assert not orc.rounding_ambiguous(np.array([mid + 1e-6]), 1e-9)[0]
+    assert orc.rounding_ambiguous(np.array([mid + 1e-6]), 2e-6)[0]
+    assert not orc.rounding_ambiguous(np.array([0.0]), 1.0)[0]
