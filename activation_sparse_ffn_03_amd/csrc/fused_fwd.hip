@@ -72,17 +72,21 @@ __global__ __launch_bounds__(256) void ffn_fwd_kernel(FwdArgs a, int G) {
         const int j = jb + t;
         const int cnt = readlane_i(cnt_l, t);
         const size_t base = (size_t)j * a.slots * N + i;
-        int col_l = 0;
-        float h_l = 0.f;
-        if (lane < cnt) {
-          col_l = a.cols[base + (size_t)lane * N];
-          h_l = Store<TS>::load(vals, base + (size_t)lane * N);
-        }
-        for (int s = 0; s < cnt; ++s) {
-          const int c = j * a.tile_n + readlane_i(col_l, s);
-          const float h = readlane_f(h_l, s);
-          float* a_out = a.a_save ? a.a_save + base + (size_t)s * N : nullptr;
-          do_pair<TS, M>(w_up, w_down, D, a.F, nch, lane, xr, acc, c, h, a_out);
+        // slots are read 64 at a time (S may reach T_n = 128)
+        for (int sb = 0; sb < cnt; sb += 64) {
+          int col_l = 0;
+          float h_l = 0.f;
+          if (sb + lane < cnt) {
+            col_l = a.cols[base + (size_t)(sb + lane) * N];
+            h_l = Store<TS>::load(vals, base + (size_t)(sb + lane) * N);
+          }
+          const int nb = min(64, cnt - sb);
+          for (int s = 0; s < nb; ++s) {
+            const int c = j * a.tile_n + readlane_i(col_l, s);
+            const float h = readlane_f(h_l, s);
+            float* a_out = a.a_save ? a.a_save + base + (size_t)(sb + s) * N : nullptr;
+            do_pair<TS, M>(w_up, w_down, D, a.F, nch, lane, xr, acc, c, h, a_out);
+          }
         }
       }
     }

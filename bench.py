@@ -2,11 +2,12 @@
 """Benchmark of the libtwell hot path on one MI355X.
 
 A step is one pass of the whole hot path over one batch of synthetic input.
-The default workload is the training step (8192 tokens, d_model 2048, d_ff
-8192, lognormal gate density with mean 1%): gate GEMM with the TwELL pack
-epilogue, overflow rows, fused up/down projection (saving a), hybrid routing
-and the sparse backward. Other workloads (forward only) can be picked with
---workload.
+The default workload is the 1B-class forward (4096 tokens, d_model 2048, d_ff
+5632, uniform gate density 1%): gate GEMM with the TwELL pack epilogue,
+overflow rows, and the fused up/down projection. The other workloads are
+picked with --workload: the 7B-class forward at three densities, the
+skewed-density forward, and the training step (forward saving a, hybrid
+routing and the sparse backward).
 
 Prints ONE JSON line: throughput in tokens/s, the dense bf16 FFN on the same
 GPU and inputs as reference, the roofline of the dominant kernel (device time
@@ -45,10 +46,12 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--workload", default="c5", choices=sorted(WORKLOADS))
+    p.add_argument("--workload", default="c2", choices=sorted(WORKLOADS))
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-dense", action="store_true")
-    p.add_argument("--cpu-sample", type=int, default=0, help="tokens in the CPU oracle sample (0 = auto)")
+    p.add_argument("--cpu-sample", type=int, default=512, help="tokens per window of the CPU oracle sample")
+    p.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of CPU oracle work")
+    p.add_argument("--copy-calib", action="store_true", help="only run the copy kernel used to scale HBM counters")
     return p.parse_args()
 
 
@@ -84,8 +87,10 @@ def kernel_work(name, w, st, train):
     return None
 
 
-def cpu_baseline(w, train, sample):
-    """The oracle, as it stands, on the first `sample` tokens of the workload."""
+def cpu_baseline(w, train, sample, budget_s=10.0):
+    """The oracle, as it stands, on successive windows of `sample` tokens of the
+    same workload (full d_model / d_ff), repeated until about `budget_s` seconds
+    of CPU work have been done; returns the oracle's tokens/s."""
     import numpy as np
     from oracle import twell_oracle as orc
     try:
@@ -94,19 +99,76 @@ def cpu_baseline(w, train, sample):
     except Exception:  # pragma: no cover
         blas_threads = None
     cores = len(os.sched_getaffinity(0))
-    n = sample
-    x, t = w.x[:n], w.t[:n]
+    n = max(1, min(sample, w.N))
+    done, windows = 0, 0
     t0 = time.perf_counter()
-    fw = orc.ffn_forward(x, w.w_gate_t, w.w_up_t, w.w_down, t, store=w.dtype)
-    pk = orc.pack(fw["g"], t, w.tile_n, w.slots, store=w.dtype, arith="f32")
-    if train:
-        orc.route(pk, w.row_cap, a=fw["a"], ovf_h=fw["hq"][pk["ovf_rows"]])
-        orc.ffn_backward(x, w.dy[:n], w.w_gate_t, w.w_up_t, w.w_down, fw["mask"], fw["hq"], w.lam)
+    while True:
+        lo = (windows * n) % w.N
+        rows = np.arange(lo, min(lo + n, w.N))
+        x, t = w.x[rows], w.t[rows]
+        fw = orc.ffn_forward(x, w.w_gate_t, w.w_up_t, w.w_down, t, store=w.dtype)
+        pk = orc.pack(fw["g"], t, w.tile_n, w.slots, store=w.dtype, arith="f32")
+        if train:
+            orc.route(pk, w.row_cap, a=fw["a"], ovf_h=fw["hq"][pk["ovf_rows"]])
+            orc.ffn_backward(x, w.dy[rows], w.w_gate_t, w.w_up_t, w.w_down, fw["mask"], fw["hq"], w.lam)
+        done += rows.size
+        windows += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
     dt = time.perf_counter() - t0
-    return {"value": n / dt, "unit": "tokens/s", "cores": blas_threads or cores, "kind": "oracle",
-            "sample": f"first {n} of {w.N} tokens of the same workload (full d_model/d_ff, fp64 NumPy, "
-                      f"{'forward + pack + route + backward' if train else 'forward + pack'}); {dt:.1f} s wall; "
-                      f"host affinity {cores} cores"}
+    return {"value": done / dt, "unit": "tokens/s", "cores": blas_threads or cores, "kind": "oracle",
+            "sample": f"{windows} windows of {n} tokens ({done} tokens) of the same workload, full d_model/d_ff, "
+                      f"fp64 NumPy, {'forward + pack + route + backward' if train else 'forward + pack'}; "
+                      f"{dt:.1f} s wall; BLAS threads {blas_threads}, host affinity {cores} cores"}
+
+
+# Source files whose code makes up each timed kernel: the committed counter
+# summary of a kernel is only used while these files are unchanged.
+KERNEL_SOURCES = {
+    "gate_mfma_bf16": ["gate_pack.hip", "twell_device.h"],
+    "ffn_fwd_kernel": ["fused_fwd.hip", "row_ops.h", "twell_device.h"],
+    "bwd_rows": ["bwd.hip", "row_ops.h", "twell_device.h"],
+    "bwd_dw": ["bwd.hip", "row_ops.h", "twell_device.h"],
+}
+
+
+def kernel_source_hash(kernel):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES.get(kernel, []):
+        with open(os.path.join(ROOT, "activation_sparse_ffn_03_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration),
+    or None if there is none or the kernel's source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha256_16") != kernel_source_hash(kernel):
+        return None
+    return float(kv["hbm_bytes_per_launch"])
+
+
+def copy_calibration():
+    """A plain device-to-device copy of known size, for scaling the HBM byte
+    counters: 1 GiB read and 1 GiB written per launch."""
+    import torch
+    src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": src.numel() * 2, "copy_bytes_written": dst.numel() * 2, "launches": 3}))
 
 
 def main():
@@ -124,6 +186,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calib:
+        copy_calibration()
+        return
     tw.lib()
     cfg, dens, train = WORKLOADS[args.workload]
     w = make_inputs(cfg, density=dens)
@@ -190,11 +255,11 @@ def main():
     if wk["bound"] == "mfma":
         ach = wk["flops"] / sec / 1e12
         roof = {"bound": "mfma", "achieved": ach, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
-                "frac": ach / MFMA_BF16_PEAK_TFS, "traffic": None, "kernel": dom}
+                "frac": ach / MFMA_BF16_PEAK_TFS, "traffic": measured_traffic(dom, args.workload), "kernel": dom}
     else:
         ach = wk["bytes"] / sec / 1e9
         roof = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": ach / HBM_PEAK_GBS, "traffic": None, "kernel": dom}
+                "frac": ach / HBM_PEAK_GBS, "traffic": measured_traffic(dom, args.workload), "kernel": dom}
     for k in main_k:
         wk_k = kernel_work(k, w, stats, train)
         s_k = kernels[k]["avg_ms"] / 1e3
@@ -261,8 +326,7 @@ def main():
         "wall_s_timed": wall,
     }
     if not args.no_cpu_baseline:
-        sample = args.cpu_sample or 4096
-        out["cpu_baseline"] = cpu_baseline(w, train, min(sample, w.N))
+        out["cpu_baseline"] = cpu_baseline(w, train, args.cpu_sample, args.cpu_budget)
     print(json.dumps(out), flush=True)
 
 

@@ -71,9 +71,12 @@ def test_fullsize_forward(name):
     valid = np.arange(S)[None, :, None] < np.minimum(ref["counts"], S)[:, None, :]
     cols = u16(ffn.pack.cols)[:, :, cr]
     np.testing.assert_array_equal(cols[valid], ref["cols"][valid])
+    # stored values: the GPU's fp32 g may differ from fl32(g64) by up to delta_i = DELTA_REL * rms_i,
+    # so Q(fl32(g - t)) may differ by that plus one bf16 rounding step on either side
     vals = f64(ffn.pack.vals)[:, :, cr]
+    delta = np.broadcast_to((DELTA_REL * rms[clean])[None, None, :], valid.shape)[valid]
     rv = ref["vals"][valid]
-    assert np.all(np.abs(vals[valid] - rv) <= np.abs(rv) * 2.0 ** -7)
+    assert np.all(np.abs(vals[valid] - rv) <= 1.01 * delta + (np.abs(rv) + delta) * 2.0 ** -7)
 
 
 def test_fullsize_training_step():

@@ -28,7 +28,7 @@ def _preact_case(N, F, D, density, seed=0):
 # ------------------------------------------------------------------ pack from a given g: bit-exact
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("tile_n,slots", [(128, 16), (64, 16), (32, 4), (16, 2), (128, 0), (128, 1)])
+@pytest.mark.parametrize("tile_n,slots", [(128, 16), (64, 16), (32, 4), (16, 2), (128, 0), (128, 1), (128, 100)])
 def test_pack_preact_bit_exact(dtype, tile_n, slots):
     require_gpu()
     N, F = 300, 1000          # ragged against the 64-row tile and the 128-column tile
@@ -150,6 +150,7 @@ def test_ovf_rows_match_epilogue_values():
     ("c4", dict(N=600, D=512, F=2048), dict(slots=8)),   # lognormal, overflow rows
     ("c2", dict(N=130, D=128, F=200), dict(tile_n=16, slots=3)),
     ("c2", dict(N=64, D=64, F=128), dict(slots=0, ovf_cap=64)),  # every non-empty row is dense
+    ("c2", dict(N=96, D=128, F=300, density=0.75), dict(slots=128)),  # more than 64 slots in use per tile
 ])
 def test_ffn_forward(name, kw, extra):
     w = make_inputs(name, **kw)
@@ -214,6 +215,9 @@ def _train_case(N=1536, D=256, F=1024, K=24, seed=0, **kw):
 
 def _check_backward(w, pl, grads, tol=1e-4):
     dx, dwg, dwu, dwd = grads
+    # rows beyond a capacity are not computed: the comparison needs every row inside it
+    assert int(pl.ffn.pack.status.item()) == 0, "overflow capacity exceeded"
+    assert int(pl.ffn.hyb.status.item()) == 0, "dense-backup capacity exceeded"
     fw = orc.ffn_forward(w.x, w.w_gate_t, w.w_up_t, w.w_down, w.t, store=w.dtype, arith="f32")
     bw = orc.ffn_backward(w.x, w.dy, w.w_gate_t, w.w_up_t, w.w_down, fw["mask"], fw["hq"], w.lam)
     rowwise_ok(f64(dx), bw["dx"], tol, "dx")
@@ -227,7 +231,7 @@ def _check_backward(w, pl, grads, tol=1e-4):
     dict(),
     dict(N=2048, D=512, F=1300, K=40),
     dict(N=1024, D=128, F=512, K=4, slots=4, dense_cap=1024),
-    dict(N=700, D=2048, F=640, K=12),
+    dict(N=700, D=2048, F=640, K=12, dense_cap=700),
 ])
 def test_route_and_backward(case):
     case = dict(case)
@@ -286,9 +290,10 @@ def test_dense_capacity_status():
 
 def test_fp32_training_path():
     w = make_inputs("c1", N=512, D=128, F=512, grid=True)
-    w.train, w.row_cap, w.lam = True, 40, 1e-3
+    # 5% of 512 units: about 26 active per row, so K = 28 sends roughly a third of the rows to the dense backup
+    w.train, w.row_cap, w.lam = True, 28, 1e-3
     w.dy = np.random.default_rng(5).integers(-16, 17, (w.N, w.D)).astype(np.float32) / 8
-    pl = Pipeline(w, row_cap=40, dense_cap=512, ovf_cap=512)
+    pl = Pipeline(w, row_cap=28, dense_cap=512, ovf_cap=512)
     pl.forward()
     grads = pl.backward()
     assert int(pl.ffn.pack.status.item()) == 0 and int(pl.ffn.hyb.status.item()) == 0
