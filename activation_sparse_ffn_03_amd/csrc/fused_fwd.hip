@@ -1,22 +1,32 @@
-// Stage 2: fused up + down projection on the TwELL activation.
+// Stage 2: up + down projection on the TwELL activation.
 //
 // "Sakana AI and NVIDIA present TwELL" (edge.aivizor.me), second paragraph:
 // the inference kernel reads the activations in TwELL and performs the up and
-// down projections at once, without writing the intermediate hidden state to
-// global memory.
+// down projections without writing the intermediate hidden state to global
+// memory.
 //
-// Design (wave-stationary token): one wave owns one token. x_i (bf16 or fp32)
-// and the fp32 accumulator of y_i live in registers for the whole pass. The
-// wave walks the TwELL tiles in ascending order (so all waves on a chip sweep
-// the weight rows in the same order, which keeps the rows of the current tiles
-// hot in L2) and, for every packed entry (c, h):
-//   a = x_i . W_up^T[c]   (coalesced row gather + bf16 dot2 + wave reduction)
-//   z = h * a             (fp32, never stored)
-//   y_i += z * W_down[c]  (coalesced row gather + fp32 FMA)
-// Overflow rows (a tile count above S) are skipped here: their dense
-// activation row is split into column chunks of kDenseChunk, each chunk is a
-// work item of its own wave writing a partial y row, and dense_reduce adds the
-// partials in chunk order (deterministic, no atomics).
+// On MI355X every packed entry (i, c) has to bring its own W_up and W_down row
+// to the ALUs (at 1% density no block of tokens shares enough columns for
+// register reuse), so what decides the speed is where those rows come from:
+// the 4 MB L2 of the XCD, or the Infinity Cache / HBM behind it. The pass is
+// therefore split in two launches that each keep a 1/8 slice of a weight in
+// each XCD's L2 (workgroups are dealt to the 8 XCDs round-robin, so block b
+// runs on XCD b % 8):
+//
+//   ffn_up_kernel    part p = b % 8 owns TwELL tiles [p*n_t/8, (p+1)*n_t/8).
+//                    One wave per token: x_i in registers, the token's packed
+//                    entries in those tiles collected into a register list,
+//                    W_up rows gathered a few at a time, a = x_i . W_up^T[c]
+//                    reduced with DPP, z = h * a stored at the entry's slot
+//                    (the sparse z, nnz x 4 B; never a dense hidden state).
+//   ffn_down_kernel  part p = b % P owns the d_model slice of y
+//                    [p*D/P, (p+1)*D/P). One wave per token: its (c, z) list,
+//                    the slice of each W_down row, y slice in registers.
+//
+// Overflow rows (a tile count above S) are skipped by both: their dense
+// activation row is split into column chunks of kDenseChunk, each chunk a
+// work item of its own wave writing a partial y row (ffn_dense_rows), and
+// dense_reduce adds the partials in chunk order (deterministic, no atomics).
 #include "row_ops.h"
 #include "twell_kernels.h"
 #include "twell_trace.h"
@@ -24,92 +34,274 @@
 namespace twell {
 namespace {
 
-template <typename TS, int M>
-__device__ __forceinline__ void do_pair(const TS* __restrict__ w_up, const TS* __restrict__ w_down, int D, int F,
-                                        int nch, int lane, const u32x4_t (&xr)[M], float (&acc)[M][8], int c,
-                                        float h, float* a_out) {
-  if ((unsigned)c >= (unsigned)F) return;  // defensive: never gather outside the weights
-  u32x4_t wr[M];
-  load_row<TS, M>(wr, w_up + (size_t)c * D, nch, lane);
-  const float a = wave_sum(dot_rows<TS, M>(xr, wr));
-  if (a_out != nullptr && lane == 0) *a_out = a;
-  const float z = h * a;
-  load_row<TS, M>(wr, w_down + (size_t)c * D, nch, lane);
-  axpy_row<TS, M>(acc, z, wr);
+constexpr int kParts = 8;  // one part per XCD
+
+// Walk TwELL tiles [j0, j1) of token i (not an overflow row) and hand its
+// packed entries to `flush` in lists of at most 64: lane k of the list holds
+// entry k as (global column c, value, slot id j*S+s). The value is the stored
+// activation h (READ_Z = false) or the z written by ffn_up_kernel. The slot
+// loads of all tiles are issued back to back into raw registers and decoded
+// once per list, so a token's metadata costs a couple of memory round trips
+// rather than one per tile.
+template <typename TS, bool READ_Z, typename Flush>
+__device__ __forceinline__ void collect_pairs(const FwdArgs& a, int64_t i, int j0, int j1, int lane, Flush&& flush) {
+  const int64_t N = a.N;
+  const TS* __restrict__ vals = reinterpret_cast<const TS*>(a.vals);
+  int n = 0;
+  int base_l = 0, slot_l = 0;
+  uint32_t col_raw = 0, val_raw = 0;
+  auto emit = [&](int cnt) {
+    const int c = base_l + (int)col_raw;
+    float v;
+    if constexpr (READ_Z) {
+      v = __uint_as_float(val_raw);
+    } else if constexpr (sizeof(TS) == 2) {
+      v = bf16_to_f32((uint16_t)val_raw);
+    } else {
+      v = __uint_as_float(val_raw);
+    }
+    flush(c, v, slot_l, cnt);
+  };
+  for (int jb = j0; jb < j1; jb += 64) {
+    const int jl = jb + lane;
+    const int cnt_l = jl < j1 ? min((int)a.counts[(size_t)jl * N + i], a.slots) : 0;
+    uint64_t nz = ballot(cnt_l > 0);
+    while (nz) {
+      const int t = __ffsll((unsigned long long)nz) - 1;
+      nz &= nz - 1;
+      const int j = jb + t;
+      const int cnt = readlane_i(cnt_l, t);
+      for (int sb = 0; sb < cnt;) {
+        if (n == 64) {
+          emit(64);
+          n = 0;
+        }
+        const int take = min(cnt - sb, 64 - n);
+        if (lane >= n && lane < n + take) {
+          const int slot = j * a.slots + sb + lane - n;
+          const size_t pos = (size_t)slot * N + i;
+          col_raw = a.cols[pos];
+          if constexpr (READ_Z)
+            val_raw = __float_as_uint(a.zbuf[pos]);
+          else if constexpr (sizeof(TS) == 2)
+            val_raw = vals[pos];
+          else
+            val_raw = __float_as_uint(vals[pos]);
+          base_l = j * a.tile_n;
+          slot_l = slot;
+        }
+        n += take;
+        sb += take;
+      }
+    }
+  }
+  if (n > 0) emit(n);
 }
 
-template <typename TS, int M>
-__global__ __launch_bounds__(256) void ffn_fwd_kernel(FwdArgs a, int G) {
-  constexpr int E = ChunkElems<TS>::E;
-  const int lane = threadIdx.x & 63;
-  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int64_t N = a.N;
-  const int D = a.D, nch = D / E;
-  const TS* __restrict__ x = reinterpret_cast<const TS*>(a.x);
-  const TS* __restrict__ w_up = reinterpret_cast<const TS*>(a.w_up);
-  const TS* __restrict__ w_down = reinterpret_cast<const TS*>(a.w_down);
-  u32x4_t xr[M];
-  float acc[M][8];
-  zero_acc<M>(acc);
+// ------------------------------------------------------------------ up: z = h * (x_i . W_up^T[c])
 
-  if (item < N) {
-    const int64_t i = item;
-    const uint16_t* __restrict__ counts = a.counts;
-    for (int jb = 0; jb < a.n_tiles; jb += 64) {
-      const int j = jb + lane;
-      const int c = j < a.n_tiles ? counts[(size_t)j * N + i] : 0;
-      if (ballot(c > a.slots)) return;  // overflow row: handled by the dense chunks
+template <typename TS, int M>
+__global__ __launch_bounds__(256) void ffn_up_kernel(FwdArgs a, int parts) {
+  constexpr int E = ChunkElems<TS>::E;
+  constexpr int U = M <= 4 ? 4 : (M == 8 ? 2 : 1);  // rows in flight per wave
+  const int lane = threadIdx.x & 63;
+  const int part = blockIdx.x % parts;
+  const int64_t i = (int64_t)(blockIdx.x / parts) * 4 + (threadIdx.x >> 6);
+  if (i >= a.N || a.ovf_flag[i]) return;
+  const int j0 = (int)((int64_t)part * a.n_tiles / parts), j1 = (int)((int64_t)(part + 1) * a.n_tiles / parts);
+  const int D = a.D, nch = D / E;
+  const TS* __restrict__ w_up = reinterpret_cast<const TS*>(a.w_up);
+  u32x4_t xr[M];
+  bool have_x = false;
+  auto flush = [&](int c_l, float h_l, int slot_l, int n) {
+    if (!have_x) {
+      load_row<TS, M>(xr, reinterpret_cast<const TS*>(a.x) + (size_t)i * D, nch, lane);
+      have_x = true;
     }
-    load_row<TS, M>(xr, x + (size_t)i * D, nch, lane);
-    const TS* __restrict__ vals = reinterpret_cast<const TS*>(a.vals);
-    for (int jb = 0; jb < a.n_tiles; jb += 64) {
-      const int jl = jb + lane;
-      const int cnt_l = jl < a.n_tiles ? counts[(size_t)jl * N + i] : 0;
-      uint64_t nz = ballot(cnt_l > 0);
-      while (nz) {
-        const int t = __ffsll((unsigned long long)nz) - 1;
-        nz &= nz - 1;
-        const int j = jb + t;
-        const int cnt = readlane_i(cnt_l, t);
-        const size_t base = (size_t)j * a.slots * N + i;
-        // slots are read 64 at a time (S may reach T_n = 128)
-        for (int sb = 0; sb < cnt; sb += 64) {
-          int col_l = 0;
-          float h_l = 0.f;
-          if (sb + lane < cnt) {
-            col_l = a.cols[base + (size_t)(sb + lane) * N];
-            h_l = Store<TS>::load(vals, base + (size_t)(sb + lane) * N);
-          }
-          const int nb = min(64, cnt - sb);
-          for (int s = 0; s < nb; ++s) {
-            const int c = j * a.tile_n + readlane_i(col_l, s);
-            const float h = readlane_f(h_l, s);
-            float* a_out = a.a_save ? a.a_save + base + (size_t)(sb + s) * N : nullptr;
-            do_pair<TS, M>(w_up, w_down, D, a.F, nch, lane, xr, acc, c, h, a_out);
-          }
+    for (int k = 0; k < n; k += U) {
+      u32x4_t wr[U][M];
+      int cs[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = readlane_i(c_l, min(k + u, n - 1));
+        cs[u] = (unsigned)c < (unsigned)a.F ? c : -1;  // a corrupted column contributes nothing
+        load_row<TS, M>(wr[u], w_up + (size_t)max(cs[u], 0) * D, nch, lane);
+      }
+      float dot[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) dot[u] = dot_rows<TS, M>(xr, wr[u]);
+#pragma unroll
+      for (int u = 0; u < U; ++u) dot[u] = wave_sum_dpp(dot[u]);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (k + u >= n) break;
+        const float av = cs[u] >= 0 ? dot[u] : 0.f;
+        const float h = readlane_f(h_l, k + u);
+        const size_t pos = (size_t)readlane_i(slot_l, k + u) * a.N + i;
+        if (lane == 0) {
+          a.zbuf[pos] = h * av;
+          if (a.a_save) a.a_save[pos] = av;
         }
       }
     }
-    store_row<TS, M>(a.y + (size_t)i * D, acc, nch, lane);
-    return;
-  }
+  };
+  collect_pairs<TS, false>(a, i, j0, j1, lane, flush);
+}
 
-  // dense chunk (overflow row o, columns [g*kDenseChunk, ...))
-  const int64_t k = item - N;
+// ------------------------------------------------------------------ down: y_i[slice] = sum z * W_down[c][slice]
+
+// EPL consecutive storage elements per lane, loaded with one or two vector
+// loads and widened to fp32.
+template <typename TS, int EPL> struct Slice;
+template <int EPL> struct Slice<uint16_t, EPL> {
+  static constexpr int W = EPL >= 2 ? EPL / 2 : 1;  // 32-bit words (EPL == 1 uses the low half)
+  uint32_t w[W];
+  __device__ __forceinline__ void load(const uint16_t* p) {
+    if constexpr (EPL == 1) {
+      w[0] = *p;
+    } else if constexpr (EPL == 2) {
+      w[0] = *reinterpret_cast<const uint32_t*>(p);
+    } else if constexpr (EPL == 4) {
+      const uint2 v = *reinterpret_cast<const uint2*>(p);
+      w[0] = v.x; w[1] = v.y;
+    } else {
+#pragma unroll
+      for (int q = 0; q < EPL / 8; ++q) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p + q * 8);
+        w[4 * q] = v.x; w[4 * q + 1] = v.y; w[4 * q + 2] = v.z; w[4 * q + 3] = v.w;
+      }
+    }
+  }
+  __device__ __forceinline__ void fma(float z, float (&acc)[EPL]) const {
+    if constexpr (EPL == 1) {
+      acc[0] = fmaf(z, bf16lo_to_f32(w[0]), acc[0]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < W; ++q) {
+        acc[2 * q] = fmaf(z, bf16lo_to_f32(w[q]), acc[2 * q]);
+        acc[2 * q + 1] = fmaf(z, bf16hi_to_f32(w[q]), acc[2 * q + 1]);
+      }
+    }
+  }
+};
+template <int EPL> struct Slice<float, EPL> {
+  float w[EPL];
+  __device__ __forceinline__ void load(const float* p) {
+    if constexpr (EPL == 1) {
+      w[0] = *p;
+    } else if constexpr (EPL == 2) {
+      const float2 v = *reinterpret_cast<const float2*>(p);
+      w[0] = v.x; w[1] = v.y;
+    } else {
+#pragma unroll
+      for (int q = 0; q < EPL / 4; ++q) {
+        const float4 v = *reinterpret_cast<const float4*>(p + q * 4);
+        w[4 * q] = v.x; w[4 * q + 1] = v.y; w[4 * q + 2] = v.z; w[4 * q + 3] = v.w;
+      }
+    }
+  }
+  __device__ __forceinline__ void fma(float z, float (&acc)[EPL]) const {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = fmaf(z, w[e], acc[e]);
+  }
+};
+
+template <typename TS, int EPL>
+__global__ __launch_bounds__(256) void ffn_down_kernel(FwdArgs a, int P) {
+  constexpr int U = 8;  // rows in flight per wave
+  const int lane = threadIdx.x & 63;
+  const int p = blockIdx.x % P;
+  const int64_t i = (int64_t)(blockIdx.x / P) * 4 + (threadIdx.x >> 6);
+  if (i >= a.N || a.ovf_flag[i]) return;
+  const int D = a.D;
+  const int d0 = (p * 64 + lane) * EPL;
+  const TS* __restrict__ w_down = reinterpret_cast<const TS*>(a.w_down) + d0;
+  float acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  auto flush = [&](int c_l, float z_l, int slot_l, int n) {
+    for (int k = 0; k < n; k += U) {
+      Slice<TS, EPL> w[U];
+      float z[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int kk = min(k + u, n - 1);
+        const int c = readlane_i(c_l, kk);
+        const bool ok = (unsigned)c < (unsigned)a.F && k + u < n;
+        z[u] = ok ? readlane_f(z_l, kk) : 0.f;
+        w[u].load(w_down + (size_t)(ok ? c : 0) * D);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) w[u].fma(z[u], acc);
+    }
+  };
+  collect_pairs<TS, true>(a, i, 0, a.n_tiles, lane, flush);
+  float* dst = a.y + (size_t)i * D + d0;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) dst[e] = acc[e];
+}
+
+// ------------------------------------------------------------------ overflow rows
+
+// Work item (o, g): overflow row o, columns [g*kDenseChunk, ...) of its dense
+// activation row; writes the partial y row part[o][g]. The active columns of
+// each 64-column block are handled in two batched passes: a for U columns at a
+// time (U W_up rows in flight), then y += z * W_down[c] likewise.
+template <typename TS, int M>
+__global__ __launch_bounds__(256) void ffn_dense_rows(FwdArgs a, int G) {
+  constexpr int E = ChunkElems<TS>::E;
+  constexpr int U = M <= 4 ? 4 : (M == 8 ? 2 : 1);
+  const int lane = threadIdx.x & 63;
+  const int64_t k = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int o = (int)(k / G), g = (int)(k % G);
   if (o >= a.ovf_cap || o >= *a.n_ovf) return;
+  const int D = a.D, nch = D / E;
+  const TS* __restrict__ w_up = reinterpret_cast<const TS*>(a.w_up);
+  const TS* __restrict__ w_down = reinterpret_cast<const TS*>(a.w_down);
   const int64_t i = a.ovf_rows[o];
-  load_row<TS, M>(xr, x + (size_t)i * D, nch, lane);
+  u32x4_t xr[M];
+  float acc[M][8];
+  zero_acc<M>(acc);
+  load_row<TS, M>(xr, reinterpret_cast<const TS*>(a.x) + (size_t)i * D, nch, lane);
   const TS* __restrict__ hrow = reinterpret_cast<const TS*>(a.ovf_h) + (size_t)o * a.F;
   const int c0 = g * kDenseChunk, c1 = min(a.F, c0 + kDenseChunk);
   for (int cb = c0; cb < c1; cb += 64) {
     const int c = cb + lane;
     const float h_l = c < c1 ? Store<TS>::load(hrow, c) : 0.f;
-    uint64_t m = ballot(h_l > 0.f);
-    while (m) {
-      const int t = __ffsll((unsigned long long)m) - 1;
-      m &= m - 1;
-      do_pair<TS, M>(w_up, w_down, D, a.F, nch, lane, xr, acc, cb + t, readlane_f(h_l, t), nullptr);
+    const uint64_t m = ballot(h_l > 0.f);
+    const int n = __popcll(m);
+    if (n == 0) continue;
+    // compact the active columns: lane q of the list gets the q-th active one,
+    // found by binary search on prefix popcounts of the ballot
+    int lo = 0, hi = 63;
+    for (int step = 0; step < 6; ++step) {
+      const int mid = (lo + hi) >> 1;
+      const uint64_t below = mid >= 63 ? ~0ull : ((2ull << mid) - 1ull);
+      if (__popcll(m & below) >= lane + 1) hi = mid; else lo = mid + 1;
+    }
+    const int col_l = cb + lo;
+    const float h_q = __shfl(h_l, lo, 64);
+    float z_l = 0.f;
+    for (int q = 0; q < n; q += U) {
+      u32x4_t wr[U][M];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        load_row<TS, M>(wr[u], w_up + (size_t)readlane_i(col_l, min(q + u, n - 1)) * D, nch, lane);
+      float dot[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) dot[u] = wave_sum_dpp(dot_rows<TS, M>(xr, wr[u]));
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (lane == q + u) z_l = h_q * dot[u];
+    }
+    for (int q = 0; q < n; q += U) {
+      u32x4_t wr[U][M];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        load_row<TS, M>(wr[u], w_down + (size_t)readlane_i(col_l, min(q + u, n - 1)) * D, nch, lane);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (q + u < n) axpy_row<TS, M>(acc, readlane_f(z_l, q + u), wr[u]);
     }
   }
   store_row<TS, M>(a.part + ((size_t)o * G + g) * D, acc, nch, lane);
@@ -133,22 +325,63 @@ __global__ __launch_bounds__(256) void dense_reduce(const float* __restrict__ pa
 template <typename TS>
 hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
   constexpr int E = ChunkElems<TS>::E;
-  const int M = pick_m(a.D / E);
-  const int G = (a.F + kDenseChunk - 1) / kDenseChunk;
-  const int64_t items = a.N + (int64_t)a.ovf_cap * G;
-  const dim3 grid((unsigned)((items + 3) / 4));
-  if (items > 0) {
-    switch (M) {
-      case 1: TWELL_LAUNCH("ffn_fwd_kernel", (ffn_fwd_kernel<TS, 1>), grid, 256, 0, s, a, G); break;
-      case 2: TWELL_LAUNCH("ffn_fwd_kernel", (ffn_fwd_kernel<TS, 2>), grid, 256, 0, s, a, G); break;
-      case 4: TWELL_LAUNCH("ffn_fwd_kernel", (ffn_fwd_kernel<TS, 4>), grid, 256, 0, s, a, G); break;
-      case 8: TWELL_LAUNCH("ffn_fwd_kernel", (ffn_fwd_kernel<TS, 8>), grid, 256, 0, s, a, G); break;
-      case 16: TWELL_LAUNCH("ffn_fwd_kernel", (ffn_fwd_kernel<TS, 16>), grid, 256, 0, s, a, G); break;
-      default: return hipErrorInvalidValue;
-    }
+  const int nch = a.D / E;
+  const int M = pick_m(nch);
+  const dim3 blk(256);
+  const int64_t tblocks = (a.N + 3) / 4;
+
+  // up: z at every packed entry of the non-overflow rows
+  const int parts = a.n_tiles < kParts ? a.n_tiles : kParts;
+  const dim3 gup((unsigned)(tblocks * parts));
+  switch (M) {
+    case 1: TWELL_LAUNCH("ffn_up_kernel", (ffn_up_kernel<TS, 1>), gup, blk, 0, s, a, parts); break;
+    case 2: TWELL_LAUNCH("ffn_up_kernel", (ffn_up_kernel<TS, 2>), gup, blk, 0, s, a, parts); break;
+    case 4: TWELL_LAUNCH("ffn_up_kernel", (ffn_up_kernel<TS, 4>), gup, blk, 0, s, a, parts); break;
+    case 8: TWELL_LAUNCH("ffn_up_kernel", (ffn_up_kernel<TS, 8>), gup, blk, 0, s, a, parts); break;
+    case 16: TWELL_LAUNCH("ffn_up_kernel", (ffn_up_kernel<TS, 16>), gup, blk, 0, s, a, parts); break;
+    default: return hipErrorInvalidValue;
   }
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess || a.ovf_cap == 0) return err;
+  if (err != hipSuccess) return err;
+
+  // down: y rows of the non-overflow rows, d_model cut into P slices of 64*EPL
+  constexpr int kMaxEpl = sizeof(TS) == 2 ? 16 : 8;
+  int epl = 1;
+  for (int e = kMaxEpl; e >= 1; e >>= 1)
+    if (a.D % (64 * e) == 0 && a.D / (64 * e) >= kParts) {
+      epl = e;
+      break;
+    }
+  const int P = a.D / (64 * epl);
+  const dim3 gdn((unsigned)(tblocks * P));
+  switch (epl) {
+    case 1: TWELL_LAUNCH("ffn_down_kernel", (ffn_down_kernel<TS, 1>), gdn, blk, 0, s, a, P); break;
+    case 2: TWELL_LAUNCH("ffn_down_kernel", (ffn_down_kernel<TS, 2>), gdn, blk, 0, s, a, P); break;
+    case 4: TWELL_LAUNCH("ffn_down_kernel", (ffn_down_kernel<TS, 4>), gdn, blk, 0, s, a, P); break;
+    case 8: TWELL_LAUNCH("ffn_down_kernel", (ffn_down_kernel<TS, 8>), gdn, blk, 0, s, a, P); break;
+    case 16:
+      if constexpr (sizeof(TS) == 2) {
+        TWELL_LAUNCH("ffn_down_kernel", (ffn_down_kernel<TS, 16>), gdn, blk, 0, s, a, P);
+        break;
+      }
+      return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+
+  // overflow rows: dense chunks + fixed-order reduction into y
+  if (a.ovf_cap == 0) return hipSuccess;
+  const int G = (a.F + kDenseChunk - 1) / kDenseChunk;
+  const dim3 gov((unsigned)(((int64_t)a.ovf_cap * G + 3) / 4));
+  switch (M) {
+    case 1: TWELL_LAUNCH("ffn_dense_rows", (ffn_dense_rows<TS, 1>), gov, blk, 0, s, a, G); break;
+    case 2: TWELL_LAUNCH("ffn_dense_rows", (ffn_dense_rows<TS, 2>), gov, blk, 0, s, a, G); break;
+    case 4: TWELL_LAUNCH("ffn_dense_rows", (ffn_dense_rows<TS, 4>), gov, blk, 0, s, a, G); break;
+    case 8: TWELL_LAUNCH("ffn_dense_rows", (ffn_dense_rows<TS, 8>), gov, blk, 0, s, a, G); break;
+    case 16: TWELL_LAUNCH("ffn_dense_rows", (ffn_dense_rows<TS, 16>), gov, blk, 0, s, a, G); break;
+    default: return hipErrorInvalidValue;
+  }
+  if ((err = hipGetLastError()) != hipSuccess) return err;
   return launch_dense_reduce(a.part, a.ovf_rows, a.n_ovf, a.ovf_cap, G, a.D, a.y, s);
 }
 

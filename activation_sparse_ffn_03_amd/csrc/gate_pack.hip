@@ -7,10 +7,11 @@
 // conversion pass, no extra round trip through global memory).
 //
 // Kernels
-//   gate_mfma_bf16   256x128 output tile per 256-thread workgroup, 4 waves of
-//                    128x64, v_mfma_f32_16x16x32_bf16, K-loop of 64 with two
-//                    LDS stages; epilogue stages the fp32 tile in LDS (two
-//                    passes of 128 rows) and packs it.
+//   gate_mfma_bf16   BM x BN output tile per workgroup (256x256 with 8 waves,
+//                    or 128x128 with 4), v_mfma_f32_16x16x32_bf16, K-loop of 64
+//                    with two LDS stages; XCD-aware tile order; the epilogue
+//                    stages the fp32 tile in LDS one 128-column group at a time
+//                    and packs it.
 //   gate_simt_f32    64x128 fp32 tile, plain FMA (fp32 storage only).
 //   pack_from_g      64x128 tile of a given pre-activation (test entry).
 //   ovf_flags        overflow flag of every row from its true tile counts
@@ -24,12 +25,11 @@
 namespace twell {
 namespace {
 
-constexpr int BM = 256, BN = 128, BK = 64;
-constexpr int AS = BK + 8;   // LDS row stride in bf16 (144 B: 16 consecutive rows hit 16 distinct bank groups)
-constexpr int GS = BN + 4;   // LDS row stride of the fp32 epilogue tile (floats)
-constexpr int EPI_ROWS = 128;
-constexpr int LDS_MFMA_BYTES = (2 * BM * AS + 2 * BN * AS) * 2;
-static_assert(EPI_ROWS * GS * 4 <= LDS_MFMA_BYTES, "epilogue tile must fit in the GEMM buffers");
+constexpr int BK = 64;
+constexpr int AS = BK + 8;      // LDS row stride in bf16 (144 B: 16 consecutive rows hit 16 distinct bank groups)
+constexpr int kPackCols = 128;  // columns one pack_epilogue call covers (two 64-lane ballots)
+constexpr int BN = kPackCols;   // N tile of the fp32 / pack_from_g kernels
+constexpr int GS = kPackCols + 4;  // LDS row stride of the fp32 epilogue tile (floats)
 
 constexpr int SBM = 64;      // rows of the fp32 / pack_from_g tiles
 constexpr int SBK = 16;
@@ -53,100 +53,203 @@ struct Epi {
 
 __device__ __forceinline__ uint64_t mask_below(int n) { return n >= 64 ? ~0ull : ((1ull << n) - 1ull); }
 
-// popcount of bits [a, b) of the 128-bit value (m1:m0), 0 <= a <= b <= 128
-__device__ __forceinline__ int popc_range128(uint64_t m0, uint64_t m1, int a, int b) {
-  int lo0 = min(a, 64), hi0 = min(b, 64);
-  int lo1 = max(a, 64) - 64, hi1 = max(b, 64) - 64;
-  int r = 0;
-  if (hi0 > lo0) r += __popcll(m0 & mask_below(hi0) & ~mask_below(lo0));
-  if (hi1 > lo1) r += __popcll(m1 & mask_below(hi1) & ~mask_below(lo1));
-  return r;
-}
-
 __device__ __forceinline__ int dense_valid(const Epi& e) { return min(*e.n_ovf, e.cap); }
 
-// Pack `rows` rows of the fp32 tile Gs (row stride GS) whose first logical row
-// is row0 and first column n0. Logical rows are tokens (MODE_PACK) or
-// positions in the overflow list (MODE_DENSE). One wave per row: lane l owns
-// columns n0+l and n0+64+l; two ballots give the row's 128-bit active mask and
-// a masked popcount gives every active column its slot inside its tile.
+// Stage the threshold and the token of logical rows [m0, m0 + nrows) of a tile
+// in LDS (token -1 past the last valid row), so the epilogue reads them
+// without a dependent global load per row. Logical rows are tokens
+// (MODE_PACK) or positions in the overflow list (MODE_DENSE).
+__device__ void stage_rows(int64_t m0, int nrows, const Epi& e, float* ts, int32_t* toks) {
+  const int64_t limit = (e.mode == MODE_DENSE) ? (int64_t)dense_valid(e) : e.N;
+  for (int r = threadIdx.x; r < nrows; r += blockDim.x) {
+    const int64_t lr = m0 + r;
+    int32_t tok = -1;
+    float tv = 0.f;
+    if (lr < limit) {
+      tok = (e.mode == MODE_DENSE) ? e.rows[lr] : (int32_t)lr;
+      tv = e.t[tok];
+    }
+    ts[r] = tv;
+    toks[r] = tok;
+  }
+}
+
+// Dense activation rows of overflow rows (MODE_DENSE): one wave per row of the
+// fp32 tile Gs, lane l writing columns n0+l and n0+64+l of ovf_h row row0+r.
 template <typename TS>
-__device__ void pack_epilogue(const float* Gs, int rows, int64_t row0, int n0, const Epi& e) {
+__device__ void dense_rows_out(const float* Gs, int rows, int64_t row0, int n0, const Epi& e, const float* ts,
+                               const int32_t* toks) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  const int tn = e.tile_n;
-  const int tpb = BN / tn;
-  const int nvalid = (e.mode == MODE_DENSE) ? dense_valid(e) : 0;
   for (int r = wave; r < rows; r += nw) {
-    const int64_t lr = row0 + r;
-    int64_t tok;
-    if (e.mode == MODE_PACK) {
-      if (lr >= e.N) break;
-      tok = lr;
-    } else {
-      if (lr >= nvalid) break;
-      tok = e.rows[lr];
-    }
-    const float tv = e.t[tok];
-    const float g0 = Gs[r * GS + lane], g1 = Gs[r * GS + 64 + lane];
-    const int c0 = n0 + lane, c1 = n0 + 64 + lane;
-    const bool a0 = (c0 < e.F) && (g0 > tv);
-    const bool a1 = (c1 < e.F) && (g1 > tv);
-    if (e.mode == MODE_DENSE) {
-      TS* oh = reinterpret_cast<TS*>(e.ovf_h) + (size_t)lr * e.F;
-      if (c0 < e.F) oh[c0] = a0 ? Store<TS>::from_f32(g0 - tv) : TS(0);
-      if (c1 < e.F) oh[c1] = a1 ? Store<TS>::from_f32(g1 - tv) : TS(0);
-      continue;
-    }
-    if (e.g_dump) {
-      float* gd = e.g_dump + (size_t)tok * e.F;
-      if (c0 < e.F) gd[c0] = g0;
-      if (c1 < e.F) gd[c1] = g1;
-    }
-    const uint64_t m0 = ballot(a0), m1 = ballot(a1);
-    const int ts0 = (lane / tn) * tn, ts1 = ((64 + lane) / tn) * tn;
-    TS* vals = reinterpret_cast<TS*>(e.vals);
-    if (a0) {
-      const int p = popc_range128(m0, m1, ts0, lane);
-      if (p < e.slots) {
-        const size_t off = ((size_t)((n0 + ts0) / tn) * e.slots + p) * (size_t)e.N + tok;
-        vals[off] = Store<TS>::from_f32(g0 - tv);
-        e.cols[off] = uint16_t(lane - ts0);
-      }
-    }
-    if (a1) {
-      const int p = popc_range128(m0, m1, ts1, 64 + lane);
-      if (p < e.slots) {
-        const size_t off = ((size_t)((n0 + ts1) / tn) * e.slots + p) * (size_t)e.N + tok;
-        vals[off] = Store<TS>::from_f32(g1 - tv);
-        e.cols[off] = uint16_t(64 + lane - ts1);
-      }
-    }
-    if (lane < tpb) {
-      const int jt = n0 / tn + lane;
-      if (jt * tn < e.F) e.counts[(size_t)jt * e.N + tok] = uint16_t(popc_range128(m0, m1, lane * tn, lane * tn + tn));
+    if (toks[r] < 0) break;  // rows past the last valid one
+    const float tv = ts[r];
+    TS* oh = reinterpret_cast<TS*>(e.ovf_h) + (size_t)(row0 + r) * e.F;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = n0 + h * 64 + lane;
+      const float g = Gs[r * GS + h * 64 + lane];
+      if (c < e.F) oh[c] = g > tv ? Store<TS>::from_f32(g - tv) : TS(0);
     }
   }
 }
 
+// Debug copy of g (g_dump): one wave per row, coalesced.
+__device__ void dump_rows(const float* Gs, int rows, int n0, const Epi& e, const int32_t* toks) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  for (int r = wave; r < rows; r += nw) {
+    const int32_t tok = toks[r];
+    if (tok < 0) break;
+    float* gd = e.g_dump + (size_t)tok * e.F;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = n0 + h * 64 + lane;
+      if (c < e.F) gd[c] = Gs[r * GS + h * 64 + lane];
+    }
+  }
+}
+
+// TwELL pack of `rows` rows of the fp32 tile Gs (row stride GS) whose first
+// column is n0; ts / toks hold the threshold and token of each row (staged by
+// stage_rows). One lane per row: the lane reads its row four columns at a time
+// and builds the row's 128-bit active mask (g > t, columns < F); then, for each
+// TwELL tile of the 128 columns, iteration s of a wave-uniform loop pops every
+// lane's lowest remaining set bit into slot s. Lanes are consecutive tokens,
+// so the slot-major stores of one iteration are contiguous.
+template <typename TS>
+__device__ void pack_lanes(const float* Gs, int rows, int n0, const Epi& e, const float* ts, const int32_t* toks) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int tn = e.tile_n, S = e.slots;
+  const int64_t N = e.N;
+  const int ncol = min(kPackCols, e.F - n0);
+  if (ncol <= 0) return;  // a 128-column group past the last column of d_ff
+  TS* vals = reinterpret_cast<TS*>(e.vals);
+  for (int rb = wave * 64; rb < rows; rb += nw * 64) {
+    const int r = rb + lane;
+    const int32_t tk = r < rows ? toks[r] : -1;
+    const bool valid = tk >= 0;
+    if (!ballot(valid)) break;  // rows past the last valid one
+    const float tv = valid ? ts[r] : 0.f;
+    uint64_t m[2] = {0ull, 0ull};
+    if (valid) {
+      const float* g = Gs + r * GS;
+#pragma unroll
+      for (int q = 0; q < kPackCols / 4; ++q) {
+        const float4 v = *reinterpret_cast<const float4*>(g + 4 * q);
+        const uint64_t b = (uint64_t)(v.x > tv) | ((uint64_t)(v.y > tv) << 1) | ((uint64_t)(v.z > tv) << 2) |
+                           ((uint64_t)(v.w > tv) << 3);
+        m[q / 16] |= b << (4 * (q % 16));
+      }
+      m[0] &= mask_below(ncol);
+      m[1] &= ncol > 64 ? mask_below(ncol - 64) : 0ull;
+    }
+    for (int t0 = 0; t0 < kPackCols; t0 += tn) {
+      const int jt = (n0 + t0) / tn;
+      if (jt * tn >= e.F) break;
+      uint64_t s0, s1;
+      if (tn == 128) {
+        s0 = m[0];
+        s1 = m[1];
+      } else {
+        s0 = (m[t0 >> 6] >> (t0 & 63)) & mask_below(tn);
+        s1 = 0ull;
+      }
+      const size_t tok = (size_t)(valid ? tk : 0);
+      if (valid) e.counts[(size_t)jt * N + tok] = (uint16_t)(__popcll(s0) + __popcll(s1));
+      for (int sl = 0; sl < S; ++sl) {
+        const bool more = valid && (s0 | s1);
+        if (!ballot(more)) break;
+        if (more) {
+          int bit;
+          if (s0) {
+            bit = __ffsll((unsigned long long)s0) - 1;
+            s0 &= s0 - 1;
+          } else {
+            bit = 64 + __ffsll((unsigned long long)s1) - 1;
+            s1 &= s1 - 1;
+          }
+          const size_t pos = ((size_t)jt * S + sl) * N + tok;
+          vals[pos] = Store<TS>::from_f32(Gs[r * GS + t0 + bit] - tv);
+          e.cols[pos] = (uint16_t)bit;
+        }
+      }
+    }
+  }
+}
+
+// Epilogue of one (rows x 128-column) block of g held in LDS.
+template <typename TS>
+__device__ void pack_epilogue(const float* Gs, int rows, int64_t row0, int n0, const Epi& e, const float* ts,
+                              const int32_t* toks) {
+  if (e.mode == MODE_DENSE) {
+    dense_rows_out<TS>(Gs, rows, row0, n0, e, ts, toks);
+    return;
+  }
+  if (e.g_dump) dump_rows(Gs, rows, n0, e, toks);
+  pack_lanes<TS>(Gs, rows, n0, e, ts, toks);
+}
+
 // ---------------------------------------------------------------- bf16 MFMA GEMM
 
-// g tile = x[m0:m0+256, :] . w[n0:n0+128, :]^T. In MODE_DENSE, A rows are
-// gathered through the overflow list. Both operands are K-contiguous; each
-// thread moves 16-byte chunks global -> registers -> LDS.
-template <int MODE>
-__global__ __launch_bounds__(256, 1) void gate_mfma_bf16(const uint16_t* __restrict__ x,
-                                                        const uint16_t* __restrict__ w, int D,
-                                                        int n_col_blocks, Epi e) {
-  __shared__ __attribute__((aligned(16))) char smem[LDS_MFMA_BYTES];
+// Block tile BM x BN of g = x . w^T, WGM x WGN waves, each owning a
+// (BM/WGM) x (BN/WGN) sub-tile of 16x16 v_mfma_f32_16x16x32_bf16 fragments.
+// K advances by BK = 64 through two LDS stages. Global loads go through
+// registers: with PF = 2 two register sets alternate, so the load of K-step
+// k+2 is issued while step k feeds the matrix cores and has two steps of
+// MFMA work to arrive in.
+template <int BM_, int BN_, int WGM_, int WGN_, int PF_ = 1>
+struct MfmaCfg {
+  static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_;
+  static constexpr int PF = PF_;  // K-steps fetched ahead into registers (1 or 2)
+  static constexpr int NT = WGM * WGN * 64;
+  static constexpr int WM = BM / WGM, WN = BN / WGN;
+  static constexpr int FM = WM / 16, FN = WN / 16;
+  static constexpr int A_CH = BM * (BK / 8) / NT;  // 16-byte chunks per thread per stage
+  static constexpr int B_CH = BN * (BK / 8) / NT;
+  static constexpr int LDS = (2 * BM * AS + 2 * BN * AS) * 2;
+  static constexpr int EPI_FIT = LDS / (GS * 4);
+  static constexpr int EPI_ROWS = EPI_FIT >= 256 && BM >= 256 ? 256 : EPI_FIT >= 128 && BM >= 128 ? 128 : 64;
+  static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile must be whole fragments");
+  static_assert(BM * (BK / 8) % NT == 0 && BN * (BK / 8) % NT == 0, "stage must split evenly over threads");
+  static_assert(BN % 128 == 0, "N tile must be whole 128-column pack groups");
+  static_assert(BM % EPI_ROWS == 0 && EPI_ROWS * GS * 4 <= LDS, "epilogue staging must fit");
+  static_assert(LDS + BM * 8 <= 160 * 1024, "LDS budget of a gfx950 workgroup");
+};
+
+// Workgroup -> output tile. Workgroups are dealt to the 8 XCDs round-robin;
+// the ids are renumbered so that each XCD gets one contiguous run of tiles,
+// and the run is walked in groups of `kGroupM` row blocks (column-major inside
+// a group), so the tiles an XCD has in flight share A and B rows in its L2.
+constexpr int kXcds = 8;
+constexpr int kGroupM = 8;
+__device__ __forceinline__ void tile_of_block(int b, int nblocks, int mbc, int ncb, int& mb, int& nb) {
+  const int q = nblocks / kXcds, r = nblocks % kXcds, x = b % kXcds;
+  const int L = x * q + min(x, r) + b / kXcds;
+  const int per_group = kGroupM * ncb;
+  const int first_m = (L / per_group) * kGroupM;
+  const int gsz = min(mbc - first_m, kGroupM);
+  const int in = L % per_group;
+  mb = first_m + in % gsz;
+  nb = in / gsz;
+}
+
+// In MODE_DENSE, A rows are gathered through the overflow list. Both operands
+// are K-contiguous.
+template <class C, int MODE>
+__global__ __launch_bounds__(C::NT, 1) void gate_mfma_bf16(const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ w, int D, int mbc,
+                                                          int ncb, Epi e) {
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+  __shared__ float ts[C::BM];
+  __shared__ int32_t toks[C::BM];
   uint16_t* As = reinterpret_cast<uint16_t*>(smem);
-  uint16_t* Bs = As + 2 * BM * AS;
+  uint16_t* Bs = As + 2 * C::BM * AS;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int nb_id = blockIdx.x % n_col_blocks;
-  const int mb_id = blockIdx.x / n_col_blocks;
-  const int64_t m0 = (int64_t)mb_id * BM;
-  const int n0 = nb_id * BN;
+  const int wm = wave / C::WGN, wn = wave % C::WGN;
+  int mb_id, nb_id;
+  tile_of_block(blockIdx.x, gridDim.x, mbc, ncb, mb_id, nb_id);
+  const int64_t m0 = (int64_t)mb_id * C::BM;
+  const int n0 = nb_id * C::BN;
 
   int64_t mlimit;
   if (MODE == MODE_DENSE) {
@@ -155,13 +258,13 @@ __global__ __launch_bounds__(256, 1) void gate_mfma_bf16(const uint16_t* __restr
   } else {
     mlimit = e.N;
   }
+  stage_rows(m0, C::BM, e, ts, toks);  // visible after the first barrier below
 
-  // Global source rows for this thread's A chunks (8) and B chunks (4).
-  const uint16_t* a_src[8];
-  bool a_ok[8];
+  const uint16_t* a_src[C::A_CH];
+  bool a_ok[C::A_CH];
 #pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    const int q = tid + 256 * r;
+  for (int r = 0; r < C::A_CH; ++r) {
+    const int q = tid + C::NT * r;
     const int row = q >> 3, kc = q & 7;
     const int64_t lr = m0 + row;
     a_ok[r] = lr < mlimit;
@@ -169,95 +272,141 @@ __global__ __launch_bounds__(256, 1) void gate_mfma_bf16(const uint16_t* __restr
     if (MODE == MODE_DENSE) tok = a_ok[r] ? (int64_t)e.rows[lr] : 0;
     a_src[r] = x + (a_ok[r] ? tok : 0) * (int64_t)D + kc * 8;
   }
-  const uint16_t* b_src[4];
-  bool b_ok[4];
+  const uint16_t* b_src[C::B_CH];
+  bool b_ok[C::B_CH];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int q = tid + 256 * r;
+  for (int r = 0; r < C::B_CH; ++r) {
+    const int q = tid + C::NT * r;
     const int row = q >> 3, kc = q & 7;
     b_ok[r] = (n0 + row) < e.F;
     b_src[r] = w + (int64_t)(b_ok[r] ? n0 + row : 0) * D + kc * 8;
   }
 
-  u32x4_t ra[8], rb[4];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int r = 0; r < 8; ++r)
-      ra[r] = a_ok[r] ? *reinterpret_cast<const u32x4_t*>(a_src[r] + k0) : u32x4_t{0, 0, 0, 0};
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      rb[r] = b_ok[r] ? *reinterpret_cast<const u32x4_t*>(b_src[r] + k0) : u32x4_t{0, 0, 0, 0};
+  struct Regs {
+    u32x4_t a[C::A_CH], b[C::B_CH];
   };
-  auto lstore = [&](int buf) {
-    uint16_t* A = As + buf * BM * AS;
-    uint16_t* B = Bs + buf * BN * AS;
+  auto gload = [&](Regs& R, int k0) {
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int q = tid + 256 * r;
-      *reinterpret_cast<u32x4_t*>(A + (q >> 3) * AS + (q & 7) * 8) = ra[r];
+    for (int r = 0; r < C::A_CH; ++r)
+      R.a[r] = a_ok[r] ? *reinterpret_cast<const u32x4_t*>(a_src[r] + k0) : u32x4_t{0, 0, 0, 0};
+#pragma unroll
+    for (int r = 0; r < C::B_CH; ++r)
+      R.b[r] = b_ok[r] ? *reinterpret_cast<const u32x4_t*>(b_src[r] + k0) : u32x4_t{0, 0, 0, 0};
+  };
+  auto lstore = [&](const Regs& R, int buf) {
+    uint16_t* A = As + buf * C::BM * AS;
+    uint16_t* B = Bs + buf * C::BN * AS;
+#pragma unroll
+    for (int r = 0; r < C::A_CH; ++r) {
+      const int q = tid + C::NT * r;
+      *reinterpret_cast<u32x4_t*>(A + (q >> 3) * AS + (q & 7) * 8) = R.a[r];
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int q = tid + 256 * r;
-      *reinterpret_cast<u32x4_t*>(B + (q >> 3) * AS + (q & 7) * 8) = rb[r];
+    for (int r = 0; r < C::B_CH; ++r) {
+      const int q = tid + C::NT * r;
+      *reinterpret_cast<u32x4_t*>(B + (q >> 3) * AS + (q & 7) * 8) = R.b[r];
     }
   };
 
-  f32x4_t acc[8][4];
+  f32x4_t acc[C::FM][C::FN];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int KT = D / BK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < KT; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < KT) gload((kt + 1) * BK);
-    const uint16_t* A = As + buf * BM * AS;
-    const uint16_t* B = Bs + buf * BN * AS;
+  auto compute = [&](int buf) {
+    const uint16_t* A = As + buf * C::BM * AS;
+    const uint16_t* B = Bs + buf * C::BN * AS;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int kc = ks * 4 + (lane >> 4);
-      bf16x8_t af[8], bfr[4];
+      bf16x8_t af[C::FM], bfr[C::FN];
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        af[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(A + (wm * 128 + i * 16 + (lane & 15)) * AS + kc * 8));
+      for (int i = 0; i < C::FM; ++i)
+        af[i] = __builtin_bit_cast(
+            bf16x8_t, *reinterpret_cast<const u32x4_t*>(A + (wm * C::WM + i * 16 + (lane & 15)) * AS + kc * 8));
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bfr[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(B + (wn * 64 + j * 16 + (lane & 15)) * AS + kc * 8));
+      for (int j = 0; j < C::FN; ++j)
+        bfr[j] = __builtin_bit_cast(
+            bf16x8_t, *reinterpret_cast<const u32x4_t*>(B + (wn * C::WN + j * 16 + (lane & 15)) * AS + kc * 8));
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < C::FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < KT) lstore(buf ^ 1);
+  };
+
+  const int KT = D / BK;
+  Regs R0, R1;
+  if constexpr (C::PF == 1) {
+    gload(R0, 0);
+    lstore(R0, 0);
     __syncthreads();
+    for (int kt = 0; kt < KT; ++kt) {
+      if (kt + 1 < KT) gload(R0, (kt + 1) * BK);
+      compute(kt & 1);
+      if (kt + 1 < KT) lstore(R0, (kt + 1) & 1);
+      __syncthreads();
+    }
+  } else {
+    // R0 holds even K-steps, R1 odd ones; LDS buffer = K-step parity.
+    gload(R0, 0);
+    lstore(R0, 0);
+    if (KT > 1) gload(R1, BK);
+    __syncthreads();
+    for (int kt = 0; kt < KT; kt += 2) {
+      if (kt + 2 < KT) gload(R0, (kt + 2) * BK);
+      compute(0);
+      if (kt + 1 < KT) lstore(R1, 1);
+      __syncthreads();
+      if (kt + 1 >= KT) break;
+      if (kt + 3 < KT) gload(R1, (kt + 3) * BK);
+      compute(1);
+      if (kt + 2 < KT) lstore(R0, 0);
+      __syncthreads();
+    }
   }
 
-  // Epilogue: two passes of 128 rows through an fp32 LDS tile.
+  // Epilogue: the fp32 tile goes through LDS one (EPI_ROWS x 128-column) block
+  // at a time; each block is packed by pack_epilogue.
   float* Gs = reinterpret_cast<float*>(smem);
 #pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    if (wm == pass) {
+  for (int cg = 0; cg < C::BN / kPackCols; ++cg) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+    for (int p0 = 0; p0 < C::BM; p0 += C::EPI_ROWS) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+      for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            // 16x16 MFMA result: lane l holds rows 4*(l>>4)+r of column l&15
-            const int row = i * 16 + 4 * (lane >> 4) + r;
-            const int col = wn * 64 + j * 16 + (lane & 15);
-            Gs[row * GS + col] = acc[i][j][r];
-          }
+        for (int j = 0; j < C::FN; ++j) {
+          // 16x16 MFMA result: lane l holds rows 4*(l>>4)+r of column l&15
+          const int rbase = wm * C::WM + i * 16 - p0;
+          const int cbase = wn * C::WN + j * 16 - cg * kPackCols;
+          if (rbase < 0 || rbase >= C::EPI_ROWS || cbase < 0 || cbase >= kPackCols) continue;
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            Gs[(rbase + 4 * (lane >> 4) + r) * GS + cbase + (lane & 15)] = acc[i][j][r];
+        }
+      __syncthreads();
+      pack_epilogue<uint16_t>(Gs, C::EPI_ROWS, m0 + p0, n0 + cg * kPackCols, e, ts + p0, toks + p0);
+      __syncthreads();
     }
-    __syncthreads();
-    pack_epilogue<uint16_t>(Gs, EPI_ROWS, m0 + pass * EPI_ROWS, n0, e);
-    __syncthreads();
   }
+}
+
+// Tile configurations of the bf16 gate GEMM. Every configuration accumulates
+// each output element over K in the same order (32-wide MFMA steps, ascending
+// K), so they all produce bit-identical g; the launcher picks by size.
+using GateBig = MfmaCfg<256, 256, 4, 2>;    // 8 waves, 64x128 per wave
+using GateSmall = MfmaCfg<128, 128, 2, 2>;  // 4 waves, 64x64 per wave
+// Problems with at least this many 256x256 tiles (three per CU) use GateBig.
+constexpr int64_t kBigTileMin = 768;
+
+template <class C, int MODE>
+void launch_mfma(const GateArgs& a, int64_t rows, const Epi& e, hipStream_t s, const char* name) {
+  const int mbc = (int)((rows + C::BM - 1) / C::BM), nbc = (a.F + C::BN - 1) / C::BN;
+  TWELL_LAUNCH(name, (gate_mfma_bf16<C, MODE>), dim3(mbc * nbc), C::NT, 0, s, (const uint16_t*)a.x,
+               (const uint16_t*)a.w, a.D, mbc, nbc, e);
 }
 
 // ---------------------------------------------------------------- fp32 SIMT GEMM
@@ -268,6 +417,8 @@ __global__ __launch_bounds__(256) void gate_simt_f32(const float* __restrict__ x
   __shared__ float Ak[SBK][SBM + 4];
   __shared__ float Bk[SBK][BN + 4];
   __shared__ float Gs[SBM * GS];
+  __shared__ float ts[SBM];
+  __shared__ int32_t toks[SBM];
   const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
   const int nb_id = blockIdx.x % n_col_blocks;
   const int64_t m0 = (int64_t)(blockIdx.x / n_col_blocks) * SBM;
@@ -277,6 +428,7 @@ __global__ __launch_bounds__(256) void gate_simt_f32(const float* __restrict__ x
     mlimit = dense_valid(e);
     if (m0 >= mlimit) return;
   }
+  stage_rows(m0, SBM, e, ts, toks);  // visible after the first barrier of the K loop
   float acc[4][8];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -321,7 +473,7 @@ __global__ __launch_bounds__(256) void gate_simt_f32(const float* __restrict__ x
 #pragma unroll
     for (int j = 0; j < 8; ++j) Gs[(ty * 4 + i) * GS + tx * 8 + j] = acc[i][j];
   __syncthreads();
-  pack_epilogue<float>(Gs, SBM, m0, n0, e);
+  pack_epilogue<float>(Gs, SBM, m0, n0, e, ts, toks);
 }
 
 // ---------------------------------------------------------------- pack from a given g
@@ -329,6 +481,8 @@ __global__ __launch_bounds__(256) void gate_simt_f32(const float* __restrict__ x
 template <typename TS, int MODE>
 __global__ __launch_bounds__(256) void pack_from_g(const float* __restrict__ g, int n_col_blocks, Epi e) {
   __shared__ float Gs[SBM * GS];
+  __shared__ float ts[SBM];
+  __shared__ int32_t toks[SBM];
   const int tid = threadIdx.x;
   const int n0 = (blockIdx.x % n_col_blocks) * BN;
   const int64_t m0 = (int64_t)(blockIdx.x / n_col_blocks) * SBM;
@@ -337,6 +491,7 @@ __global__ __launch_bounds__(256) void pack_from_g(const float* __restrict__ g, 
     mlimit = dense_valid(e);
     if (m0 >= mlimit) return;
   }
+  stage_rows(m0, SBM, e, ts, toks);
   for (int q = tid; q < SBM * BN; q += 256) {
     const int row = q / BN, col = q % BN;
     const int64_t lr = m0 + row;
@@ -348,7 +503,7 @@ __global__ __launch_bounds__(256) void pack_from_g(const float* __restrict__ g, 
     Gs[row * GS + col] = v;
   }
   __syncthreads();
-  pack_epilogue<TS>(Gs, SBM, m0, n0, e);
+  pack_epilogue<TS>(Gs, SBM, m0, n0, e, ts, toks);
 }
 
 // ---------------------------------------------------------------- overflow rows
@@ -390,8 +545,11 @@ hipError_t launch_gate_pack(const GateArgs& a, hipStream_t s) {
     else
       TWELL_LAUNCH("pack_from_g", (pack_from_g<float, MODE_PACK>), dim3(mb * ncb), 256, 0, s, a.g_in, ncb, e);
   } else if (a.is_bf16) {
-    const int64_t mb = (a.N + BM - 1) / BM;
-    TWELL_LAUNCH("gate_mfma_bf16", gate_mfma_bf16<MODE_PACK>, dim3(mb * ncb), 256, 0, s, (const uint16_t*)a.x, (const uint16_t*)a.w, a.D, ncb, e);
+    const int64_t big_tiles = ((a.N + 255) / 256) * ((a.F + 255) / 256);
+    if (big_tiles >= kBigTileMin)
+      launch_mfma<GateBig, MODE_PACK>(a, a.N, e, s, "gate_mfma_bf16");
+    else
+      launch_mfma<GateSmall, MODE_PACK>(a, a.N, e, s, "gate_mfma_bf16");
   } else {
     const int64_t mb = (a.N + SBM - 1) / SBM;
     TWELL_LAUNCH("gate_simt_f32", gate_simt_f32<MODE_PACK>, dim3(mb * ncb), 256, 0, s, (const float*)a.x, (const float*)a.w, a.D, ncb, e);
@@ -413,8 +571,7 @@ hipError_t launch_gate_pack(const GateArgs& a, hipStream_t s) {
     else
       TWELL_LAUNCH("pack_from_g_rows", (pack_from_g<float, MODE_DENSE>), dim3(mb * ncb), 256, 0, s, a.g_in, ncb, e);
   } else if (a.is_bf16) {
-    const int64_t mb = (a.ovf_cap + BM - 1) / BM;
-    TWELL_LAUNCH("gate_mfma_bf16_rows", gate_mfma_bf16<MODE_DENSE>, dim3(mb * ncb), 256, 0, s, (const uint16_t*)a.x, (const uint16_t*)a.w, a.D, ncb, e);
+    launch_mfma<GateSmall, MODE_DENSE>(a, a.ovf_cap, e, s, "gate_mfma_bf16_rows");
   } else {
     const int64_t mb = (a.ovf_cap + SBM - 1) / SBM;
     TWELL_LAUNCH("gate_simt_f32_rows", gate_simt_f32<MODE_DENSE>, dim3(mb * ncb), 256, 0, s, (const float*)a.x, (const float*)a.w, a.D, ncb, e);

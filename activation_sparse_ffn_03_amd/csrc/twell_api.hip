@@ -147,7 +147,7 @@ twell_status twell_ffn_fwd(const twell_dims* dims, twell_dtype dtype, const twel
   TWELL_CHECK_PTR(y, (size_t)s.N * s.D * 4, "y");
   if (a_save != nullptr) TWELL_CHECK_PTR(a_save, z.a_save, "a_save");
   if (ws_bytes < z.ws_fwd) return fail(TWELL_ERR_WORKSPACE, "forward workspace smaller than twell_sizes.ws_fwd");
-  if (z.ws_fwd > 0 && twell::bad_ptr(ws, z.ws_fwd))
+  if (twell::bad_ptr(ws, z.ws_fwd))
     return fail(TWELL_ERR_WORKSPACE, "forward workspace is NULL or not 16-byte aligned");
   if (s.N == 0) return TWELL_OK;
 
@@ -162,6 +162,7 @@ twell_status twell_ffn_fwd(const twell_dims* dims, twell_dtype dtype, const twel
   a.vals = pack->vals;
   a.cols = pack->cols;
   a.counts = pack->counts;
+  a.ovf_flag = pack->ovf_flag;
   a.ovf_rows = pack->ovf_rows;
   a.ovf_h = pack->ovf_h;
   a.n_ovf = pack->n_ovf;
@@ -171,7 +172,8 @@ twell_status twell_ffn_fwd(const twell_dims* dims, twell_dtype dtype, const twel
   a.w_down = w_down;
   a.y = y;
   a.a_save = a_save;
-  a.part = reinterpret_cast<float*>(ws);
+  a.zbuf = reinterpret_cast<float*>(ws);
+  a.part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + twell::fwd_zbuf_bytes(s));
   return hip_status(twell::launch_ffn_fwd(a, (hipStream_t)stream), "twell_ffn_fwd");
 }
 

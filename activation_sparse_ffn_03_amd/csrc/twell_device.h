@@ -37,6 +37,27 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// One DPP step: v + (the value the DPP pattern routes to this lane), lanes
+// outside row_mask adding 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
+}
+
+// Full-wave sum with DPP (GFX9 row broadcasts), returned in every lane:
+// quad swaps, half-row and row mirrors give every lane its 16-lane row sum;
+// row_bcast:15 and row_bcast:31 fold rows 0..3 into lane 63, read back with
+// readlane. Six VALU ops instead of six LDS-crossbar shuffles.
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v = dpp_add<0xB1, 0xF>(v);   // quad_perm [1,0,3,2]
+  v = dpp_add<0x4E, 0xF>(v);   // quad_perm [2,3,0,1]
+  v = dpp_add<0x141, 0xF>(v);  // row_half_mirror
+  v = dpp_add<0x140, 0xF>(v);  // row_mirror
+  v = dpp_add<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v = dpp_add<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
 __device__ __forceinline__ int wave_lane() { return threadIdx.x & (kWave - 1); }
 
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }

@@ -84,7 +84,9 @@ twell_status check_shape(const twell_dims* d, int dtype, Shape* s, std::string* 
   return TWELL_OK;
 }
 
-size_t fwd_ws_bytes(const Shape& s) { return (size_t)s.ovf_cap * s.G * s.D * 4; }
+size_t fwd_zbuf_bytes(const Shape& s) { return align_up((size_t)s.n_tiles * s.slots * (size_t)s.N * 4); }
+
+size_t fwd_ws_bytes(const Shape& s) { return fwd_zbuf_bytes(s) + (size_t)s.ovf_cap * s.G * s.D * 4; }
 
 BwdLayout bwd_layout(const Shape& s) {
   BwdLayout L{};

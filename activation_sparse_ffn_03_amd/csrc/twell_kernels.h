@@ -48,6 +48,7 @@ struct FwdArgs {
   const void* vals;
   const uint16_t* cols;
   const uint16_t* counts;
+  const uint8_t* ovf_flag;
   const int32_t* ovf_rows;
   const void* ovf_h;
   const int32_t* n_ovf;
@@ -57,7 +58,8 @@ struct FwdArgs {
   const void* w_down;
   float* y;
   float* a_save;
-  float* part;  // [ovf_cap][G][D] fp32 partial outputs of dense-row chunks
+  float* zbuf;  // [n_t][S][N] fp32: z = h * a at every packed entry (workspace)
+  float* part;  // [ovf_cap][G][D] fp32 partial outputs of dense-row chunks (workspace)
 };
 
 hipError_t launch_ffn_fwd(const FwdArgs& a, hipStream_t s);

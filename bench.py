@@ -75,9 +75,12 @@ def kernel_work(name, w, st, train):
     if name == "gate_mfma_bf16":
         twell = n_t * w.slots * N * (e + 2) + n_t * N * 2
         return {"flops": 2.0 * N * D * F, "bytes": N * D * e + F * D * e + twell, "bound": "mfma"}
-    if name == "ffn_fwd_kernel":
-        byt = N * D * e + 2 * F * D * e + nnz * (e + 2) + n_t * N * 2 + N * D * 4 + (nnz * 4 if train else 0)
-        return {"flops": 4.0 * D * nnz, "bytes": byt, "bound": "hbm"}
+    if name == "ffn_up_kernel":   # x, W_up once; TwELL read; z (and a when training) written
+        byt = N * D * e + F * D * e + nnz * (e + 2) + n_t * N * 2 + nnz * 4 + (nnz * 4 if train else 0)
+        return {"flops": 2.0 * D * nnz, "bytes": byt, "bound": "hbm"}
+    if name == "ffn_down_kernel":  # W_down once; cols + z read; y written (fp32)
+        byt = F * D * e + nnz * (2 + 4) + n_t * N * 2 + N * D * 4
+        return {"flops": 2.0 * D * nnz, "bytes": byt, "bound": "hbm"}
     if name == "bwd_rows":
         byt = N * D * e + 3 * F * D * e + nnz_ell * (e + 8) + N * D * 4 + nnz * 20
         return {"flops": 6.0 * D * nnz, "bytes": byt, "bound": "hbm"}
@@ -126,7 +129,8 @@ def cpu_baseline(w, train, sample, budget_s=10.0):
 # summary of a kernel is only used while these files are unchanged.
 KERNEL_SOURCES = {
     "gate_mfma_bf16": ["gate_pack.hip", "twell_device.h"],
-    "ffn_fwd_kernel": ["fused_fwd.hip", "row_ops.h", "twell_device.h"],
+    "ffn_up_kernel": ["fused_fwd.hip", "row_ops.h", "twell_device.h"],
+    "ffn_down_kernel": ["fused_fwd.hip", "row_ops.h", "twell_device.h"],
     "bwd_rows": ["bwd.hip", "row_ops.h", "twell_device.h"],
     "bwd_dw": ["bwd.hip", "row_ops.h", "twell_device.h"],
 }

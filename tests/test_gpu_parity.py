@@ -124,6 +124,26 @@ def test_gate_pack_margin_bit_exact(name, kw):
     assert np.all(np.abs(got - want) <= np.abs(want) * 2.0 ** -7)
 
 
+@pytest.mark.parametrize("tile_n,slots", [(128, 16), (32, 3)])
+def test_gate_pack_big_tiles_ragged(tile_n, slots):
+    """Enough 256x256 tiles to select the large GEMM configuration, with d_ff
+    ragged against it (the last 128-column group lies past d_ff): margin
+    thresholds make the mask unique, so the pack must match bit for bit."""
+    w = make_inputs("c2", N=6144, D=256, F=8300, density=0.02)
+    g64 = orc.gate_preact(w.x, w.w_gate_t)
+    t = orc.margin_thresholds(g64, w.p)
+    pl = Pipeline(w, thresholds=t, tile_n=tile_n, slots=slots, ovf_cap=w.N)
+    pl.forward()
+    ref = orc.pack(g64, t, tile_n, slots, store="bf16", arith="f64")
+    check_pack(pl.ffn.pack, ref, pl.ovf_cap, exact_vals=False)
+    n = min(ref["n_ovf"], pl.ovf_cap)
+    dense = orc.dense_activation(g64, t, store="bf16", arith="f64")
+    got = f64(pl.ffn.pack.ovf_h[:n])
+    want = dense[ref["ovf_rows"][:n]]
+    assert np.all((got > 0) == (want > 0))
+    assert np.all(np.abs(got - want) <= np.abs(want) * 2.0 ** -7)
+
+
 def test_ovf_rows_match_epilogue_values():
     """Overflow rows are recomputed with the GEMM's own arithmetic: their dense
     activation equals, bit for bit, the values the pack epilogue stored."""
