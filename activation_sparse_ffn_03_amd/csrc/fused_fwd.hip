@@ -36,14 +36,29 @@ namespace {
 
 constexpr int kParts = 8;  // one part per XCD
 
+// Per-row tile offsets: offs[j][i] = number of packed entries of row i in
+// tiles before j (offs[n_t][i] = the row's total), i.e. where tile j's entries
+// start in the row's (column, z) list.
+__global__ __launch_bounds__(256) void ffn_row_offsets(FwdArgs a) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= a.N) return;
+  const int64_t N = a.N;
+  int32_t run = 0;
+#pragma unroll 8
+  for (int j = 0; j < a.n_tiles; ++j) {
+    a.offs[(size_t)j * N + i] = run;
+    run += min((int)a.counts[(size_t)j * N + i], a.slots);
+  }
+  a.offs[(size_t)a.n_tiles * N + i] = run;
+}
+
 // Walk TwELL tiles [j0, j1) of token i (not an overflow row) and hand its
 // packed entries to `flush` in lists of at most 64: lane k of the list holds
-// entry k as (global column c, value, slot id j*S+s). The value is the stored
-// activation h (READ_Z = false) or the z written by ffn_up_kernel. The slot
+// entry k as (global column c, stored activation h, slot id j*S+s). The slot
 // loads of all tiles are issued back to back into raw registers and decoded
 // once per list, so a token's metadata costs a couple of memory round trips
 // rather than one per tile.
-template <typename TS, bool READ_Z, typename Flush>
+template <typename TS, typename Flush>
 __device__ __forceinline__ void collect_pairs(const FwdArgs& a, int64_t i, int j0, int j1, int lane, Flush&& flush) {
   const int64_t N = a.N;
   const TS* __restrict__ vals = reinterpret_cast<const TS*>(a.vals);
@@ -53,13 +68,10 @@ __device__ __forceinline__ void collect_pairs(const FwdArgs& a, int64_t i, int j
   auto emit = [&](int cnt) {
     const int c = base_l + (int)col_raw;
     float v;
-    if constexpr (READ_Z) {
-      v = __uint_as_float(val_raw);
-    } else if constexpr (sizeof(TS) == 2) {
+    if constexpr (sizeof(TS) == 2)
       v = bf16_to_f32((uint16_t)val_raw);
-    } else {
+    else
       v = __uint_as_float(val_raw);
-    }
     flush(c, v, slot_l, cnt);
   };
   for (int jb = j0; jb < j1; jb += 64) {
@@ -81,9 +93,7 @@ __device__ __forceinline__ void collect_pairs(const FwdArgs& a, int64_t i, int j
           const int slot = j * a.slots + sb + lane - n;
           const size_t pos = (size_t)slot * N + i;
           col_raw = a.cols[pos];
-          if constexpr (READ_Z)
-            val_raw = __float_as_uint(a.zbuf[pos]);
-          else if constexpr (sizeof(TS) == 2)
+          if constexpr (sizeof(TS) == 2)
             val_raw = vals[pos];
           else
             val_raw = __float_as_uint(vals[pos]);
@@ -101,16 +111,19 @@ __device__ __forceinline__ void collect_pairs(const FwdArgs& a, int64_t i, int j
 // ------------------------------------------------------------------ up: z = h * (x_i . W_up^T[c])
 
 template <typename TS, int M>
-__global__ __launch_bounds__(256) void ffn_up_kernel(FwdArgs a, int parts) {
+__global__ __launch_bounds__(256) void ffn_up_kernel(FwdArgs a, int parts, int64_t i0, int64_t i1) {
   constexpr int E = ChunkElems<TS>::E;
   constexpr int U = M <= 4 ? 4 : (M == 8 ? 2 : 1);  // rows in flight per wave
   const int lane = threadIdx.x & 63;
   const int part = blockIdx.x % parts;
-  const int64_t i = (int64_t)(blockIdx.x / parts) * 4 + (threadIdx.x >> 6);
-  if (i >= a.N || a.ovf_flag[i]) return;
+  const int64_t i = i0 + (int64_t)(blockIdx.x / parts) * 4 + (threadIdx.x >> 6);
+  if (i >= i1 || a.ovf_flag[i]) return;
   const int j0 = (int)((int64_t)part * a.n_tiles / parts), j1 = (int)((int64_t)(part + 1) * a.n_tiles / parts);
   const int D = a.D, nch = D / E;
+  const size_t L = (size_t)a.n_tiles * a.slots;
   const TS* __restrict__ w_up = reinterpret_cast<const TS*>(a.w_up);
+  uint2* __restrict__ zl = a.zlist + (size_t)i * L;
+  int lbase = a.offs[(size_t)j0 * a.N + i];  // list position of this part's first entry
   u32x4_t xr[M];
   bool have_x = false;
   auto flush = [&](int c_l, float h_l, int slot_l, int n) {
@@ -118,14 +131,15 @@ __global__ __launch_bounds__(256) void ffn_up_kernel(FwdArgs a, int parts) {
       load_row<TS, M>(xr, reinterpret_cast<const TS*>(a.x) + (size_t)i * D, nch, lane);
       have_x = true;
     }
+    float a_l = 0.f;
     for (int k = 0; k < n; k += U) {
       u32x4_t wr[U][M];
-      int cs[U];
+      bool ok[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int c = readlane_i(c_l, min(k + u, n - 1));
-        cs[u] = (unsigned)c < (unsigned)a.F ? c : -1;  // a corrupted column contributes nothing
-        load_row<TS, M>(wr[u], w_up + (size_t)max(cs[u], 0) * D, nch, lane);
+        ok[u] = (unsigned)c < (unsigned)a.F;  // a corrupted column contributes nothing
+        load_row<TS, M>(wr[u], w_up + (size_t)(ok[u] ? c : 0) * D, nch, lane);
       }
       float dot[U];
 #pragma unroll
@@ -133,19 +147,17 @@ __global__ __launch_bounds__(256) void ffn_up_kernel(FwdArgs a, int parts) {
 #pragma unroll
       for (int u = 0; u < U; ++u) dot[u] = wave_sum_dpp(dot[u]);
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (k + u >= n) break;
-        const float av = cs[u] >= 0 ? dot[u] : 0.f;
-        const float h = readlane_f(h_l, k + u);
-        const size_t pos = (size_t)readlane_i(slot_l, k + u) * a.N + i;
-        if (lane == 0) {
-          a.zbuf[pos] = h * av;
-          if (a.a_save) a.a_save[pos] = av;
-        }
-      }
+      for (int u = 0; u < U; ++u)
+        if (lane == k + u) a_l = ok[u] ? dot[u] : 0.f;
     }
+    // lane k holds entry k: one coalesced store of the (column, z) pairs
+    if (lane < n) {
+      zl[lbase + lane] = make_uint2((uint32_t)c_l, __float_as_uint(h_l * a_l));
+      if (a.a_save) a.a_save[(size_t)slot_l * a.N + i] = a_l;
+    }
+    lbase += n;
   };
-  collect_pairs<TS, false>(a, i, j0, j1, lane, flush);
+  collect_pairs<TS>(a, i, j0, j1, lane, flush);
 }
 
 // ------------------------------------------------------------------ down: y_i[slice] = sum z * W_down[c][slice]
@@ -207,19 +219,25 @@ template <int EPL> struct Slice<float, EPL> {
 };
 
 template <typename TS, int EPL>
-__global__ __launch_bounds__(256) void ffn_down_kernel(FwdArgs a, int P) {
+__global__ __launch_bounds__(256) void ffn_down_kernel(FwdArgs a, int P, int64_t i0, int64_t i1) {
   constexpr int U = 8;  // rows in flight per wave
   const int lane = threadIdx.x & 63;
   const int p = blockIdx.x % P;
-  const int64_t i = (int64_t)(blockIdx.x / P) * 4 + (threadIdx.x >> 6);
-  if (i >= a.N || a.ovf_flag[i]) return;
+  const int64_t i = i0 + (int64_t)(blockIdx.x / P) * 4 + (threadIdx.x >> 6);
+  if (i >= i1 || a.ovf_flag[i]) return;
   const int D = a.D;
   const int d0 = (p * 64 + lane) * EPL;
   const TS* __restrict__ w_down = reinterpret_cast<const TS*>(a.w_down) + d0;
+  const uint2* __restrict__ zl = a.zlist + (size_t)i * a.n_tiles * a.slots;
+  const int total = a.offs[(size_t)a.n_tiles * a.N + i];
   float acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-  auto flush = [&](int c_l, float z_l, int slot_l, int n) {
+  for (int kb = 0; kb < total; kb += 64) {
+    const int n = min(64, total - kb);
+    const uint2 ent = lane < n ? zl[kb + lane] : make_uint2(0u, 0u);
+    const int c_l = (int)ent.x;
+    const float z_l = __uint_as_float(ent.y);
     for (int k = 0; k < n; k += U) {
       Slice<TS, EPL> w[U];
       float z[U];
@@ -234,8 +252,7 @@ __global__ __launch_bounds__(256) void ffn_down_kernel(FwdArgs a, int P) {
 #pragma unroll
       for (int u = 0; u < U; ++u) w[u].fma(z[u], acc);
     }
-  };
-  collect_pairs<TS, true>(a, i, 0, a.n_tiles, lane, flush);
+  }
   float* dst = a.y + (size_t)i * D + d0;
 #pragma unroll
   for (int e = 0; e < EPL; ++e) dst[e] = acc[e];
@@ -322,29 +339,23 @@ __global__ __launch_bounds__(256) void dense_reduce(const float* __restrict__ pa
   out[(size_t)rows[o] * D + d] = s;
 }
 
+// Token rows per pair of up / down launches (0 = all rows in one pair).
+constexpr int64_t kTokenChunk = 0;
+
 template <typename TS>
-hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
+hipError_t launch_t(const FwdArgs& a, hipStream_t s, int64_t chunk) {
   constexpr int E = ChunkElems<TS>::E;
   const int nch = a.D / E;
   const int M = pick_m(nch);
   const dim3 blk(256);
-  const int64_t tblocks = (a.N + 3) / 4;
+  hipError_t err;
 
-  // up: z at every packed entry of the non-overflow rows
+  TWELL_LAUNCH("ffn_row_offsets", ffn_row_offsets, dim3((unsigned)((a.N + 255) / 256)), blk, 0, s, a);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+
+  // up: (column, z) list of the non-overflow rows; down: their y rows, d_model
+  // cut into P slices of 64*EPL elements
   const int parts = a.n_tiles < kParts ? a.n_tiles : kParts;
-  const dim3 gup((unsigned)(tblocks * parts));
-  switch (M) {
-    case 1: TWELL_LAUNCH("ffn_up_kernel", (ffn_up_kernel<TS, 1>), gup, blk, 0, s, a, parts); break;
-    case 2: TWELL_LAUNCH("ffn_up_kernel", (ffn_up_kernel<TS, 2>), gup, blk, 0, s, a, parts); break;
-    case 4: TWELL_LAUNCH("ffn_up_kernel", (ffn_up_kernel<TS, 4>), gup, blk, 0, s, a, parts); break;
-    case 8: TWELL_LAUNCH("ffn_up_kernel", (ffn_up_kernel<TS, 8>), gup, blk, 0, s, a, parts); break;
-    case 16: TWELL_LAUNCH("ffn_up_kernel", (ffn_up_kernel<TS, 16>), gup, blk, 0, s, a, parts); break;
-    default: return hipErrorInvalidValue;
-  }
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-
-  // down: y rows of the non-overflow rows, d_model cut into P slices of 64*EPL
   constexpr int kMaxEpl = sizeof(TS) == 2 ? 16 : 8;
   int epl = 1;
   for (int e = kMaxEpl; e >= 1; e >>= 1)
@@ -353,21 +364,36 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
       break;
     }
   const int P = a.D / (64 * epl);
-  const dim3 gdn((unsigned)(tblocks * P));
-  switch (epl) {
-    case 1: TWELL_LAUNCH("ffn_down_kernel", (ffn_down_kernel<TS, 1>), gdn, blk, 0, s, a, P); break;
-    case 2: TWELL_LAUNCH("ffn_down_kernel", (ffn_down_kernel<TS, 2>), gdn, blk, 0, s, a, P); break;
-    case 4: TWELL_LAUNCH("ffn_down_kernel", (ffn_down_kernel<TS, 4>), gdn, blk, 0, s, a, P); break;
-    case 8: TWELL_LAUNCH("ffn_down_kernel", (ffn_down_kernel<TS, 8>), gdn, blk, 0, s, a, P); break;
-    case 16:
-      if constexpr (sizeof(TS) == 2) {
-        TWELL_LAUNCH("ffn_down_kernel", (ffn_down_kernel<TS, 16>), gdn, blk, 0, s, a, P);
-        break;
-      }
-      return hipErrorInvalidValue;
-    default: return hipErrorInvalidValue;
+  if (chunk <= 0) chunk = a.N;
+  for (int64_t i0 = 0; i0 < a.N; i0 += chunk) {
+    const int64_t i1 = i0 + chunk < a.N ? i0 + chunk : a.N;
+    const int64_t tblocks = (i1 - i0 + 3) / 4;
+    const dim3 gup((unsigned)(tblocks * parts));
+    switch (M) {
+      case 1: TWELL_LAUNCH("ffn_up_kernel", (ffn_up_kernel<TS, 1>), gup, blk, 0, s, a, parts, i0, i1); break;
+      case 2: TWELL_LAUNCH("ffn_up_kernel", (ffn_up_kernel<TS, 2>), gup, blk, 0, s, a, parts, i0, i1); break;
+      case 4: TWELL_LAUNCH("ffn_up_kernel", (ffn_up_kernel<TS, 4>), gup, blk, 0, s, a, parts, i0, i1); break;
+      case 8: TWELL_LAUNCH("ffn_up_kernel", (ffn_up_kernel<TS, 8>), gup, blk, 0, s, a, parts, i0, i1); break;
+      case 16: TWELL_LAUNCH("ffn_up_kernel", (ffn_up_kernel<TS, 16>), gup, blk, 0, s, a, parts, i0, i1); break;
+      default: return hipErrorInvalidValue;
+    }
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    const dim3 gdn((unsigned)(tblocks * P));
+    switch (epl) {
+      case 1: TWELL_LAUNCH("ffn_down_kernel", (ffn_down_kernel<TS, 1>), gdn, blk, 0, s, a, P, i0, i1); break;
+      case 2: TWELL_LAUNCH("ffn_down_kernel", (ffn_down_kernel<TS, 2>), gdn, blk, 0, s, a, P, i0, i1); break;
+      case 4: TWELL_LAUNCH("ffn_down_kernel", (ffn_down_kernel<TS, 4>), gdn, blk, 0, s, a, P, i0, i1); break;
+      case 8: TWELL_LAUNCH("ffn_down_kernel", (ffn_down_kernel<TS, 8>), gdn, blk, 0, s, a, P, i0, i1); break;
+      case 16:
+        if constexpr (sizeof(TS) == 2) {
+          TWELL_LAUNCH("ffn_down_kernel", (ffn_down_kernel<TS, 16>), gdn, blk, 0, s, a, P, i0, i1);
+          break;
+        }
+        return hipErrorInvalidValue;
+      default: return hipErrorInvalidValue;
+    }
+    if ((err = hipGetLastError()) != hipSuccess) return err;
   }
-  if ((err = hipGetLastError()) != hipSuccess) return err;
 
   // overflow rows: dense chunks + fixed-order reduction into y
   if (a.ovf_cap == 0) return hipSuccess;
@@ -395,7 +421,7 @@ hipError_t launch_dense_reduce(const float* part, const int32_t* rows, const int
 }
 
 hipError_t launch_ffn_fwd(const FwdArgs& a, hipStream_t s) {
-  return a.is_bf16 ? launch_t<uint16_t>(a, s) : launch_t<float>(a, s);
+  return a.is_bf16 ? launch_t<uint16_t>(a, s, kTokenChunk) : launch_t<float>(a, s, kTokenChunk);
 }
 
 }  // namespace twell

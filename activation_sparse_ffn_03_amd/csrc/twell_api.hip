@@ -172,8 +172,11 @@ twell_status twell_ffn_fwd(const twell_dims* dims, twell_dtype dtype, const twel
   a.w_down = w_down;
   a.y = y;
   a.a_save = a_save;
-  a.zbuf = reinterpret_cast<float*>(ws);
-  a.part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + twell::fwd_zbuf_bytes(s));
+  const twell::FwdLayout L = twell::fwd_layout(s);
+  char* base = reinterpret_cast<char*>(ws);
+  a.offs = reinterpret_cast<int32_t*>(base + L.offs);
+  a.zlist = reinterpret_cast<uint2*>(base + L.zlist);
+  a.part = reinterpret_cast<float*>(base + L.part);
   return hip_status(twell::launch_ffn_fwd(a, (hipStream_t)stream), "twell_ffn_fwd");
 }
 

@@ -84,9 +84,16 @@ twell_status check_shape(const twell_dims* d, int dtype, Shape* s, std::string* 
   return TWELL_OK;
 }
 
-size_t fwd_zbuf_bytes(const Shape& s) { return align_up((size_t)s.n_tiles * s.slots * (size_t)s.N * 4); }
+FwdLayout fwd_layout(const Shape& s) {
+  FwdLayout L{};
+  L.offs = 0;
+  L.zlist = align_up(((size_t)s.n_tiles + 1) * (size_t)s.N * 4);
+  L.part = L.zlist + align_up((size_t)s.N * s.n_tiles * s.slots * 8);
+  L.total = L.part + (size_t)s.ovf_cap * s.G * s.D * 4;
+  return L;
+}
 
-size_t fwd_ws_bytes(const Shape& s) { return fwd_zbuf_bytes(s) + (size_t)s.ovf_cap * s.G * s.D * 4; }
+size_t fwd_ws_bytes(const Shape& s) { return s.N == 0 ? 0 : fwd_layout(s).total; }
 
 BwdLayout bwd_layout(const Shape& s) {
   BwdLayout L{};

@@ -33,8 +33,12 @@ struct BwdLayout {
 twell_status check_shape(const twell_dims* dims, int dtype, Shape* out, std::string* why);
 void compute_sizes(const Shape& s, twell_sizes* out);
 BwdLayout bwd_layout(const Shape& s);
-// Forward workspace: the z buffer ([n_t][S][N] fp32) then the dense-row partials.
-size_t fwd_zbuf_bytes(const Shape& s);
+// Forward workspace, in order: per-row tile offsets ([n_t+1][N] int32), the
+// row-major (column, z) list ([N][n_t*S] x 8 bytes), the dense-row partials.
+struct FwdLayout {
+  size_t offs, zlist, part, total;
+};
+FwdLayout fwd_layout(const Shape& s);
 size_t fwd_ws_bytes(const Shape& s);
 
 // Pointer checks: null (when bytes > 0) or not 16-byte aligned.

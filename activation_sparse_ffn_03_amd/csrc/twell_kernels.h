@@ -58,8 +58,9 @@ struct FwdArgs {
   const void* w_down;
   float* y;
   float* a_save;
-  float* zbuf;  // [n_t][S][N] fp32: z = h * a at every packed entry (workspace)
-  float* part;  // [ovf_cap][G][D] fp32 partial outputs of dense-row chunks (workspace)
+  int32_t* offs;  // [n_t+1][N]: entries of the row's tiles before tile j (workspace)
+  uint2* zlist;   // [N][n_t*S]: (column, z = h*a) of every packed entry, row-major (workspace)
+  float* part;    // [ovf_cap][G][D] fp32 partial outputs of dense-row chunks (workspace)
 };
 
 hipError_t launch_ffn_fwd(const FwdArgs& a, hipStream_t s);

@@ -167,9 +167,10 @@ twell_status twell_pack_preact(const twell_dims* dims, twell_dtype dtype, const 
  * left unwritten; the pack's status says so).
  * a_save: optional [n_t][S][N] fp32; when given, a = x_i · w_up_t[c] is stored
  * at the slot of every packed entry of non-overflow rows (training).
- * ws: workspace of at least twell_sizes.ws_fwd bytes: z = h·a at every packed
- * entry ([n_t][S][N] fp32, the sparse intermediate between the up and the down
- * projection) followed by the partial rows of the overflow-row chunks. */
+ * ws: workspace of at least twell_sizes.ws_fwd bytes: per-row tile offsets,
+ * the (column, z = h·a) pair of every packed entry in row-major order (the
+ * sparse intermediate between the up and the down projection, never a dense
+ * hidden state) and the partial rows of the overflow-row chunks. */
 twell_status twell_ffn_fwd(const twell_dims* dims, twell_dtype dtype, const twell_pack* pack,
                            const void* x, const void* w_up_t, const void* w_down, float* y,
                            float* a_save, void* ws, size_t ws_bytes, void* stream);
