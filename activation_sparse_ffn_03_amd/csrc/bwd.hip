@@ -103,95 +103,192 @@ __global__ __launch_bounds__(1024) void row_scan(BwdArgs a, const int32_t* dense
   if (tid == 1023) a.ws.row_ptr[N] = part[1023];
 }
 
-// --------------------------------------------------------------- row pass
+// --------------------------------------------------------------- dz pass
 
+// ELL rows. Part p (= XCD p when parts = 8) owns the columns
+// [p*F/parts, (p+1)*F/parts), so each XCD gathers only its 1/8 of W_down's
+// rows. One wave per (row, part): dy_i in registers, the row's ELL entries in
+// range (contiguous: ELL columns ascend) taken 64 at a time, U W_down rows in
+// flight, dz = dy_i . W_down[c] reduced with DPP; then every lane writes the
+// record of its entry: column and (z, da, dg) = (h*a, dz*h, dz*a + lambda).
 template <typename TS, int M>
-__device__ __forceinline__ void bwd_pair(const BwdArgs& a, int nch, int lane, const u32x4_t (&dyr)[M],
-                                         const u32x4_t (&xr)[M], bool recompute_a, float (&acc)[M][8], int c,
-                                         float h, float av, int32_t p) {
+__global__ __launch_bounds__(256) void bwd_dz_ell(BwdArgs a, int parts) {
+  constexpr int E = ChunkElems<TS>::E;
+  constexpr int U = M <= 4 ? 4 : (M == 8 ? 2 : 1);
+  const int lane = threadIdx.x & 63;
+  const int part = blockIdx.x % parts;
+  const int64_t i = (int64_t)(blockIdx.x / parts) * 4 + (threadIdx.x >> 6);
+  const int64_t N = a.N;
+  if (i >= N || a.is_dense[i]) return;
+  const int n = min(a.row_nnz[i], a.row_cap);
+  const int clo = (int)((int64_t)part * a.F / parts), chi = (int)((int64_t)(part + 1) * a.F / parts);
+  const int D = a.D, nch = D / E;
+  const int32_t p0 = a.ws.row_ptr[i];
   const TS* __restrict__ wd = reinterpret_cast<const TS*>(a.w_down);
-  const TS* __restrict__ wu = reinterpret_cast<const TS*>(a.w_up);
-  const TS* __restrict__ wg = reinterpret_cast<const TS*>(a.w_gate);
-  const int D = a.D;
-  const bool ok = c >= 0 && c < a.F;  // defensive: a corrupted column contributes nothing
-  if (!ok) {
-    c = 0;
-    h = 0.f;
-  }
-  u32x4_t wr[M];
-  load_row<TS, M>(wr, wd + (size_t)c * D, nch, lane);
-  const float dz = wave_sum(dot_rows<TS, M>(dyr, wr));
-  load_row<TS, M>(wr, wu + (size_t)c * D, nch, lane);
-  if (recompute_a) av = wave_sum(dot_rows<TS, M>(xr, wr));
-  const float da = ok ? dz * h : 0.f;
-  const float dg = ok ? fmaf(dz, av, a.lam) : 0.f;
-  const float z = h * av;
-  axpy_row<TS, M>(acc, da, wr);
-  load_row<TS, M>(wr, wg + (size_t)c * D, nch, lane);
-  axpy_row<TS, M>(acc, dg, wr);
-  if (lane == 0) {
-    a.ws.pair_col[p] = c;
-    a.ws.coef[p] = make_float4(z, da, dg, 0.f);
+  const TS* __restrict__ ev = reinterpret_cast<const TS*>(a.ell_vals);
+  u32x4_t dyr[M];
+  bool have_dy = false;
+  for (int kb = 0; kb < n; kb += 64) {
+    const int k = kb + lane;
+    const size_t off = (size_t)k * N + i;
+    const int c_l = k < n ? a.ell_cols[off] : -1;
+    const uint64_t m = ballot(c_l >= clo && c_l < chi);
+    if (m == 0) continue;
+    const int first = __ffsll((unsigned long long)m) - 1, cnt = __popcll(m);
+    const bool mine = (m >> lane) & 1ull;
+    float h_l = 0.f, a_l = 0.f;
+    if (mine) {
+      h_l = Store<TS>::load(ev, off);
+      a_l = a.ell_a[off];
+    }
+    if (!have_dy) {
+      load_row<TS, M>(dyr, reinterpret_cast<const TS*>(a.dy) + (size_t)i * D, nch, lane);
+      have_dy = true;
+    }
+    float dz_l = 0.f;
+    for (int q = 0; q < cnt; q += U) {
+      u32x4_t wr[U][M];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        load_row<TS, M>(wr[u], wd + (size_t)readlane_i(c_l, first + min(q + u, cnt - 1)) * D, nch, lane);
+      float dot[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) dot[u] = wave_sum_dpp(dot_rows<TS, M>(dyr, wr[u]));
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (lane == first + q + u) dz_l = dot[u];
+    }
+    if (mine) {
+      a.ws.pair_col[p0 + k] = c_l;
+      a.ws.coef[p0 + k] = make_float4(h_l * a_l, dz_l * h_l, fmaf(dz_l, a_l, a.lam), 0.f);
+    }
   }
 }
 
+// Dense-backup rows. Work item (o, g): dense row o, columns
+// [g*kDenseChunk, ...). The active columns (h > 0) of each 64-column block are
+// compacted into lanes; for each, dz = dy_i . W_down[c] and the up activation
+// a = x_i . W_up^T[c] (not saved for these rows) are reduced, then the
+// records go to positions row_ptr[i] + grp_off[o][g] + rank.
 template <typename TS, int M>
-__global__ __launch_bounds__(256) void bwd_rows(BwdArgs a, int G) {
+__global__ __launch_bounds__(256) void bwd_dz_dense(BwdArgs a, int G) {
   constexpr int E = ChunkElems<TS>::E;
+  constexpr int U = M <= 4 ? 2 : 1;
   const int lane = threadIdx.x & 63;
   const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int64_t N = a.N;
-  const int D = a.D, nch = D / E;
-  const TS* __restrict__ x = reinterpret_cast<const TS*>(a.x);
-  const TS* __restrict__ dy = reinterpret_cast<const TS*>(a.dy);
-  u32x4_t dyr[M], xr[M];
-  float acc[M][8];
-  zero_acc<M>(acc);
-  if (item < N) {
-    const int64_t i = item;
-    if (a.is_dense[i]) return;
-    const int n = min(a.row_nnz[i], a.row_cap);
-    const int32_t p0 = a.ws.row_ptr[i];
-    load_row<TS, M>(dyr, dy + (size_t)i * D, nch, lane);
-    const TS* ev = reinterpret_cast<const TS*>(a.ell_vals);
-    for (int kb = 0; kb < n; kb += 64) {
-      const int k = kb + lane;
-      int c_l = 0;
-      float h_l = 0.f, a_l = 0.f;
-      if (k < n) {
-        const size_t off = (size_t)k * N + i;
-        c_l = a.ell_cols[off];
-        h_l = Store<TS>::load(ev, off);
-        a_l = a.ell_a[off];
-      }
-      const int nb = min(64, n - kb);
-      for (int t = 0; t < nb; ++t)
-        bwd_pair<TS, M>(a, nch, lane, dyr, xr, false, acc, readlane_i(c_l, t), readlane_f(h_l, t),
-                        readlane_f(a_l, t), p0 + kb + t);
-    }
-    store_row<TS, M>(a.dx + (size_t)i * D, acc, nch, lane);
-    return;
-  }
-  const int64_t k = item - N;
-  const int o = (int)(k / G), g = (int)(k % G);
+  const int o = (int)(item / G), g = (int)(item % G);
   if (o >= a.dense_cap || o >= *a.n_dense) return;
+  const int D = a.D, nch = D / E;
   const int64_t i = a.dense_rows[o];
+  const TS* __restrict__ wd = reinterpret_cast<const TS*>(a.w_down);
+  const TS* __restrict__ wu = reinterpret_cast<const TS*>(a.w_up);
+  const TS* __restrict__ hrow = reinterpret_cast<const TS*>(a.dense_h) + (size_t)o * a.F;
+  u32x4_t dyr[M], xr[M];
+  load_row<TS, M>(dyr, reinterpret_cast<const TS*>(a.dy) + (size_t)i * D, nch, lane);
+  load_row<TS, M>(xr, reinterpret_cast<const TS*>(a.x) + (size_t)i * D, nch, lane);
   int32_t p = a.ws.row_ptr[i] + a.ws.grp_off[(size_t)o * G + g];
-  load_row<TS, M>(dyr, dy + (size_t)i * D, nch, lane);
-  load_row<TS, M>(xr, x + (size_t)i * D, nch, lane);
-  const TS* hrow = reinterpret_cast<const TS*>(a.dense_h) + (size_t)o * a.F;
   const int c0 = g * kDenseChunk, c1 = min(a.F, c0 + kDenseChunk);
   for (int cb = c0; cb < c1; cb += 64) {
     const int c = cb + lane;
-    const float h_l = c < c1 ? Store<TS>::load(hrow, c) : 0.f;
-    uint64_t m = ballot(h_l > 0.f);
-    while (m) {
-      const int t = __ffsll((unsigned long long)m) - 1;
-      m &= m - 1;
-      bwd_pair<TS, M>(a, nch, lane, dyr, xr, true, acc, cb + t, readlane_f(h_l, t), 0.f, p++);
+    const float h_c = c < c1 ? Store<TS>::load(hrow, c) : 0.f;
+    const uint64_t m = ballot(h_c > 0.f);
+    const int n = __popcll(m);
+    if (n == 0) continue;
+    // lane q of the list gets the q-th active column (binary search on prefix popcounts)
+    int lo = 0, hi = 63;
+    for (int step = 0; step < 6; ++step) {
+      const int mid = (lo + hi) >> 1;
+      const uint64_t below = mid >= 63 ? ~0ull : ((2ull << mid) - 1ull);
+      if (__popcll(m & below) >= lane + 1) hi = mid; else lo = mid + 1;
+    }
+    const int col_l = cb + lo;
+    const float h_l = __shfl(h_c, lo, 64);
+    float dz_l = 0.f, a_l = 0.f;
+    for (int q = 0; q < n; q += U) {
+      u32x4_t wr[U][M], ur[U][M];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const size_t row = (size_t)readlane_i(col_l, min(q + u, n - 1)) * D;
+        load_row<TS, M>(wr[u], wd + row, nch, lane);
+        load_row<TS, M>(ur[u], wu + row, nch, lane);
+      }
+      float dz[U], av[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        dz[u] = wave_sum_dpp(dot_rows<TS, M>(dyr, wr[u]));
+        av[u] = wave_sum_dpp(dot_rows<TS, M>(xr, ur[u]));
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (lane == q + u) {
+          dz_l = dz[u];
+          a_l = av[u];
+        }
+    }
+    if (lane < n) {
+      a.ws.pair_col[p + lane] = col_l;
+      a.ws.coef[p + lane] = make_float4(h_l * a_l, dz_l * h_l, fmaf(dz_l, a_l, a.lam), 0.f);
+    }
+    p += n;
+  }
+}
+
+// --------------------------------------------------------------- dx pass
+
+// Every row (ELL and dense-backup alike): its records are contiguous in CSR
+// order. Part p owns the d_model slice [p*64*EPL, (p+1)*64*EPL) of dx, so each
+// XCD gathers only that slice of the W_up / W_gate rows.
+//   dx_i[slice] = sum over records (da * W_up^T[c][slice] + dg * W_gate^T[c][slice])
+// Dense rows beyond the dense capacity have no records and get dx = 0.
+template <typename TS, int EPL>
+__global__ __launch_bounds__(256) void bwd_dx(BwdArgs a, int P) {
+  constexpr int U = 4;
+  const int lane = threadIdx.x & 63;
+  const int p = blockIdx.x % P;
+  const int64_t i = (int64_t)(blockIdx.x / P) * 4 + (threadIdx.x >> 6);
+  if (i >= a.N) return;
+  const int D = a.D;
+  const int d0 = (p * 64 + lane) * EPL;
+  const TS* __restrict__ wu = reinterpret_cast<const TS*>(a.w_up) + d0;
+  const TS* __restrict__ wg = reinterpret_cast<const TS*>(a.w_gate) + d0;
+  const int32_t q0 = a.ws.row_ptr[i], q1 = a.ws.row_ptr[i + 1];
+  float acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  for (int qb = q0; qb < q1; qb += 64) {
+    const int n = min(64, q1 - qb);
+    int c_l = 0;
+    float da_l = 0.f, dg_l = 0.f;
+    if (lane < n) {
+      c_l = a.ws.pair_col[qb + lane];
+      const float4 cf = a.ws.coef[qb + lane];
+      da_l = cf.y;
+      dg_l = cf.z;
+    }
+    for (int k = 0; k < n; k += U) {
+      Slice<TS, EPL> su[U], sg[U];
+      float da[U], dg[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int kk = min(k + u, n - 1);
+        const int c = readlane_i(c_l, kk);
+        const bool ok = (unsigned)c < (unsigned)a.F && k + u < n;
+        da[u] = ok ? readlane_f(da_l, kk) : 0.f;
+        dg[u] = ok ? readlane_f(dg_l, kk) : 0.f;
+        const size_t row = (size_t)(ok ? c : 0) * D;
+        su[u].load(wu + row);
+        sg[u].load(wg + row);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        su[u].fma(da[u], acc);
+        sg[u].fma(dg[u], acc);
+      }
     }
   }
-  store_row<TS, M>(a.ws.part + ((size_t)o * G + g) * D, acc, nch, lane);
+  float* dst = a.dx + (size_t)i * D + d0;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) dst[e] = acc[e];
 }
 
 // --------------------------------------------------------------- column transpose
@@ -282,47 +379,62 @@ __global__ __launch_bounds__(64) void csc_fill(const int32_t* __restrict__ row_p
 
 // --------------------------------------------------------------- weight gradients
 
-template <typename TS, int MP>
-__global__ __launch_bounds__(256) void bwd_dw(BwdArgs a, int parts) {
-  constexpr int E = ChunkElems<TS>::E;
+// Wave per (column c, d_model slice p): the column's records in ascending row
+// order (from the column transpose), U token rows in flight:
+//   dW_down[c][slice] += z * dy_i[slice], dW_up^T[c][slice] += da * x_i[slice],
+//   dW_gate^T[c][slice] += dg * x_i[slice].
+template <typename TS, int EPL>
+__global__ __launch_bounds__(256) void bwd_dw(BwdArgs a, int P) {
+  constexpr int U = 4;
   const int lane = threadIdx.x & 63;
-  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (item >= (int64_t)a.F * parts) return;
-  const int c = (int)(item / parts), pr = (int)(item % parts);
-  const int D = a.D, nch = D / E;
-  const int ch0 = pr * MP * 64;
-  const int nchp = min(MP * 64, nch - ch0);
-  const TS* __restrict__ x = reinterpret_cast<const TS*>(a.x) + (size_t)ch0 * E;
-  const TS* __restrict__ dy = reinterpret_cast<const TS*>(a.dy) + (size_t)ch0 * E;
-  float accD[MP][8], accU[MP][8], accG[MP][8];
-  zero_acc<MP>(accD);
-  zero_acc<MP>(accU);
-  zero_acc<MP>(accG);
+  const int p = blockIdx.x % P;
+  const int64_t c = (int64_t)(blockIdx.x / P) * 4 + (threadIdx.x >> 6);
+  if (c >= a.F) return;
+  const int D = a.D;
+  const int d0 = (p * 64 + lane) * EPL;
+  const TS* __restrict__ x = reinterpret_cast<const TS*>(a.x) + d0;
+  const TS* __restrict__ dy = reinterpret_cast<const TS*>(a.dy) + d0;
+  float accD[EPL], accU[EPL], accG[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) accD[e] = accU[e] = accG[e] = 0.f;
   const int32_t q0 = a.ws.col_ptr[c], q1 = a.ws.col_ptr[c + 1];
-  for (int32_t qb = q0; qb < q1; qb += 64) {
-    const int32_t q = qb + lane;
+  for (int qb = q0; qb < q1; qb += 64) {
+    const int n = min(64, q1 - qb);
     int i_l = 0;
     float4 cf = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (q < q1) {
-      i_l = a.ws.csc_row[q];
-      cf = a.ws.coef[a.ws.csc_pair[q]];
+    if (lane < n) {
+      i_l = a.ws.csc_row[qb + lane];
+      cf = a.ws.coef[a.ws.csc_pair[qb + lane]];
     }
-    const int nb = min(64, q1 - qb);
-    for (int t = 0; t < nb; ++t) {
-      const int64_t i = readlane_i(i_l, t);
-      const float z = readlane_f(cf.x, t), da = readlane_f(cf.y, t), dg = readlane_f(cf.z, t);
-      u32x4_t r[MP];
-      load_row<TS, MP>(r, dy + (size_t)i * D, nchp, lane);
-      axpy_row<TS, MP>(accD, z, r);
-      load_row<TS, MP>(r, x + (size_t)i * D, nchp, lane);
-      axpy_row<TS, MP>(accU, da, r);
-      axpy_row<TS, MP>(accG, dg, r);
+    for (int k = 0; k < n; k += U) {
+      Slice<TS, EPL> sd[U], sx[U];
+      float z[U], da[U], dg[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int kk = min(k + u, n - 1);
+        const bool ok = k + u < n;
+        const size_t row = (size_t)readlane_i(i_l, kk) * D;
+        z[u] = ok ? readlane_f(cf.x, kk) : 0.f;
+        da[u] = ok ? readlane_f(cf.y, kk) : 0.f;
+        dg[u] = ok ? readlane_f(cf.z, kk) : 0.f;
+        sd[u].load(dy + row);
+        sx[u].load(x + row);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        sd[u].fma(z[u], accD);
+        sx[u].fma(da[u], accU);
+        sx[u].fma(dg[u], accG);
+      }
     }
   }
-  const size_t ro = (size_t)c * D + (size_t)ch0 * E;
-  store_row<TS, MP>(a.dw_down + ro, accD, nchp, lane);
-  store_row<TS, MP>(a.dw_up + ro, accU, nchp, lane);
-  store_row<TS, MP>(a.dw_gate + ro, accG, nchp, lane);
+  const size_t ro = (size_t)c * D + d0;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    a.dw_down[ro + e] = accD[e];
+    a.dw_up[ro + e] = accU[e];
+    a.dw_gate[ro + e] = accG[e];
+  }
 }
 
 template <typename TS>
@@ -333,42 +445,81 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t s) {
   const int G = (a.F + kDenseChunk - 1) / kDenseChunk;
   const int nrb = (int)((a.N + RB - 1) / RB);
   int32_t* dense_nnz = a.ws.row_ptr + a.N + 1;  // [dense_cap] lives after row_ptr
+  const dim3 blk(256);
   hipError_t err;
 
   if (a.dense_cap > 0) {
-    TWELL_LAUNCH("dense_groups", dense_groups<TS>, dim3((a.dense_cap + 3) / 4), 256, 0, s, a, G, dense_nnz);
+    TWELL_LAUNCH("dense_groups", dense_groups<TS>, dim3((a.dense_cap + 3) / 4), blk, 0, s, a, G, dense_nnz);
   }
   TWELL_LAUNCH("row_scan", row_scan, 1, 1024, 0, s, a, dense_nnz);
-  const int64_t items = a.N + (int64_t)a.dense_cap * G;
-  const dim3 grid((unsigned)((items + 3) / 4));
+
+  // dz records: ELL rows by column part, dense rows by column chunk
+  const int parts = 8;
+  const dim3 gdz((unsigned)(((a.N + 3) / 4) * parts));
   switch (M) {
-    case 1: TWELL_LAUNCH("bwd_rows", (bwd_rows<TS, 1>), grid, 256, 0, s, a, G); break;
-    case 2: TWELL_LAUNCH("bwd_rows", (bwd_rows<TS, 2>), grid, 256, 0, s, a, G); break;
-    case 4: TWELL_LAUNCH("bwd_rows", (bwd_rows<TS, 4>), grid, 256, 0, s, a, G); break;
-    case 8: TWELL_LAUNCH("bwd_rows", (bwd_rows<TS, 8>), grid, 256, 0, s, a, G); break;
-    case 16: TWELL_LAUNCH("bwd_rows", (bwd_rows<TS, 16>), grid, 256, 0, s, a, G); break;
+    case 1: TWELL_LAUNCH("bwd_dz_ell", (bwd_dz_ell<TS, 1>), gdz, blk, 0, s, a, parts); break;
+    case 2: TWELL_LAUNCH("bwd_dz_ell", (bwd_dz_ell<TS, 2>), gdz, blk, 0, s, a, parts); break;
+    case 4: TWELL_LAUNCH("bwd_dz_ell", (bwd_dz_ell<TS, 4>), gdz, blk, 0, s, a, parts); break;
+    case 8: TWELL_LAUNCH("bwd_dz_ell", (bwd_dz_ell<TS, 8>), gdz, blk, 0, s, a, parts); break;
+    case 16: TWELL_LAUNCH("bwd_dz_ell", (bwd_dz_ell<TS, 16>), gdz, blk, 0, s, a, parts); break;
     default: return hipErrorInvalidValue;
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  if ((err = launch_dense_reduce(a.ws.part, a.dense_rows, a.n_dense, a.dense_cap, G, a.D, a.dx, s)) != hipSuccess)
-    return err;
+  if (a.dense_cap > 0) {
+    const dim3 gdd((unsigned)(((int64_t)a.dense_cap * G + 3) / 4));
+    switch (M) {
+      case 1: TWELL_LAUNCH("bwd_dz_dense", (bwd_dz_dense<TS, 1>), gdd, blk, 0, s, a, G); break;
+      case 2: TWELL_LAUNCH("bwd_dz_dense", (bwd_dz_dense<TS, 2>), gdd, blk, 0, s, a, G); break;
+      case 4: TWELL_LAUNCH("bwd_dz_dense", (bwd_dz_dense<TS, 4>), gdd, blk, 0, s, a, G); break;
+      case 8: TWELL_LAUNCH("bwd_dz_dense", (bwd_dz_dense<TS, 8>), gdd, blk, 0, s, a, G); break;
+      case 16: TWELL_LAUNCH("bwd_dz_dense", (bwd_dz_dense<TS, 16>), gdd, blk, 0, s, a, G); break;
+      default: return hipErrorInvalidValue;
+    }
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
 
+  // dx: every row, d_model sliced
+  int epl, P;
+  pick_slices(a.D, (int)sizeof(TS), &epl, &P);
+  const dim3 gdx((unsigned)(((a.N + 3) / 4) * P));
+  switch (epl) {
+    case 1: TWELL_LAUNCH("bwd_dx", (bwd_dx<TS, 1>), gdx, blk, 0, s, a, P); break;
+    case 2: TWELL_LAUNCH("bwd_dx", (bwd_dx<TS, 2>), gdx, blk, 0, s, a, P); break;
+    case 4: TWELL_LAUNCH("bwd_dx", (bwd_dx<TS, 4>), gdx, blk, 0, s, a, P); break;
+    case 8: TWELL_LAUNCH("bwd_dx", (bwd_dx<TS, 8>), gdx, blk, 0, s, a, P); break;
+    case 16:
+      if constexpr (sizeof(TS) == 2) {
+        TWELL_LAUNCH("bwd_dx", (bwd_dx<TS, 16>), gdx, blk, 0, s, a, P);
+        break;
+      }
+      return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+
+  // column transpose of the records (stable: rows ascend within a column)
   const size_t lds = (size_t)((a.F + 1) / 2) * 4;
   TWELL_LAUNCH("csc_hist", csc_hist, dim3(nrb), 256, lds, s, a.ws.row_ptr, a.ws.pair_col, a.N, a.F, a.ws.blk_cnt);
   TWELL_LAUNCH("csc_coltotal", csc_coltotal, dim3((a.F + 255) / 256), 256, 0, s, a.ws.blk_cnt, nrb, a.F, a.ws.col_ptr);
   TWELL_LAUNCH("csc_colscan", csc_colscan, 1, 1024, 0, s, a.ws.col_ptr, a.F);
   TWELL_LAUNCH("csc_offsets", csc_offsets, dim3((a.F + 255) / 256), 256, 0, s, a.ws.blk_cnt, a.ws.col_ptr, nrb, a.F);
-  TWELL_LAUNCH("csc_fill", csc_fill, dim3(nrb), 64, lds, s, a.ws.row_ptr, a.ws.pair_col, a.ws.blk_cnt, a.N, a.F, a.ws.csc_pair,
-                                      a.ws.csc_row);
+  TWELL_LAUNCH("csc_fill", csc_fill, dim3(nrb), 64, lds, s, a.ws.row_ptr, a.ws.pair_col, a.ws.blk_cnt, a.N, a.F,
+               a.ws.csc_pair, a.ws.csc_row);
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
-  const int MP = M < 4 ? M : 4;
-  const int parts = (nch + MP * 64 - 1) / (MP * 64);
-  const dim3 gdw((unsigned)(((int64_t)a.F * parts + 3) / 4));
-  switch (MP) {
-    case 1: TWELL_LAUNCH("bwd_dw", (bwd_dw<TS, 1>), gdw, 256, 0, s, a, parts); break;
-    case 2: TWELL_LAUNCH("bwd_dw", (bwd_dw<TS, 2>), gdw, 256, 0, s, a, parts); break;
-    case 4: TWELL_LAUNCH("bwd_dw", (bwd_dw<TS, 4>), gdw, 256, 0, s, a, parts); break;
+  // weight gradients: column-owned, d_model sliced
+  const dim3 gdw((unsigned)(((a.F + 3) / 4) * (int64_t)P));
+  switch (epl) {
+    case 1: TWELL_LAUNCH("bwd_dw", (bwd_dw<TS, 1>), gdw, blk, 0, s, a, P); break;
+    case 2: TWELL_LAUNCH("bwd_dw", (bwd_dw<TS, 2>), gdw, blk, 0, s, a, P); break;
+    case 4: TWELL_LAUNCH("bwd_dw", (bwd_dw<TS, 4>), gdw, blk, 0, s, a, P); break;
+    case 8: TWELL_LAUNCH("bwd_dw", (bwd_dw<TS, 8>), gdw, blk, 0, s, a, P); break;
+    case 16:
+      if constexpr (sizeof(TS) == 2) {
+        TWELL_LAUNCH("bwd_dw", (bwd_dw<TS, 16>), gdw, blk, 0, s, a, P);
+        break;
+      }
+      return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -162,62 +162,6 @@ __global__ __launch_bounds__(256) void ffn_up_kernel(FwdArgs a, int parts, int64
 
 // ------------------------------------------------------------------ down: y_i[slice] = sum z * W_down[c][slice]
 
-// EPL consecutive storage elements per lane, loaded with one or two vector
-// loads and widened to fp32.
-template <typename TS, int EPL> struct Slice;
-template <int EPL> struct Slice<uint16_t, EPL> {
-  static constexpr int W = EPL >= 2 ? EPL / 2 : 1;  // 32-bit words (EPL == 1 uses the low half)
-  uint32_t w[W];
-  __device__ __forceinline__ void load(const uint16_t* p) {
-    if constexpr (EPL == 1) {
-      w[0] = *p;
-    } else if constexpr (EPL == 2) {
-      w[0] = *reinterpret_cast<const uint32_t*>(p);
-    } else if constexpr (EPL == 4) {
-      const uint2 v = *reinterpret_cast<const uint2*>(p);
-      w[0] = v.x; w[1] = v.y;
-    } else {
-#pragma unroll
-      for (int q = 0; q < EPL / 8; ++q) {
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p + q * 8);
-        w[4 * q] = v.x; w[4 * q + 1] = v.y; w[4 * q + 2] = v.z; w[4 * q + 3] = v.w;
-      }
-    }
-  }
-  __device__ __forceinline__ void fma(float z, float (&acc)[EPL]) const {
-    if constexpr (EPL == 1) {
-      acc[0] = fmaf(z, bf16lo_to_f32(w[0]), acc[0]);
-    } else {
-#pragma unroll
-      for (int q = 0; q < W; ++q) {
-        acc[2 * q] = fmaf(z, bf16lo_to_f32(w[q]), acc[2 * q]);
-        acc[2 * q + 1] = fmaf(z, bf16hi_to_f32(w[q]), acc[2 * q + 1]);
-      }
-    }
-  }
-};
-template <int EPL> struct Slice<float, EPL> {
-  float w[EPL];
-  __device__ __forceinline__ void load(const float* p) {
-    if constexpr (EPL == 1) {
-      w[0] = *p;
-    } else if constexpr (EPL == 2) {
-      const float2 v = *reinterpret_cast<const float2*>(p);
-      w[0] = v.x; w[1] = v.y;
-    } else {
-#pragma unroll
-      for (int q = 0; q < EPL / 4; ++q) {
-        const float4 v = *reinterpret_cast<const float4*>(p + q * 4);
-        w[4 * q] = v.x; w[4 * q + 1] = v.y; w[4 * q + 2] = v.z; w[4 * q + 3] = v.w;
-      }
-    }
-  }
-  __device__ __forceinline__ void fma(float z, float (&acc)[EPL]) const {
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] = fmaf(z, w[e], acc[e]);
-  }
-};
-
 template <typename TS, int EPL>
 __global__ __launch_bounds__(256) void ffn_down_kernel(FwdArgs a, int P, int64_t i0, int64_t i1) {
   constexpr int U = 8;  // rows in flight per wave
@@ -356,14 +300,8 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t s, int64_t chunk) {
   // up: (column, z) list of the non-overflow rows; down: their y rows, d_model
   // cut into P slices of 64*EPL elements
   const int parts = a.n_tiles < kParts ? a.n_tiles : kParts;
-  constexpr int kMaxEpl = sizeof(TS) == 2 ? 16 : 8;
-  int epl = 1;
-  for (int e = kMaxEpl; e >= 1; e >>= 1)
-    if (a.D % (64 * e) == 0 && a.D / (64 * e) >= kParts) {
-      epl = e;
-      break;
-    }
-  const int P = a.D / (64 * epl);
+  int epl, P;
+  pick_slices(a.D, (int)sizeof(TS), &epl, &P);
   if (chunk <= 0) chunk = a.N;
   for (int64_t i0 = 0; i0 < a.N; i0 += chunk) {
     const int64_t i1 = i0 + chunk < a.N ? i0 + chunk : a.N;

@@ -11,7 +11,7 @@
 // ascending order.
 //
 // Kernels
-//   route_rows     thread per row: row_nnz, is_dense, and the ELL entries of
+//   route_rows     wave per row: row_nnz, is_dense, and the ELL entries of
 //                  ELL rows (vals, global cols, saved a).
 //   launch_compact ascending dense-row list + capacity status.
 //   route_dense_h  thread per (dense row, column): dense activation rows,
@@ -23,29 +23,64 @@
 namespace twell {
 namespace {
 
+// Maximum of v over the 64 lanes of a wave (every lane gets it).
+__device__ __forceinline__ int wave_max_i(int v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = max(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// Exclusive prefix sum of v over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_excl_scan(int v) {
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if ((threadIdx.x & 63) >= off) x += y;
+  }
+  return x - v;
+}
+
+// One wave per row. Pass 1: row_nnz and the dense decision from the tile
+// counts (64 tiles per load). Pass 2 (ELL rows): lane l takes tile jb+l of a
+// 64-tile batch; iteration s copies slot s of every lane's tile to ELL
+// position (start of the tile + s), so all loads of one iteration are in
+// flight together.
 template <typename TS>
 __global__ __launch_bounds__(256) void route_rows(RouteArgs a) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (i >= a.N) return;
   const int64_t N = a.N;
-  int32_t nnz = 0;
-  for (int j = 0; j < a.n_tiles; ++j) nnz += a.counts[(size_t)j * N + i];
+  int nnz = 0;
+  for (int jb = 0; jb < a.n_tiles; jb += 64) {
+    const int jl = jb + lane;
+    nnz += (int)wave_sum_dpp(jl < a.n_tiles ? (float)a.counts[(size_t)jl * N + i] : 0.f);  // exact: < 2^24
+  }
   const bool dense = nnz > a.row_cap || a.ovf_flag[i] != 0;
-  a.row_nnz[i] = nnz;
-  a.is_dense[i] = dense ? 1 : 0;
+  if (lane == 0) {
+    a.row_nnz[i] = nnz;
+    a.is_dense[i] = dense ? 1 : 0;
+  }
   if (dense) return;
   const TS* vals = reinterpret_cast<const TS*>(a.vals);
   TS* ev = reinterpret_cast<TS*>(a.ell_vals);
-  int k = 0;
-  for (int j = 0; j < a.n_tiles; ++j) {
-    const int cnt = a.counts[(size_t)j * N + i];
-    for (int s = 0; s < cnt; ++s, ++k) {
-      const size_t src = ((size_t)j * a.slots + s) * N + i;
-      const size_t dst = (size_t)k * N + i;
-      ev[dst] = vals[src];
-      a.ell_cols[dst] = j * a.tile_n + a.cols[src];
-      a.ell_a[dst] = a.a_save[src];
+  int base = 0;
+  for (int jb = 0; jb < a.n_tiles; jb += 64) {
+    const int jl = jb + lane;
+    const int cnt = jl < a.n_tiles ? (int)a.counts[(size_t)jl * N + i] : 0;  // <= S: the row did not overflow
+    const int start = base + wave_excl_scan(cnt);
+    const int maxc = wave_max_i(cnt);
+    for (int sl = 0; sl < maxc; ++sl) {
+      if (sl < cnt) {
+        const size_t src = ((size_t)jl * a.slots + sl) * N + i;
+        const size_t dst = (size_t)(start + sl) * N + i;
+        ev[dst] = vals[src];
+        a.ell_cols[dst] = jl * a.tile_n + a.cols[src];
+        a.ell_a[dst] = a.a_save[src];
+      }
     }
+    base = __builtin_amdgcn_readlane(start + cnt, 63);  // start already includes base
   }
 }
 
@@ -85,7 +120,7 @@ __global__ __launch_bounds__(256) void route_dense_h(RouteArgs a) {
 
 template <typename TS>
 hipError_t launch_t(const RouteArgs& a, hipStream_t s) {
-  TWELL_LAUNCH("route_rows", route_rows<TS>, dim3((unsigned)((a.N + 255) / 256)), 256, 0, s, a);
+  TWELL_LAUNCH("route_rows", route_rows<TS>, dim3((unsigned)((a.N + 3) / 4)), 256, 0, s, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   err = launch_compact(a.is_dense, a.N, a.dense_rows, a.dense_cap, a.n_dense, a.status, 2u /*TWELL_DEV_DENSE_CAPACITY*/, s);

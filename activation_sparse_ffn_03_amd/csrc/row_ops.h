@@ -89,9 +89,80 @@ __device__ __forceinline__ void store_row(float* __restrict__ dst, const float (
   }
 }
 
+// EPL consecutive storage elements per lane, loaded with one or two vector
+// loads and widened to fp32.
+template <typename TS, int EPL> struct Slice;
+template <int EPL> struct Slice<uint16_t, EPL> {
+  static constexpr int W = EPL >= 2 ? EPL / 2 : 1;  // 32-bit words (EPL == 1 uses the low half)
+  uint32_t w[W];
+  __device__ __forceinline__ void load(const uint16_t* p) {
+    if constexpr (EPL == 1) {
+      w[0] = *p;
+    } else if constexpr (EPL == 2) {
+      w[0] = *reinterpret_cast<const uint32_t*>(p);
+    } else if constexpr (EPL == 4) {
+      const uint2 v = *reinterpret_cast<const uint2*>(p);
+      w[0] = v.x; w[1] = v.y;
+    } else {
+#pragma unroll
+      for (int q = 0; q < EPL / 8; ++q) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(p + q * 8);
+        w[4 * q] = v.x; w[4 * q + 1] = v.y; w[4 * q + 2] = v.z; w[4 * q + 3] = v.w;
+      }
+    }
+  }
+  __device__ __forceinline__ void fma(float z, float (&acc)[EPL]) const {
+    if constexpr (EPL == 1) {
+      acc[0] = fmaf(z, bf16lo_to_f32(w[0]), acc[0]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < W; ++q) {
+        acc[2 * q] = fmaf(z, bf16lo_to_f32(w[q]), acc[2 * q]);
+        acc[2 * q + 1] = fmaf(z, bf16hi_to_f32(w[q]), acc[2 * q + 1]);
+      }
+    }
+  }
+};
+template <int EPL> struct Slice<float, EPL> {
+  float w[EPL];
+  __device__ __forceinline__ void load(const float* p) {
+    if constexpr (EPL == 1) {
+      w[0] = *p;
+    } else if constexpr (EPL == 2) {
+      const float2 v = *reinterpret_cast<const float2*>(p);
+      w[0] = v.x; w[1] = v.y;
+    } else {
+#pragma unroll
+      for (int q = 0; q < EPL / 4; ++q) {
+        const float4 v = *reinterpret_cast<const float4*>(p + q * 4);
+        w[4 * q] = v.x; w[4 * q + 1] = v.y; w[4 * q + 2] = v.z; w[4 * q + 3] = v.w;
+      }
+    }
+  }
+  __device__ __forceinline__ void fma(float z, float (&acc)[EPL]) const {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = fmaf(z, w[e], acc[e]);
+  }
+};
+
 __device__ __forceinline__ int readlane_i(int v, int l) { return __builtin_amdgcn_readlane(v, l); }
 __device__ __forceinline__ float readlane_f(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// d_model slicing of the sliced kernels: P slices of 64*EPL elements, EPL the
+// largest power of two (<= 32 bytes per lane) that still gives >= 8 slices
+// (one per XCD); EPL = 1 when d_model < 512.
+inline void pick_slices(int D, int esz, int* epl_out, int* P_out) {
+  const int max_epl = esz == 2 ? 16 : 8;
+  int epl = 1;
+  for (int e = max_epl; e >= 1; e >>= 1)
+    if (D % (64 * e) == 0 && D / (64 * e) >= 8) {
+      epl = e;
+      break;
+    }
+  *epl_out = epl;
+  *P_out = D / (64 * epl);
 }
 
 // Dispatch helper: smallest M in {1,2,4,8,16} with M*64 chunks covering nch.

@@ -297,7 +297,6 @@ twell_status twell_ffn_bwd(const twell_dims* dims, twell_dtype dtype, const twel
   a.ws.col_ptr = reinterpret_cast<int32_t*>(base + L.col_ptr);
   a.ws.blk_cnt = reinterpret_cast<int32_t*>(base + L.blk_cnt);
   a.ws.grp_off = reinterpret_cast<int32_t*>(base + L.grp_off);
-  a.ws.part = reinterpret_cast<float*>(base + L.part);
   return hip_status(twell::launch_ffn_bwd(a, (hipStream_t)stream), "twell_ffn_bwd");
 }
 

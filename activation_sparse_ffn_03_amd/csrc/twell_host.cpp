@@ -113,7 +113,6 @@ BwdLayout bwd_layout(const Shape& s) {
   L.col_ptr = take(((size_t)s.F + 1) * 4);
   L.blk_cnt = take((size_t)s.nrb * s.F * 4);
   L.grp_off = take((size_t)s.dense_cap * s.G * 4);
-  L.part = take((size_t)s.dense_cap * s.G * s.D * 4);
   L.total = off;
   return L;
 }

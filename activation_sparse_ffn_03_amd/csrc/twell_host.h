@@ -26,7 +26,7 @@ struct Shape {
 
 // Offsets (bytes from the workspace base) of every backward workspace array.
 struct BwdLayout {
-  size_t row_ptr, dense_pos, pair_col, coef, csc_pair, csc_row, col_ptr, blk_cnt, grp_off, part, total;
+  size_t row_ptr, dense_pos, pair_col, coef, csc_pair, csc_row, col_ptr, blk_cnt, grp_off, total;
 };
 
 // Validate dims/dtype; on failure returns the status and sets *why.

@@ -105,7 +105,6 @@ struct BwdWorkspace {
   int32_t* col_ptr;    // [F+1]
   int32_t* blk_cnt;    // [n_rb][F]
   int32_t* grp_off;    // [dense_cap][G]
-  float* part;         // [dense_cap][G][D]
 };
 
 struct BwdArgs {

@@ -81,10 +81,13 @@ def kernel_work(name, w, st, train):
     if name == "ffn_down_kernel":  # W_down once; cols + z read; y written (fp32)
         byt = F * D * e + nnz * (2 + 4) + n_t * N * 2 + N * D * 4
         return {"flops": 2.0 * D * nnz, "bytes": byt, "bound": "hbm"}
-    if name == "bwd_rows":
-        byt = N * D * e + 3 * F * D * e + nnz_ell * (e + 8) + N * D * 4 + nnz * 20
-        return {"flops": 6.0 * D * nnz, "bytes": byt, "bound": "hbm"}
-    if name == "bwd_dw":
+    if name == "bwd_dz_ell":   # dy, W_down once; row-ELL read; (col, z, da, dg) records written
+        byt = N * D * e + F * D * e + nnz_ell * (e + 8) + nnz_ell * 20
+        return {"flops": 2.0 * D * nnz_ell, "bytes": byt, "bound": "hbm"}
+    if name == "bwd_dx":       # W_up, W_gate once; records read; dx written (fp32)
+        byt = 2 * F * D * e + nnz * 12 + N * D * 4
+        return {"flops": 4.0 * D * nnz, "bytes": byt, "bound": "hbm"}
+    if name == "bwd_dw":       # x, dy once; records read via the column transpose; 3 dW written (fp32)
         byt = 2 * N * D * e + nnz * 24 + 3 * F * D * 4
         return {"flops": 6.0 * D * nnz, "bytes": byt, "bound": "hbm"}
     return None
@@ -131,7 +134,8 @@ KERNEL_SOURCES = {
     "gate_mfma_bf16": ["gate_pack.hip", "twell_device.h"],
     "ffn_up_kernel": ["fused_fwd.hip", "row_ops.h", "twell_device.h"],
     "ffn_down_kernel": ["fused_fwd.hip", "row_ops.h", "twell_device.h"],
-    "bwd_rows": ["bwd.hip", "row_ops.h", "twell_device.h"],
+    "bwd_dz_ell": ["bwd.hip", "row_ops.h", "twell_device.h"],
+    "bwd_dx": ["bwd.hip", "row_ops.h", "twell_device.h"],
     "bwd_dw": ["bwd.hip", "row_ops.h", "twell_device.h"],
 }
 

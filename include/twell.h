@@ -190,7 +190,9 @@ twell_status twell_route_hybrid(const twell_dims* dims, twell_dtype dtype, const
  *   dW_down[c] = sum_i h_ic a_ic dy_i.
  * dy: [N][D] storage dtype. dx: [N][D] fp32; dw_*: [F][D] fp32; all four are
  * fully overwritten (deterministic: no floating-point atomics). For dense rows
- * a is recomputed from x. ws: at least twell_sizes.ws_bwd bytes.
+ * a is recomputed from x. Dense rows beyond dense_cap (status bit set by
+ * twell_route_hybrid) contribute nothing and get dx = 0.
+ * ws: at least twell_sizes.ws_bwd bytes.
  * Returns TWELL_ERR_UNSUPPORTED for d_ff > 32768. */
 twell_status twell_ffn_bwd(const twell_dims* dims, twell_dtype dtype, const twell_hybrid* hyb,
                            const void* x, const void* dy, const void* w_gate_t,

@@ -252,6 +252,7 @@ def _check_backward(w, pl, grads, tol=1e-4):
     dict(N=2048, D=512, F=1300, K=40),
     dict(N=1024, D=128, F=512, K=4, slots=4, dense_cap=1024),
     dict(N=700, D=2048, F=640, K=12, dense_cap=700),
+    dict(N=512, D=512, F=1300, K=40, tile_n=16),   # 82 tiles: the router's tile batches of 64
 ])
 def test_route_and_backward(case):
     case = dict(case)
