@@ -25,8 +25,6 @@
 namespace twell {
 namespace {
 
-constexpr int BK = 64;
-constexpr int AS = BK + 8;      // LDS row stride in bf16 (144 B: 16 consecutive rows hit 16 distinct bank groups)
 constexpr int kPackCols = 128;  // columns one pack_epilogue call covers (two 64-lane ballots)
 constexpr int BN = kPackCols;   // N tile of the fp32 / pack_from_g kernels
 constexpr int GS = kPackCols + 4;  // LDS row stride of the fp32 epilogue tile (floats)
@@ -196,20 +194,25 @@ __device__ void pack_epilogue(const float* Gs, int rows, int64_t row0, int n0, c
 // registers: with PF = 2 two register sets alternate, so the load of K-step
 // k+2 is issued while step k feeds the matrix cores and has two steps of
 // MFMA work to arrive in.
-template <int BM_, int BN_, int WGM_, int WGN_, int PF_ = 1>
+template <int BM_, int BN_, int WGM_, int WGN_, int PF_ = 1, int BK_ = 64, int OCC_ = 1>
 struct MfmaCfg {
   static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_;
-  static constexpr int PF = PF_;  // K-steps fetched ahead into registers (1 or 2)
+  static constexpr int PF = PF_;    // K-steps fetched ahead into registers (1 or 2)
+  static constexpr int BK = BK_;    // K per LDS stage (32 or 64)
+  static constexpr int OCC = OCC_;  // occupancy hint: waves per SIMD the register budget aims at
+  static constexpr int KC = BK / 8;  // 16-byte chunks per row per stage
+  static constexpr int AS = BK + 8;  // LDS row stride in bf16 (16 consecutive rows hit distinct bank groups)
   static constexpr int NT = WGM * WGN * 64;
   static constexpr int WM = BM / WGM, WN = BN / WGN;
   static constexpr int FM = WM / 16, FN = WN / 16;
-  static constexpr int A_CH = BM * (BK / 8) / NT;  // 16-byte chunks per thread per stage
-  static constexpr int B_CH = BN * (BK / 8) / NT;
+  static constexpr int A_CH = BM * KC / NT;  // 16-byte chunks per thread per stage
+  static constexpr int B_CH = BN * KC / NT;
   static constexpr int LDS = (2 * BM * AS + 2 * BN * AS) * 2;
   static constexpr int EPI_FIT = LDS / (GS * 4);
   static constexpr int EPI_ROWS = EPI_FIT >= 256 && BM >= 256 ? 256 : EPI_FIT >= 128 && BM >= 128 ? 128 : 64;
   static_assert(WM % 16 == 0 && WN % 16 == 0, "wave tile must be whole fragments");
-  static_assert(BM * (BK / 8) % NT == 0 && BN * (BK / 8) % NT == 0, "stage must split evenly over threads");
+  static_assert(BK == 32 || BK == 64, "K step");
+  static_assert(BM * KC % NT == 0 && BN * KC % NT == 0, "stage must split evenly over threads");
   static_assert(BN % 128 == 0, "N tile must be whole 128-column pack groups");
   static_assert(BM % EPI_ROWS == 0 && EPI_ROWS * GS * 4 <= LDS, "epilogue staging must fit");
   static_assert(LDS + BM * 8 <= 160 * 1024, "LDS budget of a gfx950 workgroup");
@@ -235,12 +238,13 @@ __device__ __forceinline__ void tile_of_block(int b, int nblocks, int mbc, int n
 // In MODE_DENSE, A rows are gathered through the overflow list. Both operands
 // are K-contiguous.
 template <class C, int MODE>
-__global__ __launch_bounds__(C::NT, 1) void gate_mfma_bf16(const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(C::NT, C::OCC) void gate_mfma_bf16(const uint16_t* __restrict__ x,
                                                           const uint16_t* __restrict__ w, int D, int mbc,
                                                           int ncb, Epi e) {
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
   __shared__ float ts[C::BM];
   __shared__ int32_t toks[C::BM];
+  constexpr int AS = C::AS, KC = C::KC, BK = C::BK;
   uint16_t* As = reinterpret_cast<uint16_t*>(smem);
   uint16_t* Bs = As + 2 * C::BM * AS;
 
@@ -260,26 +264,25 @@ __global__ __launch_bounds__(C::NT, 1) void gate_mfma_bf16(const uint16_t* __res
   }
   stage_rows(m0, C::BM, e, ts, toks);  // visible after the first barrier below
 
+  // Rows past the last token (or overflow row) and columns past d_ff load row
+  // 0 instead: their g is never stored (the epilogue skips those rows and
+  // masks those columns), so the loads need no bounds branches.
   const uint16_t* a_src[C::A_CH];
-  bool a_ok[C::A_CH];
 #pragma unroll
   for (int r = 0; r < C::A_CH; ++r) {
     const int q = tid + C::NT * r;
-    const int row = q >> 3, kc = q & 7;
+    const int row = q / KC, kc = q % KC;
     const int64_t lr = m0 + row;
-    a_ok[r] = lr < mlimit;
-    int64_t tok = lr;
-    if (MODE == MODE_DENSE) tok = a_ok[r] ? (int64_t)e.rows[lr] : 0;
-    a_src[r] = x + (a_ok[r] ? tok : 0) * (int64_t)D + kc * 8;
+    int64_t tok = lr < mlimit ? lr : 0;
+    if (MODE == MODE_DENSE) tok = lr < mlimit ? (int64_t)e.rows[lr] : 0;
+    a_src[r] = x + tok * (int64_t)D + kc * 8;
   }
   const uint16_t* b_src[C::B_CH];
-  bool b_ok[C::B_CH];
 #pragma unroll
   for (int r = 0; r < C::B_CH; ++r) {
     const int q = tid + C::NT * r;
-    const int row = q >> 3, kc = q & 7;
-    b_ok[r] = (n0 + row) < e.F;
-    b_src[r] = w + (int64_t)(b_ok[r] ? n0 + row : 0) * D + kc * 8;
+    const int row = q / KC, kc = q % KC;
+    b_src[r] = w + (int64_t)((n0 + row) < e.F ? n0 + row : 0) * D + kc * 8;
   }
 
   struct Regs {
@@ -287,11 +290,9 @@ __global__ __launch_bounds__(C::NT, 1) void gate_mfma_bf16(const uint16_t* __res
   };
   auto gload = [&](Regs& R, int k0) {
 #pragma unroll
-    for (int r = 0; r < C::A_CH; ++r)
-      R.a[r] = a_ok[r] ? *reinterpret_cast<const u32x4_t*>(a_src[r] + k0) : u32x4_t{0, 0, 0, 0};
+    for (int r = 0; r < C::A_CH; ++r) R.a[r] = *reinterpret_cast<const u32x4_t*>(a_src[r] + k0);
 #pragma unroll
-    for (int r = 0; r < C::B_CH; ++r)
-      R.b[r] = b_ok[r] ? *reinterpret_cast<const u32x4_t*>(b_src[r] + k0) : u32x4_t{0, 0, 0, 0};
+    for (int r = 0; r < C::B_CH; ++r) R.b[r] = *reinterpret_cast<const u32x4_t*>(b_src[r] + k0);
   };
   auto lstore = [&](const Regs& R, int buf) {
     uint16_t* A = As + buf * C::BM * AS;
@@ -299,12 +300,12 @@ __global__ __launch_bounds__(C::NT, 1) void gate_mfma_bf16(const uint16_t* __res
 #pragma unroll
     for (int r = 0; r < C::A_CH; ++r) {
       const int q = tid + C::NT * r;
-      *reinterpret_cast<u32x4_t*>(A + (q >> 3) * AS + (q & 7) * 8) = R.a[r];
+      *reinterpret_cast<u32x4_t*>(A + (q / KC) * AS + (q % KC) * 8) = R.a[r];
     }
 #pragma unroll
     for (int r = 0; r < C::B_CH; ++r) {
       const int q = tid + C::NT * r;
-      *reinterpret_cast<u32x4_t*>(B + (q >> 3) * AS + (q & 7) * 8) = R.b[r];
+      *reinterpret_cast<u32x4_t*>(B + (q / KC) * AS + (q % KC) * 8) = R.b[r];
     }
   };
 
@@ -318,7 +319,7 @@ __global__ __launch_bounds__(C::NT, 1) void gate_mfma_bf16(const uint16_t* __res
     const uint16_t* A = As + buf * C::BM * AS;
     const uint16_t* B = Bs + buf * C::BN * AS;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < BK / 32; ++ks) {
       const int kc = ks * 4 + (lane >> 4);
       bf16x8_t af[C::FM], bfr[C::FN];
 #pragma unroll
