@@ -39,7 +39,7 @@ constexpr int kParts = 8;  // one part per XCD
 // Per-row tile offsets: offs[j][i] = number of packed entries of row i in
 // tiles before j (offs[n_t][i] = the row's total), i.e. where tile j's entries
 // start in the row's (column, z) list.
-__global__ __launch_bounds__(256) void ffn_row_offsets(FwdArgs a) {
+__global__ __launch_bounds__(64) void ffn_row_offsets(FwdArgs a) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= a.N) return;
   const int64_t N = a.N;
@@ -294,7 +294,7 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t s, int64_t chunk) {
   const dim3 blk(256);
   hipError_t err;
 
-  TWELL_LAUNCH("ffn_row_offsets", ffn_row_offsets, dim3((unsigned)((a.N + 255) / 256)), blk, 0, s, a);
+  TWELL_LAUNCH("ffn_row_offsets", ffn_row_offsets, dim3((unsigned)((a.N + 63) / 64)), dim3(64), 0, s, a);
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
   // up: (column, z) list of the non-overflow rows; down: their y rows, d_model

@@ -7,11 +7,13 @@
 // conversion pass, no extra round trip through global memory).
 //
 // Kernels
-//   gate_mfma_bf16   BM x BN output tile per workgroup (256x256 with 8 waves,
-//                    or 128x128 with 4), v_mfma_f32_16x16x32_bf16, K-loop of 64
-//                    with two LDS stages; XCD-aware tile order; the epilogue
-//                    stages the fp32 tile in LDS one 128-column group at a time
-//                    and packs it.
+//   gate_mfma_dma    TwELL pack path (bf16): 128x384 output tile per 4-wave
+//                    workgroup, v_mfma_f32_16x16x32_bf16, K-steps of 32 loaded
+//                    straight into a 2-stage LDS ring by global_load_lds;
+//                    XCD-aware tile order; the epilogue stages the fp32 tile in
+//                    LDS one 128-column group at a time and packs it.
+//   gate_mfma_bf16   register-staged variant (128x128, K-steps of 64), used to
+//                    recompute the overflow rows with identical arithmetic.
 //   gate_simt_f32    64x128 fp32 tile, plain FMA (fp32 storage only).
 //   pack_from_g      64x128 tile of a given pre-activation (test entry).
 //   ovf_flags        overflow flag of every row from its true tile counts
@@ -190,14 +192,11 @@ __device__ void pack_epilogue(const float* Gs, int rows, int64_t row0, int n0, c
 
 // Block tile BM x BN of g = x . w^T, WGM x WGN waves, each owning a
 // (BM/WGM) x (BN/WGN) sub-tile of 16x16 v_mfma_f32_16x16x32_bf16 fragments.
-// K advances by BK = 64 through two LDS stages. Global loads go through
-// registers: with PF = 2 two register sets alternate, so the load of K-step
-// k+2 is issued while step k feeds the matrix cores and has two steps of
-// MFMA work to arrive in.
-template <int BM_, int BN_, int WGM_, int WGN_, int PF_ = 1, int BK_ = 64, int OCC_ = 1>
+// K advances by BK through two LDS stages; the next stage is fetched global ->
+// registers while the current one feeds the matrix cores.
+template <int BM_, int BN_, int WGM_, int WGN_, int BK_ = 64, int OCC_ = 1>
 struct MfmaCfg {
   static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_;
-  static constexpr int PF = PF_;    // K-steps fetched ahead into registers (1 or 2)
   static constexpr int BK = BK_;    // K per LDS stage (32 or 64)
   static constexpr int OCC = OCC_;  // occupancy hint: waves per SIMD the register budget aims at
   static constexpr int KC = BK / 8;  // 16-byte chunks per row per stage
@@ -339,34 +338,15 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gate_mfma_bf16(const uint16_t* 
   };
 
   const int KT = D / BK;
-  Regs R0, R1;
-  if constexpr (C::PF == 1) {
-    gload(R0, 0);
-    lstore(R0, 0);
+  Regs R0;
+  gload(R0, 0);
+  lstore(R0, 0);
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    if (kt + 1 < KT) gload(R0, (kt + 1) * BK);
+    compute(kt & 1);
+    if (kt + 1 < KT) lstore(R0, (kt + 1) & 1);
     __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-      if (kt + 1 < KT) gload(R0, (kt + 1) * BK);
-      compute(kt & 1);
-      if (kt + 1 < KT) lstore(R0, (kt + 1) & 1);
-      __syncthreads();
-    }
-  } else {
-    // R0 holds even K-steps, R1 odd ones; LDS buffer = K-step parity.
-    gload(R0, 0);
-    lstore(R0, 0);
-    if (KT > 1) gload(R1, BK);
-    __syncthreads();
-    for (int kt = 0; kt < KT; kt += 2) {
-      if (kt + 2 < KT) gload(R0, (kt + 2) * BK);
-      compute(0);
-      if (kt + 1 < KT) lstore(R1, 1);
-      __syncthreads();
-      if (kt + 1 >= KT) break;
-      if (kt + 3 < KT) gload(R1, (kt + 3) * BK);
-      compute(1);
-      if (kt + 2 < KT) lstore(R0, 0);
-      __syncthreads();
-    }
   }
 
   // Epilogue: the fp32 tile goes through LDS one (EPI_ROWS x 128-column) block
@@ -395,20 +375,182 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gate_mfma_bf16(const uint16_t* 
   }
 }
 
-// Tile configurations of the bf16 gate GEMM. Every configuration accumulates
-// each output element over K in the same order (32-wide MFMA steps, ascending
-// K), so they all produce bit-identical g; the launcher picks by size.
-using GateBig = MfmaCfg<256, 256, 4, 2>;    // 8 waves, 64x128 per wave
-using GateSmall = MfmaCfg<128, 128, 2, 2>;  // 4 waves, 64x64 per wave
-// Problems with at least this many 256x256 tiles (three per CU) use GateBig.
-constexpr int64_t kBigTileMin = 768;
+// ---------------------------------------------------------------- bf16 MFMA GEMM, LDS DMA pipeline
+
+// Variant of gate_mfma_bf16 whose K-steps (32 wide) go straight from global
+// memory into a ring of ST LDS stages with global_load_lds_dwordx4, so up to
+// ST-1 steps are in flight without holding staging registers. Each DMA
+// instruction writes 1 KB = 16 LDS rows of 64 bytes (lane l -> row l/4,
+// 16-byte position l%4). The 16-byte chunk kc of LDS row r sits at position
+// kc ^ dma_swz(r), which keeps the MFMA operand reads free of bank conflicts;
+// each lane therefore fetches the global chunk that belongs at its position.
+// The DMA and its waits are inline assembly: the compiler does not see these
+// LDS writes, so the ring is synchronised by hand (vmcnt per wave, then a
+// workgroup barrier) before a stage is read.
+template <int BM_, int BN_, int WGM_, int WGN_, int ST_ = 4, int OCC_ = 2>
+struct DmaCfg {
+  static constexpr int BM = BM_, BN = BN_, WGM = WGM_, WGN = WGN_, ST = ST_, OCC = OCC_;
+  static constexpr int NT = WGM * WGN * 64, NW = NT / 64;
+  static constexpr int WM = BM / WGM, WN = BN / WGN;
+  static constexpr int FM = WM / 16, FN = WN / 16;
+  static constexpr int ROWB = 64;                    // LDS bytes per row per stage (32 bf16)
+  static constexpr int STAGE = (BM + BN) * ROWB;     // bytes per stage: A rows then B rows
+  static constexpr int LDS = ST * STAGE;
+  static constexpr int GROUPS = (BM + BN) / 16;      // 1 KB DMA groups per stage
+  static constexpr int GPW = GROUPS / NW;            // DMA instructions per wave per stage
+  static constexpr int EPI_FIT = LDS / (GS * 4);
+  static constexpr int EPI_ROWS = EPI_FIT >= 256 && BM >= 256 ? 256 : EPI_FIT >= 128 && BM >= 128 ? 128 : 64;
+  static_assert(WM % 16 == 0 && WN % 16 == 0 && BM % 16 == 0 && BN % 16 == 0, "whole fragments");
+  static_assert(GROUPS % NW == 0, "DMA groups must split evenly over waves");
+  static_assert(BN % 128 == 0, "N tile must be whole 128-column pack groups");
+  static_assert(ST >= 2 && ST <= 4, "ring depth");
+  static_assert(BM % EPI_ROWS == 0 && EPI_ROWS * GS * 4 <= LDS, "epilogue staging must fit");
+  static_assert(LDS + BM * 8 <= 160 * 1024, "LDS budget of a gfx950 workgroup");
+};
+
+// Row -> 2-bit XOR key of the 16-byte positions: rows of any 8-row group
+// differ in (row & 1, key) and rows of any 16-row group in (row & 3, key), so
+// 8 or 16 lanes reading one chunk of consecutive rows hit distinct banks.
+__device__ __forceinline__ int dma_swz(int r) { return ((r >> 2) & 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 1); }
+
+__device__ __forceinline__ void dma_16B(const void* g, uint32_t lds_byte) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane(lds_byte);  // wave-uniform by construction
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 template <class C, int MODE>
-void launch_mfma(const GateArgs& a, int64_t rows, const Epi& e, hipStream_t s, const char* name) {
-  const int mbc = (int)((rows + C::BM - 1) / C::BM), nbc = (a.F + C::BN - 1) / C::BN;
-  TWELL_LAUNCH(name, (gate_mfma_bf16<C, MODE>), dim3(mbc * nbc), C::NT, 0, s, (const uint16_t*)a.x,
-               (const uint16_t*)a.w, a.D, mbc, nbc, e);
+__global__ __launch_bounds__(C::NT, C::OCC) void gate_mfma_dma(const uint16_t* __restrict__ x,
+                                                               const uint16_t* __restrict__ w, int D, int mbc,
+                                                               int ncb, Epi e) {
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
+  __shared__ float ts[C::BM];
+  __shared__ int32_t toks[C::BM];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / C::WGN, wn = wave % C::WGN;
+  int mb_id, nb_id;
+  tile_of_block(blockIdx.x, gridDim.x, mbc, ncb, mb_id, nb_id);
+  const int64_t m0 = (int64_t)mb_id * C::BM;
+  const int n0 = nb_id * C::BN;
+  int64_t mlimit;
+  if (MODE == MODE_DENSE) {
+    mlimit = dense_valid(e);
+    if (m0 >= mlimit) return;
+  } else {
+    mlimit = e.N;
+  }
+  stage_rows(m0, C::BM, e, ts, toks);
+
+  // Sources of this wave's DMA groups (rows past the last token / column past
+  // d_ff read row 0: never stored).
+  const char* src[C::GPW];
+  uint32_t grp_off[C::GPW];
+  const int rin = lane >> 2, p = lane & 3;
+#pragma unroll
+  for (int t = 0; t < C::GPW; ++t) {
+    const int g = wave + C::NW * t;
+    const uint16_t* base;
+    int lrow;
+    if (g < C::BM / 16) {
+      lrow = g * 16 + rin;
+      const int64_t lr = m0 + lrow;
+      int64_t tok = lr < mlimit ? lr : 0;
+      if (MODE == MODE_DENSE) tok = lr < mlimit ? (int64_t)e.rows[lr] : 0;
+      base = x + tok * (int64_t)D;
+    } else {
+      const int r = (g - C::BM / 16) * 16 + rin;
+      lrow = C::BM + r;
+      base = w + (int64_t)((n0 + r) < e.F ? n0 + r : 0) * D;
+    }
+    src[t] = reinterpret_cast<const char*>(base) + ((p ^ dma_swz(lrow & 15)) << 4);
+    grp_off[t] = (uint32_t)((lrow - rin) * C::ROWB);
+  }
+  const uint32_t lds0 =
+      (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)(smem));
+  auto issue = [&](int kt) {
+    const uint32_t sb = lds0 + (uint32_t)((kt % C::ST) * C::STAGE);
+#pragma unroll
+    for (int t = 0; t < C::GPW; ++t) dma_16B(src[t] + (size_t)kt * 64, sb + grp_off[t]);
+  };
+
+  f32x4_t acc[C::FM][C::FN];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int KT = D / 32;
+#pragma unroll
+  for (int st = 0; st < C::ST - 1; ++st)
+    if (st < KT) issue(st);
+  for (int kt = 0; kt < KT; ++kt) {
+    // stage kt is complete for this wave once at most the later stages issued
+    // so far are pending; the barrier extends that to every wave
+    const int later = min(C::ST - 2, KT - 1 - kt);
+    if (later >= 2) wait_vmcnt<2 * C::GPW>();
+    else if (later == 1) wait_vmcnt<C::GPW>();
+    else wait_vmcnt<0>();
+    lds_barrier();  // also: every wave is done reading the buffer refilled below
+    if (kt + C::ST - 1 < KT) issue(kt + C::ST - 1);
+    const char* A = smem + (kt % C::ST) * C::STAGE;
+    const char* B = A + C::BM * C::ROWB;
+    const int kc = lane >> 4;
+    bf16x8_t af[C::FM], bfr[C::FN];
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) {
+      const int R = wm * C::WM + i * 16 + (lane & 15);
+      af[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(A + R * C::ROWB + ((kc ^ dma_swz(R & 15)) << 4)));
+    }
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) {
+      const int R = wn * C::WN + j * 16 + (lane & 15);
+      bfr[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(B + R * C::ROWB + ((kc ^ dma_swz(R & 15)) << 4)));
+    }
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+  }
+  wait_vmcnt<0>();
+  lds_barrier();  // the ring is reused for the epilogue below
+
+  float* Gs = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int cg = 0; cg < C::BN / kPackCols; ++cg) {
+#pragma unroll
+    for (int p0 = 0; p0 < C::BM; p0 += C::EPI_ROWS) {
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) {
+          const int rbase = wm * C::WM + i * 16 - p0;
+          const int cbase = wn * C::WN + j * 16 - cg * kPackCols;
+          if (rbase < 0 || rbase >= C::EPI_ROWS || cbase < 0 || cbase >= kPackCols) continue;
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            Gs[(rbase + 4 * (lane >> 4) + r) * GS + cbase + (lane & 15)] = acc[i][j][r];
+        }
+      __syncthreads();
+      pack_epilogue<uint16_t>(Gs, C::EPI_ROWS, m0 + p0, n0 + cg * kPackCols, e, ts + p0, toks + p0);
+      __syncthreads();
+    }
+  }
 }
+
+// Tile configurations of the bf16 gate GEMM. Both accumulate each output
+// element over K in the same order (32-wide MFMA steps, ascending K), so they
+// produce bit-identical g: the TwELL pack uses the LDS-DMA kernel with a
+// 128x384 tile (four waves of 128x96: the operand reads per MFMA stay within
+// the LDS bandwidth with two such workgroups per CU), the overflow rows the
+// register-staged 128x128 kernel (a few rows, gathered).
+using GatePack = DmaCfg<128, 384, 1, 4, 2, 2>;
+using GateRows = MfmaCfg<128, 128, 2, 2>;
+
 
 // ---------------------------------------------------------------- fp32 SIMT GEMM
 
@@ -509,13 +651,16 @@ __global__ __launch_bounds__(256) void pack_from_g(const float* __restrict__ g, 
 
 // ---------------------------------------------------------------- overflow rows
 
-__global__ __launch_bounds__(256) void ovf_flags(const uint16_t* __restrict__ counts, int64_t N, int n_tiles,
-                                                 int slots, uint8_t* __restrict__ flag) {
+// One lane per token, 64 tokens per workgroup: each tile's counts of the 64
+// tokens are one coalesced 128-byte load, eight tiles in flight at a time.
+__global__ __launch_bounds__(64) void ovf_flags(const uint16_t* __restrict__ counts, int64_t N, int n_tiles,
+                                                int slots, uint8_t* __restrict__ flag) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= N) return;
-  uint8_t f = 0;
-  for (int j = 0; j < n_tiles; ++j) f |= counts[(size_t)j * N + i] > slots;
-  flag[i] = f;
+  int mx = 0;
+#pragma unroll 8
+  for (int j = 0; j < n_tiles; ++j) mx = max(mx, (int)counts[(size_t)j * N + i]);
+  flag[i] = mx > slots ? 1 : 0;
 }
 
 }  // namespace
@@ -546,11 +691,9 @@ hipError_t launch_gate_pack(const GateArgs& a, hipStream_t s) {
     else
       TWELL_LAUNCH("pack_from_g", (pack_from_g<float, MODE_PACK>), dim3(mb * ncb), 256, 0, s, a.g_in, ncb, e);
   } else if (a.is_bf16) {
-    const int64_t big_tiles = ((a.N + 255) / 256) * ((a.F + 255) / 256);
-    if (big_tiles >= kBigTileMin)
-      launch_mfma<GateBig, MODE_PACK>(a, a.N, e, s, "gate_mfma_bf16");
-    else
-      launch_mfma<GateSmall, MODE_PACK>(a, a.N, e, s, "gate_mfma_bf16");
+    const int mbc = (int)((a.N + GatePack::BM - 1) / GatePack::BM), nbc = (a.F + GatePack::BN - 1) / GatePack::BN;
+    TWELL_LAUNCH("gate_mfma_bf16", (gate_mfma_dma<GatePack, MODE_PACK>), dim3(mbc * nbc), GatePack::NT, 0, s,
+                 (const uint16_t*)a.x, (const uint16_t*)a.w, a.D, mbc, nbc, e);
   } else {
     const int64_t mb = (a.N + SBM - 1) / SBM;
     TWELL_LAUNCH("gate_simt_f32", gate_simt_f32<MODE_PACK>, dim3(mb * ncb), 256, 0, s, (const float*)a.x, (const float*)a.w, a.D, ncb, e);
@@ -559,7 +702,7 @@ hipError_t launch_gate_pack(const GateArgs& a, hipStream_t s) {
   if (err != hipSuccess) return err;
 
   // 2. overflow rows from the true counts
-  TWELL_LAUNCH("ovf_flags", ovf_flags, dim3((a.N + 255) / 256), 256, 0, s, a.counts, a.N, a.n_tiles, a.slots, a.ovf_flag);
+  TWELL_LAUNCH("ovf_flags", ovf_flags, dim3((a.N + 63) / 64), 64, 0, s, a.counts, a.N, a.n_tiles, a.slots, a.ovf_flag);
   err = launch_compact(a.ovf_flag, a.N, a.ovf_rows, a.ovf_cap, a.n_ovf, a.status, 1u /*TWELL_DEV_OVF_CAPACITY*/, s);
   if (err != hipSuccess || a.ovf_cap == 0) return err;
 
@@ -572,7 +715,9 @@ hipError_t launch_gate_pack(const GateArgs& a, hipStream_t s) {
     else
       TWELL_LAUNCH("pack_from_g_rows", (pack_from_g<float, MODE_DENSE>), dim3(mb * ncb), 256, 0, s, a.g_in, ncb, e);
   } else if (a.is_bf16) {
-    launch_mfma<GateSmall, MODE_DENSE>(a, a.ovf_cap, e, s, "gate_mfma_bf16_rows");
+    const int mbc = (a.ovf_cap + GateRows::BM - 1) / GateRows::BM, nbc = (a.F + GateRows::BN - 1) / GateRows::BN;
+    TWELL_LAUNCH("gate_mfma_bf16_rows", (gate_mfma_bf16<GateRows, MODE_DENSE>), dim3(mbc * nbc), GateRows::NT, 0, s,
+                 (const uint16_t*)a.x, (const uint16_t*)a.w, a.D, mbc, nbc, e);
   } else {
     const int64_t mb = (a.ovf_cap + SBM - 1) / SBM;
     TWELL_LAUNCH("gate_simt_f32_rows", gate_simt_f32<MODE_DENSE>, dim3(mb * ncb), 256, 0, s, (const float*)a.x, (const float*)a.w, a.D, ncb, e);
