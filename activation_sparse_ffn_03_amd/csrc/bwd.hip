@@ -39,13 +39,20 @@ __global__ __launch_bounds__(256) void dense_groups(BwdArgs a, int G, int32_t* d
   if (o >= a.dense_cap || o >= *a.n_dense) return;
   const TS* h = reinterpret_cast<const TS*>(a.dense_h) + (size_t)o * a.F;
   int run = 0;
+#pragma unroll 2
   for (int g = 0; g < G; ++g) {
     if (lane == 0) a.ws.grp_off[(size_t)o * G + g] = run;
-    const int c1 = min(a.F, (g + 1) * kDenseChunk);
-    for (int cb = g * kDenseChunk; cb < c1; cb += 64) {
-      const int c = cb + lane;
-      run += __popcll(ballot(c < c1 && Store<TS>::load(h, c) > 0.f));
+    // the chunk's eight 64-column blocks are loaded together (clamped column,
+    // no branch around the load), then counted
+    float v[kDenseChunk / 64];
+#pragma unroll
+    for (int b = 0; b < kDenseChunk / 64; ++b) {
+      const int c = g * kDenseChunk + b * 64 + lane;
+      const float hv = Store<TS>::load(h, min(c, a.F - 1));
+      v[b] = c < a.F ? hv : 0.f;
     }
+#pragma unroll
+    for (int b = 0; b < kDenseChunk / 64; ++b) run += __popcll(ballot(v[b] > 0.f));
   }
   if (lane == 0) dense_nnz[o] = run;
 }
@@ -242,7 +249,7 @@ __global__ __launch_bounds__(256) void bwd_dz_dense(BwdArgs a, int G) {
 // Dense rows beyond the dense capacity have no records and get dx = 0.
 template <typename TS, int EPL>
 __global__ __launch_bounds__(256) void bwd_dx(BwdArgs a, int P) {
-  constexpr int U = 4;
+  constexpr int U = 8;
   const int lane = threadIdx.x & 63;
   const int p = blockIdx.x % P;
   const int64_t i = (int64_t)(blockIdx.x / P) * 4 + (threadIdx.x >> 6);
@@ -316,6 +323,7 @@ __global__ __launch_bounds__(256) void csc_coltotal(const int32_t* __restrict__ 
   const int c = blockIdx.x * blockDim.x + threadIdx.x;
   if (c >= F) return;
   int32_t s = 0;
+#pragma unroll 8
   for (int b = 0; b < nrb; ++b) s += blk_cnt[(size_t)b * F + c];
   col_ptr[c] = s;
 }
@@ -385,7 +393,7 @@ __global__ __launch_bounds__(64) void csc_fill(const int32_t* __restrict__ row_p
 //   dW_gate^T[c][slice] += dg * x_i[slice].
 template <typename TS, int EPL>
 __global__ __launch_bounds__(256) void bwd_dw(BwdArgs a, int P) {
-  constexpr int U = 4;
+  constexpr int U = 8;
   const int lane = threadIdx.x & 63;
   const int p = blockIdx.x % P;
   const int64_t c = (int64_t)(blockIdx.x / P) * 4 + (threadIdx.x >> 6);
