@@ -242,20 +242,34 @@ __global__ __launch_bounds__(256) void bwd_dz_dense(BwdArgs a, int G) {
 
 // --------------------------------------------------------------- dx pass
 
+// Lane group g of a sliced wave reads entry k + u*RPI + g: a wave-uniform
+// readlane when one group spans the wave, else a cross-lane shuffle.
+template <int RPI>
+__device__ __forceinline__ int entry_i(int v, int k) {
+  if constexpr (RPI == 1) return __builtin_amdgcn_readlane(v, k);
+  else return __shfl(v, k, 64);
+}
+template <int RPI>
+__device__ __forceinline__ float entry_f(float v, int k) {
+  if constexpr (RPI == 1) return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), k));
+  else return __shfl(v, k, 64);
+}
+
 // Every row (ELL and dense-backup alike): its records are contiguous in CSR
-// order. Part p owns the d_model slice [p*64*EPL, (p+1)*64*EPL) of dx, so each
-// XCD gathers only that slice of the W_up / W_gate rows.
+// order. Part p owns a d_model slice of dx (pick_slices), so each XCD gathers
+// only that slice of the W_up / W_gate rows, 16 bytes per lane:
 //   dx_i[slice] = sum over records (da * W_up^T[c][slice] + dg * W_gate^T[c][slice])
 // Dense rows beyond the dense capacity have no records and get dx = 0.
-template <typename TS, int EPL>
+template <typename TS, int EPL, int RPI>
 __global__ __launch_bounds__(256) void bwd_dx(BwdArgs a, int P) {
-  constexpr int U = 8;
-  const int lane = threadIdx.x & 63;
+  constexpr int LPR = 64 / RPI;
+  constexpr int U = RPI >= 8 ? 1 : 8 / RPI;
+  const int lane = threadIdx.x & 63, g = lane / LPR;
   const int p = blockIdx.x % P;
   const int64_t i = (int64_t)(blockIdx.x / P) * 4 + (threadIdx.x >> 6);
   if (i >= a.N) return;
   const int D = a.D;
-  const int d0 = (p * 64 + lane) * EPL;
+  const int d0 = p * (LPR * EPL) + (lane % LPR) * EPL;
   const TS* __restrict__ wu = reinterpret_cast<const TS*>(a.w_up) + d0;
   const TS* __restrict__ wg = reinterpret_cast<const TS*>(a.w_gate) + d0;
   const int32_t q0 = a.ws.row_ptr[i], q1 = a.ws.row_ptr[i + 1];
@@ -272,16 +286,18 @@ __global__ __launch_bounds__(256) void bwd_dx(BwdArgs a, int P) {
       da_l = cf.y;
       dg_l = cf.z;
     }
-    for (int k = 0; k < n; k += U) {
+    for (int k = 0; k < n; k += U * RPI) {
       Slice<TS, EPL> su[U], sg[U];
       float da[U], dg[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int kk = min(k + u, n - 1);
-        const int c = readlane_i(c_l, kk);
-        const bool ok = (unsigned)c < (unsigned)a.F && k + u < n;
-        da[u] = ok ? readlane_f(da_l, kk) : 0.f;
-        dg[u] = ok ? readlane_f(dg_l, kk) : 0.f;
+        const int kk = k + u * RPI + g;
+        const int ks = min(kk, n - 1);
+        const int c = entry_i<RPI>(c_l, ks);
+        const bool ok = kk < n && (unsigned)c < (unsigned)a.F;
+        const float da_v = entry_f<RPI>(da_l, ks), dg_v = entry_f<RPI>(dg_l, ks);
+        da[u] = ok ? da_v : 0.f;
+        dg[u] = ok ? dg_v : 0.f;
         const size_t row = (size_t)(ok ? c : 0) * D;
         su[u].load(wu + row);
         sg[u].load(wg + row);
@@ -293,9 +309,12 @@ __global__ __launch_bounds__(256) void bwd_dx(BwdArgs a, int P) {
       }
     }
   }
-  float* dst = a.dx + (size_t)i * D + d0;
+  combine_groups<EPL, RPI>(acc);
+  if (lane < LPR) {
+    float* dst = a.dx + (size_t)i * D + d0;
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) dst[e] = acc[e];
+    for (int e = 0; e < EPL; ++e) dst[e] = acc[e];
+  }
 }
 
 // --------------------------------------------------------------- column transpose
@@ -388,18 +407,19 @@ __global__ __launch_bounds__(64) void csc_fill(const int32_t* __restrict__ row_p
 // --------------------------------------------------------------- weight gradients
 
 // Wave per (column c, d_model slice p): the column's records in ascending row
-// order (from the column transpose), U token rows in flight:
+// order (from the column transpose), token-row slices read 16 bytes per lane:
 //   dW_down[c][slice] += z * dy_i[slice], dW_up^T[c][slice] += da * x_i[slice],
 //   dW_gate^T[c][slice] += dg * x_i[slice].
-template <typename TS, int EPL>
+template <typename TS, int EPL, int RPI>
 __global__ __launch_bounds__(256) void bwd_dw(BwdArgs a, int P) {
-  constexpr int U = 8;
-  const int lane = threadIdx.x & 63;
+  constexpr int LPR = 64 / RPI;
+  constexpr int U = RPI >= 8 ? 1 : 8 / RPI;
+  const int lane = threadIdx.x & 63, g = lane / LPR;
   const int p = blockIdx.x % P;
   const int64_t c = (int64_t)(blockIdx.x / P) * 4 + (threadIdx.x >> 6);
   if (c >= a.F) return;
   const int D = a.D;
-  const int d0 = (p * 64 + lane) * EPL;
+  const int d0 = p * (LPR * EPL) + (lane % LPR) * EPL;
   const TS* __restrict__ x = reinterpret_cast<const TS*>(a.x) + d0;
   const TS* __restrict__ dy = reinterpret_cast<const TS*>(a.dy) + d0;
   float accD[EPL], accU[EPL], accG[EPL];
@@ -414,17 +434,19 @@ __global__ __launch_bounds__(256) void bwd_dw(BwdArgs a, int P) {
       i_l = a.ws.csc_row[qb + lane];
       cf = a.ws.coef[a.ws.csc_pair[qb + lane]];
     }
-    for (int k = 0; k < n; k += U) {
+    for (int k = 0; k < n; k += U * RPI) {
       Slice<TS, EPL> sd[U], sx[U];
       float z[U], da[U], dg[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int kk = min(k + u, n - 1);
-        const bool ok = k + u < n;
-        const size_t row = (size_t)readlane_i(i_l, kk) * D;
-        z[u] = ok ? readlane_f(cf.x, kk) : 0.f;
-        da[u] = ok ? readlane_f(cf.y, kk) : 0.f;
-        dg[u] = ok ? readlane_f(cf.z, kk) : 0.f;
+        const int kk = k + u * RPI + g;
+        const int ks = min(kk, n - 1);
+        const bool ok = kk < n;
+        const size_t row = (size_t)entry_i<RPI>(i_l, ks) * D;
+        const float zv = entry_f<RPI>(cf.x, ks), dav = entry_f<RPI>(cf.y, ks), dgv = entry_f<RPI>(cf.z, ks);
+        z[u] = ok ? zv : 0.f;
+        da[u] = ok ? dav : 0.f;
+        dg[u] = ok ? dgv : 0.f;
         sd[u].load(dy + row);
         sx[u].load(x + row);
       }
@@ -436,12 +458,17 @@ __global__ __launch_bounds__(256) void bwd_dw(BwdArgs a, int P) {
       }
     }
   }
-  const size_t ro = (size_t)c * D + d0;
+  combine_groups<EPL, RPI>(accD);
+  combine_groups<EPL, RPI>(accU);
+  combine_groups<EPL, RPI>(accG);
+  if (lane < LPR) {
+    const size_t ro = (size_t)c * D + d0;
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    a.dw_down[ro + e] = accD[e];
-    a.dw_up[ro + e] = accU[e];
-    a.dw_gate[ro + e] = accG[e];
+    for (int e = 0; e < EPL; ++e) {
+      a.dw_down[ro + e] = accD[e];
+      a.dw_up[ro + e] = accU[e];
+      a.dw_gate[ro + e] = accG[e];
+    }
   }
 }
 
@@ -487,22 +514,16 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t s) {
   }
 
   // dx: every row, d_model sliced
-  int epl, P;
-  pick_slices(a.D, (int)sizeof(TS), &epl, &P);
+  const SliceGeom geom = pick_slices(a.D, (int)sizeof(TS));
+  const int P = geom.P;
   const dim3 gdx((unsigned)(((a.N + 3) / 4) * P));
-  switch (epl) {
-    case 1: TWELL_LAUNCH("bwd_dx", (bwd_dx<TS, 1>), gdx, blk, 0, s, a, P); break;
-    case 2: TWELL_LAUNCH("bwd_dx", (bwd_dx<TS, 2>), gdx, blk, 0, s, a, P); break;
-    case 4: TWELL_LAUNCH("bwd_dx", (bwd_dx<TS, 4>), gdx, blk, 0, s, a, P); break;
-    case 8: TWELL_LAUNCH("bwd_dx", (bwd_dx<TS, 8>), gdx, blk, 0, s, a, P); break;
-    case 16:
-      if constexpr (sizeof(TS) == 2) {
-        TWELL_LAUNCH("bwd_dx", (bwd_dx<TS, 16>), gdx, blk, 0, s, a, P);
-        break;
-      }
-      return hipErrorInvalidValue;
-    default: return hipErrorInvalidValue;
+#define TWELL_DX(E, R) TWELL_LAUNCH("bwd_dx", (bwd_dx<TS, E, R>), gdx, blk, 0, s, a, P)
+  if constexpr (sizeof(TS) == 2) {
+    TWELL_SLICED_CASES(8, TWELL_DX)
+  } else {
+    TWELL_SLICED_CASES(4, TWELL_DX)
   }
+#undef TWELL_DX
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
   // column transpose of the records (stable: rows ascend within a column)
@@ -517,19 +538,13 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t s) {
 
   // weight gradients: column-owned, d_model sliced
   const dim3 gdw((unsigned)(((a.F + 3) / 4) * (int64_t)P));
-  switch (epl) {
-    case 1: TWELL_LAUNCH("bwd_dw", (bwd_dw<TS, 1>), gdw, blk, 0, s, a, P); break;
-    case 2: TWELL_LAUNCH("bwd_dw", (bwd_dw<TS, 2>), gdw, blk, 0, s, a, P); break;
-    case 4: TWELL_LAUNCH("bwd_dw", (bwd_dw<TS, 4>), gdw, blk, 0, s, a, P); break;
-    case 8: TWELL_LAUNCH("bwd_dw", (bwd_dw<TS, 8>), gdw, blk, 0, s, a, P); break;
-    case 16:
-      if constexpr (sizeof(TS) == 2) {
-        TWELL_LAUNCH("bwd_dw", (bwd_dw<TS, 16>), gdw, blk, 0, s, a, P);
-        break;
-      }
-      return hipErrorInvalidValue;
-    default: return hipErrorInvalidValue;
+#define TWELL_DW(E, R) TWELL_LAUNCH("bwd_dw", (bwd_dw<TS, E, R>), gdw, blk, 0, s, a, P)
+  if constexpr (sizeof(TS) == 2) {
+    TWELL_SLICED_CASES(8, TWELL_DW)
+  } else {
+    TWELL_SLICED_CASES(4, TWELL_DW)
   }
+#undef TWELL_DW
   return hipGetLastError();
 }
 

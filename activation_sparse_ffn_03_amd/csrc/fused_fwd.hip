@@ -162,15 +162,18 @@ __global__ __launch_bounds__(256) void ffn_up_kernel(FwdArgs a, int parts, int64
 
 // ------------------------------------------------------------------ down: y_i[slice] = sum z * W_down[c][slice]
 
-template <typename TS, int EPL>
+// Wave per (row i, d_model slice p); the slice is read 16 bytes per lane, so a
+// load instruction covers RPI rows of W_down (see pick_slices).
+template <typename TS, int EPL, int RPI>
 __global__ __launch_bounds__(256) void ffn_down_kernel(FwdArgs a, int P, int64_t i0, int64_t i1) {
-  constexpr int U = 8;  // rows in flight per wave
+  constexpr int LPR = 64 / RPI;
+  constexpr int U = RPI >= 8 ? 1 : 8 / RPI;  // load instructions in flight
   const int lane = threadIdx.x & 63;
   const int p = blockIdx.x % P;
   const int64_t i = i0 + (int64_t)(blockIdx.x / P) * 4 + (threadIdx.x >> 6);
   if (i >= i1 || a.ovf_flag[i]) return;
   const int D = a.D;
-  const int d0 = (p * 64 + lane) * EPL;
+  const int d0 = p * (LPR * EPL) + (lane % LPR) * EPL;
   const TS* __restrict__ w_down = reinterpret_cast<const TS*>(a.w_down) + d0;
   const uint2* __restrict__ zl = a.zlist + (size_t)i * a.n_tiles * a.slots;
   const int total = a.offs[(size_t)a.n_tiles * a.N + i];
@@ -180,26 +183,14 @@ __global__ __launch_bounds__(256) void ffn_down_kernel(FwdArgs a, int P, int64_t
   for (int kb = 0; kb < total; kb += 64) {
     const int n = min(64, total - kb);
     const uint2 ent = lane < n ? zl[kb + lane] : make_uint2(0u, 0u);
-    const int c_l = (int)ent.x;
-    const float z_l = __uint_as_float(ent.y);
-    for (int k = 0; k < n; k += U) {
-      Slice<TS, EPL> w[U];
-      float z[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int kk = min(k + u, n - 1);
-        const int c = readlane_i(c_l, kk);
-        const bool ok = (unsigned)c < (unsigned)a.F && k + u < n;
-        z[u] = ok ? readlane_f(z_l, kk) : 0.f;
-        w[u].load(w_down + (size_t)(ok ? c : 0) * D);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) w[u].fma(z[u], acc);
-    }
+    sliced_axpy<TS, EPL, RPI, U>(w_down, D, a.F, (int)ent.x, __uint_as_float(ent.y), n, lane, acc);
   }
-  float* dst = a.y + (size_t)i * D + d0;
+  combine_groups<EPL, RPI>(acc);
+  if (lane < LPR) {
+    float* dst = a.y + (size_t)i * D + d0;
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) dst[e] = acc[e];
+    for (int e = 0; e < EPL; ++e) dst[e] = acc[e];
+  }
 }
 
 // ------------------------------------------------------------------ overflow rows
@@ -298,10 +289,10 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t s, int64_t chunk) {
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
   // up: (column, z) list of the non-overflow rows; down: their y rows, d_model
-  // cut into P slices of 64*EPL elements
+  // cut into P slices (pick_slices)
   const int parts = a.n_tiles < kParts ? a.n_tiles : kParts;
-  int epl, P;
-  pick_slices(a.D, (int)sizeof(TS), &epl, &P);
+  const SliceGeom geom = pick_slices(a.D, (int)sizeof(TS));
+  const int P = geom.P;
   if (chunk <= 0) chunk = a.N;
   for (int64_t i0 = 0; i0 < a.N; i0 += chunk) {
     const int64_t i1 = i0 + chunk < a.N ? i0 + chunk : a.N;
@@ -317,19 +308,13 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t s, int64_t chunk) {
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;
     const dim3 gdn((unsigned)(tblocks * P));
-    switch (epl) {
-      case 1: TWELL_LAUNCH("ffn_down_kernel", (ffn_down_kernel<TS, 1>), gdn, blk, 0, s, a, P, i0, i1); break;
-      case 2: TWELL_LAUNCH("ffn_down_kernel", (ffn_down_kernel<TS, 2>), gdn, blk, 0, s, a, P, i0, i1); break;
-      case 4: TWELL_LAUNCH("ffn_down_kernel", (ffn_down_kernel<TS, 4>), gdn, blk, 0, s, a, P, i0, i1); break;
-      case 8: TWELL_LAUNCH("ffn_down_kernel", (ffn_down_kernel<TS, 8>), gdn, blk, 0, s, a, P, i0, i1); break;
-      case 16:
-        if constexpr (sizeof(TS) == 2) {
-          TWELL_LAUNCH("ffn_down_kernel", (ffn_down_kernel<TS, 16>), gdn, blk, 0, s, a, P, i0, i1);
-          break;
-        }
-        return hipErrorInvalidValue;
-      default: return hipErrorInvalidValue;
+#define TWELL_DOWN(E, R) TWELL_LAUNCH("ffn_down_kernel", (ffn_down_kernel<TS, E, R>), gdn, blk, 0, s, a, P, i0, i1)
+    if constexpr (sizeof(TS) == 2) {
+      TWELL_SLICED_CASES(8, TWELL_DOWN)
+    } else {
+      TWELL_SLICED_CASES(4, TWELL_DOWN)
     }
+#undef TWELL_DOWN
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
 

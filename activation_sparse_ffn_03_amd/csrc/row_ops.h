@@ -150,20 +150,92 @@ __device__ __forceinline__ float readlane_f(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
-// d_model slicing of the sliced kernels: P slices of 64*EPL elements, EPL the
-// largest power of two (<= 32 bytes per lane) that still gives >= 8 slices
-// (one per XCD); EPL = 1 when d_model < 512.
-inline void pick_slices(int D, int esz, int* epl_out, int* P_out) {
-  const int max_epl = esz == 2 ? 16 : 8;
-  int epl = 1;
-  for (int e = max_epl; e >= 1; e >>= 1)
-    if (D % (64 * e) == 0 && D / (64 * e) >= 8) {
-      epl = e;
+// d_model slicing of the sliced gather kernels. d_model is cut into P slices
+// (P = 8, one per XCD, whenever the slice length is then a power of two); a
+// row's slice is read by LPR lanes with EPL elements each, 16 bytes per lane
+// wherever the slice allows, so one wave load instruction covers RPI = 64/LPR
+// rows. Load instructions, not bytes, bound these gathers on MI355X: 16-byte
+// lanes move twice the data per instruction of 8-byte lanes.
+struct SliceGeom {
+  int P, EPL, RPI;
+};
+inline SliceGeom pick_slices(int D, int esz) {
+  const int e16 = 16 / esz;
+  int P = 0, slice = 0;
+  for (int p = 8; p >= 1; p >>= 1) {
+    const int sl = D / p;
+    if (D % p == 0 && (sl & (sl - 1)) == 0 && sl >= e16) {
+      P = p;
+      slice = sl;
       break;
     }
-  *epl_out = epl;
-  *P_out = D / (64 * epl);
+  }
+  if (P == 0) {  // d_model is not a power of two times <= 8: 64-element slices
+    P = D / 64;
+    slice = 64;
+  }
+  const int lpr = slice / e16 >= 64 ? 64 : slice / e16;
+  return {P, slice / lpr, 64 / lpr};
 }
+
+// acc += sum over the list entries k < n of z_k * row(c_k)[slice], where lane
+// k of (c_l, z_l) holds entry k and `base` already points at this lane's slice
+// elements. Lane group g = lane / (64/RPI) takes entries g, g+RPI, ...; U load
+// instructions (U*RPI rows) are in flight at a time. Entries whose column is
+// outside [0, F) contribute nothing.
+template <typename TS, int EPL, int RPI, int U>
+__device__ __forceinline__ void sliced_axpy(const TS* __restrict__ base, int D, int F, int c_l, float z_l, int n,
+                                            int lane, float (&acc)[EPL]) {
+  constexpr int LPR = 64 / RPI;
+  const int g = lane / LPR;
+  for (int k = 0; k < n; k += U * RPI) {
+    Slice<TS, EPL> w[U];
+    float z[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kk = k + u * RPI + g;
+      const int ks = kk < n ? kk : n - 1;
+      int c;
+      float zz;
+      if constexpr (RPI == 1) {  // ks is wave-uniform
+        c = __builtin_amdgcn_readlane(c_l, ks);
+        zz = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(z_l), ks));
+      } else {
+        c = __shfl(c_l, ks, 64);
+        zz = __shfl(z_l, ks, 64);
+      }
+      const bool ok = kk < n && (unsigned)c < (unsigned)F;
+      z[u] = ok ? zz : 0.f;
+      w[u].load(base + (size_t)(ok ? c : 0) * D);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) w[u].fma(z[u], acc);
+  }
+}
+
+// Add up the partial slices of the RPI lane groups (lanes l, l + 64/RPI, ...
+// hold the same slice elements); afterwards group 0 holds the total.
+template <int EPL, int RPI>
+__device__ __forceinline__ void combine_groups(float (&acc)[EPL]) {
+#pragma unroll
+  for (int off = 32; off >= 64 / RPI; off >>= 1)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] += __shfl_xor(acc[e], off, 64);
+}
+
+// Dispatch a sliced kernel template K<EPL, RPI> for the runtime geometry.
+#define TWELL_SLICED_CASES(E16, CALL)                                                       \
+  switch (geom.EPL == E16 ? geom.RPI : (geom.EPL == 2 * E16 ? 100 + geom.RPI : -1)) {      \
+    case 1: CALL(E16, 1); break;                                                            \
+    case 2: CALL(E16, 2); break;                                                            \
+    case 4: CALL(E16, 4); break;                                                            \
+    case 8: CALL(E16, 8); break;                                                            \
+    case 16: CALL(E16, 16); break;                                                          \
+    case 32: CALL(E16, 32); break;                                                          \
+    case 64: CALL(E16, 64); break;                                                          \
+    case 101: CALL(2 * E16, 1); break;                                                      \
+    default: return hipErrorInvalidValue;                                                   \
+  }
 
 // Dispatch helper: smallest M in {1,2,4,8,16} with M*64 chunks covering nch.
 inline int pick_m(int nch) {
