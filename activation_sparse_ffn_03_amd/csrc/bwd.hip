@@ -257,61 +257,40 @@ __device__ __forceinline__ float entry_f(float v, int k) {
 
 // Every row (ELL and dense-backup alike): its records are contiguous in CSR
 // order. Part p owns a d_model slice of dx (pick_slices), so each XCD gathers
-// only that slice of the W_up / W_gate rows, 16 bytes per lane:
-//   dx_i[slice] = sum over records (da * W_up^T[c][slice] + dg * W_gate^T[c][slice])
+// only that slice, 16 bytes per lane. Two passes, one weight each, so that an
+// XCD's working set is a single 1/8 slice:
+//   GATE = false:  dx_i[slice]  = sum over records da * W_up^T[c][slice]
+//   GATE = true:   dx_i[slice] += sum over records dg * W_gate^T[c][slice]
 // Dense rows beyond the dense capacity have no records and get dx = 0.
-template <typename TS, int EPL, int RPI>
+template <typename TS, int EPL, int RPI, bool GATE>
 __global__ __launch_bounds__(256) void bwd_dx(BwdArgs a, int P) {
   constexpr int LPR = 64 / RPI;
   constexpr int U = RPI >= 8 ? 1 : 8 / RPI;
-  const int lane = threadIdx.x & 63, g = lane / LPR;
+  const int lane = threadIdx.x & 63;
   const int p = blockIdx.x % P;
   const int64_t i = (int64_t)(blockIdx.x / P) * 4 + (threadIdx.x >> 6);
   if (i >= a.N) return;
   const int D = a.D;
   const int d0 = p * (LPR * EPL) + (lane % LPR) * EPL;
-  const TS* __restrict__ wu = reinterpret_cast<const TS*>(a.w_up) + d0;
-  const TS* __restrict__ wg = reinterpret_cast<const TS*>(a.w_gate) + d0;
+  const TS* __restrict__ wt = reinterpret_cast<const TS*>(GATE ? a.w_gate : a.w_up) + d0;
   const int32_t q0 = a.ws.row_ptr[i], q1 = a.ws.row_ptr[i + 1];
+  float* dst = a.dx + (size_t)i * D + d0;
   float acc[EPL];
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  for (int e = 0; e < EPL; ++e) acc[e] = (GATE && lane < LPR) ? dst[e] : 0.f;
   for (int qb = q0; qb < q1; qb += 64) {
     const int n = min(64, q1 - qb);
     int c_l = 0;
-    float da_l = 0.f, dg_l = 0.f;
+    float k_l = 0.f;
     if (lane < n) {
       c_l = a.ws.pair_col[qb + lane];
       const float4 cf = a.ws.coef[qb + lane];
-      da_l = cf.y;
-      dg_l = cf.z;
+      k_l = GATE ? cf.z : cf.y;
     }
-    for (int k = 0; k < n; k += U * RPI) {
-      Slice<TS, EPL> su[U], sg[U];
-      float da[U], dg[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int kk = k + u * RPI + g;
-        const int ks = min(kk, n - 1);
-        const int c = entry_i<RPI>(c_l, ks);
-        const bool ok = kk < n && (unsigned)c < (unsigned)a.F;
-        const float da_v = entry_f<RPI>(da_l, ks), dg_v = entry_f<RPI>(dg_l, ks);
-        da[u] = ok ? da_v : 0.f;
-        dg[u] = ok ? dg_v : 0.f;
-        const size_t row = (size_t)(ok ? c : 0) * D;
-        su[u].load(wu + row);
-        sg[u].load(wg + row);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        su[u].fma(da[u], acc);
-        sg[u].fma(dg[u], acc);
-      }
-    }
+    sliced_axpy<TS, EPL, RPI, U>(wt, D, a.F, c_l, k_l, n, lane, acc);
   }
   combine_groups<EPL, RPI>(acc);
   if (lane < LPR) {
-    float* dst = a.dx + (size_t)i * D + d0;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) dst[e] = acc[e];
   }
@@ -407,10 +386,12 @@ __global__ __launch_bounds__(64) void csc_fill(const int32_t* __restrict__ row_p
 // --------------------------------------------------------------- weight gradients
 
 // Wave per (column c, d_model slice p): the column's records in ascending row
-// order (from the column transpose), token-row slices read 16 bytes per lane:
-//   dW_down[c][slice] += z * dy_i[slice], dW_up^T[c][slice] += da * x_i[slice],
-//   dW_gate^T[c][slice] += dg * x_i[slice].
-template <typename TS, int EPL, int RPI>
+// order (from the column transpose), token-row slices read 16 bytes per lane.
+// Two passes, one token matrix each (an XCD's working set is one 1/8 slice):
+//   X = false:  dW_down[c][slice]   = sum z  * dy_i[slice]
+//   X = true:   dW_up^T[c][slice]   = sum da * x_i[slice],
+//               dW_gate^T[c][slice] = sum dg * x_i[slice].
+template <typename TS, int EPL, int RPI, bool X>
 __global__ __launch_bounds__(256) void bwd_dw(BwdArgs a, int P) {
   constexpr int LPR = 64 / RPI;
   constexpr int U = RPI >= 8 ? 1 : 8 / RPI;
@@ -420,11 +401,10 @@ __global__ __launch_bounds__(256) void bwd_dw(BwdArgs a, int P) {
   if (c >= a.F) return;
   const int D = a.D;
   const int d0 = p * (LPR * EPL) + (lane % LPR) * EPL;
-  const TS* __restrict__ x = reinterpret_cast<const TS*>(a.x) + d0;
-  const TS* __restrict__ dy = reinterpret_cast<const TS*>(a.dy) + d0;
-  float accD[EPL], accU[EPL], accG[EPL];
+  const TS* __restrict__ src = reinterpret_cast<const TS*>(X ? a.x : a.dy) + d0;
+  float acc0[EPL], acc1[EPL];
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) accD[e] = accU[e] = accG[e] = 0.f;
+  for (int e = 0; e < EPL; ++e) acc0[e] = acc1[e] = 0.f;
   const int32_t q0 = a.ws.col_ptr[c], q1 = a.ws.col_ptr[c + 1];
   for (int qb = q0; qb < q1; qb += 64) {
     const int n = min(64, q1 - qb);
@@ -434,40 +414,43 @@ __global__ __launch_bounds__(256) void bwd_dw(BwdArgs a, int P) {
       i_l = a.ws.csc_row[qb + lane];
       cf = a.ws.coef[a.ws.csc_pair[qb + lane]];
     }
+    const float k0_l = X ? cf.y : cf.x;
     for (int k = 0; k < n; k += U * RPI) {
-      Slice<TS, EPL> sd[U], sx[U];
-      float z[U], da[U], dg[U];
+      Slice<TS, EPL> sr[U];
+      float k0[U], k1[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int kk = k + u * RPI + g;
         const int ks = min(kk, n - 1);
         const bool ok = kk < n;
         const size_t row = (size_t)entry_i<RPI>(i_l, ks) * D;
-        const float zv = entry_f<RPI>(cf.x, ks), dav = entry_f<RPI>(cf.y, ks), dgv = entry_f<RPI>(cf.z, ks);
-        z[u] = ok ? zv : 0.f;
-        da[u] = ok ? dav : 0.f;
-        dg[u] = ok ? dgv : 0.f;
-        sd[u].load(dy + row);
-        sx[u].load(x + row);
+        const float v0 = entry_f<RPI>(k0_l, ks);
+        k0[u] = ok ? v0 : 0.f;
+        if (X) {
+          const float v1 = entry_f<RPI>(cf.z, ks);
+          k1[u] = ok ? v1 : 0.f;
+        }
+        sr[u].load(src + row);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        sd[u].fma(z[u], accD);
-        sx[u].fma(da[u], accU);
-        sx[u].fma(dg[u], accG);
+        sr[u].fma(k0[u], acc0);
+        if (X) sr[u].fma(k1[u], acc1);
       }
     }
   }
-  combine_groups<EPL, RPI>(accD);
-  combine_groups<EPL, RPI>(accU);
-  combine_groups<EPL, RPI>(accG);
+  combine_groups<EPL, RPI>(acc0);
+  if (X) combine_groups<EPL, RPI>(acc1);
   if (lane < LPR) {
     const size_t ro = (size_t)c * D + d0;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
-      a.dw_down[ro + e] = accD[e];
-      a.dw_up[ro + e] = accU[e];
-      a.dw_gate[ro + e] = accG[e];
+      if (X) {
+        a.dw_up[ro + e] = acc0[e];
+        a.dw_gate[ro + e] = acc1[e];
+      } else {
+        a.dw_down[ro + e] = acc0[e];
+      }
     }
   }
 }
@@ -517,13 +500,17 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t s) {
   const SliceGeom geom = pick_slices(a.D, (int)sizeof(TS));
   const int P = geom.P;
   const dim3 gdx((unsigned)(((a.N + 3) / 4) * P));
-#define TWELL_DX(E, R) TWELL_LAUNCH("bwd_dx", (bwd_dx<TS, E, R>), gdx, blk, 0, s, a, P)
+#define TWELL_DX(E, R) TWELL_LAUNCH("bwd_dx", (bwd_dx<TS, E, R, false>), gdx, blk, 0, s, a, P)
+#define TWELL_DXG(E, R) TWELL_LAUNCH("bwd_dx_gate", (bwd_dx<TS, E, R, true>), gdx, blk, 0, s, a, P)
   if constexpr (sizeof(TS) == 2) {
     TWELL_SLICED_CASES(8, TWELL_DX)
+    TWELL_SLICED_CASES(8, TWELL_DXG)
   } else {
     TWELL_SLICED_CASES(4, TWELL_DX)
+    TWELL_SLICED_CASES(4, TWELL_DXG)
   }
 #undef TWELL_DX
+#undef TWELL_DXG
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
   // column transpose of the records (stable: rows ascend within a column)
@@ -538,12 +525,16 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t s) {
 
   // weight gradients: column-owned, d_model sliced
   const dim3 gdw((unsigned)(((a.F + 3) / 4) * (int64_t)P));
-#define TWELL_DW(E, R) TWELL_LAUNCH("bwd_dw", (bwd_dw<TS, E, R>), gdw, blk, 0, s, a, P)
+#define TWELL_DWD(E, R) TWELL_LAUNCH("bwd_dw_down", (bwd_dw<TS, E, R, false>), gdw, blk, 0, s, a, P)
+#define TWELL_DW(E, R) TWELL_LAUNCH("bwd_dw", (bwd_dw<TS, E, R, true>), gdw, blk, 0, s, a, P)
   if constexpr (sizeof(TS) == 2) {
+    TWELL_SLICED_CASES(8, TWELL_DWD)
     TWELL_SLICED_CASES(8, TWELL_DW)
   } else {
+    TWELL_SLICED_CASES(4, TWELL_DWD)
     TWELL_SLICED_CASES(4, TWELL_DW)
   }
+#undef TWELL_DWD
 #undef TWELL_DW
   return hipGetLastError();
 }

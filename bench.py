@@ -84,12 +84,18 @@ def kernel_work(name, w, st, train):
     if name == "bwd_dz_ell":   # dy, W_down once; row-ELL read; (col, z, da, dg) records written
         byt = N * D * e + F * D * e + nnz_ell * (e + 8) + nnz_ell * 20
         return {"flops": 2.0 * D * nnz_ell, "bytes": byt, "bound": "hbm"}
-    if name == "bwd_dx":       # W_up, W_gate once; records read; dx written (fp32)
-        byt = 2 * F * D * e + nnz * 12 + N * D * 4
+    if name == "bwd_dx":       # W_up once; records read; dx written (fp32)
+        byt = F * D * e + nnz * 8 + N * D * 4
+        return {"flops": 2.0 * D * nnz, "bytes": byt, "bound": "hbm"}
+    if name == "bwd_dx_gate":  # W_gate once; records read; dx read and written (fp32)
+        byt = F * D * e + nnz * 8 + 2 * N * D * 4
+        return {"flops": 2.0 * D * nnz, "bytes": byt, "bound": "hbm"}
+    if name == "bwd_dw_down":  # dy once; records via the column transpose; dW_down written (fp32)
+        byt = N * D * e + nnz * 12 + F * D * 4
+        return {"flops": 2.0 * D * nnz, "bytes": byt, "bound": "hbm"}
+    if name == "bwd_dw":       # x once; records via the column transpose; dW_up, dW_gate written (fp32)
+        byt = N * D * e + nnz * 16 + 2 * F * D * 4
         return {"flops": 4.0 * D * nnz, "bytes": byt, "bound": "hbm"}
-    if name == "bwd_dw":       # x, dy once; records read via the column transpose; 3 dW written (fp32)
-        byt = 2 * N * D * e + nnz * 24 + 3 * F * D * 4
-        return {"flops": 6.0 * D * nnz, "bytes": byt, "bound": "hbm"}
     return None
 
 
@@ -136,6 +142,8 @@ KERNEL_SOURCES = {
     "ffn_down_kernel": ["fused_fwd.hip", "row_ops.h", "twell_device.h"],
     "bwd_dz_ell": ["bwd.hip", "row_ops.h", "twell_device.h"],
     "bwd_dx": ["bwd.hip", "row_ops.h", "twell_device.h"],
+    "bwd_dx_gate": ["bwd.hip", "row_ops.h", "twell_device.h"],
+    "bwd_dw_down": ["bwd.hip", "row_ops.h", "twell_device.h"],
     "bwd_dw": ["bwd.hip", "row_ops.h", "twell_device.h"],
 }
 
