@@ -113,7 +113,7 @@ __device__ __forceinline__ void collect_pairs(const FwdArgs& a, int64_t i, int j
 template <typename TS, int M>
 __global__ __launch_bounds__(256) void ffn_up_kernel(FwdArgs a, int parts, int64_t i0, int64_t i1) {
   constexpr int E = ChunkElems<TS>::E;
-  constexpr int U = M <= 4 ? 4 : (M == 8 ? 2 : 1);  // rows in flight per wave
+  constexpr int U = M <= 4 ? 2 : 1;  // rows in flight per wave (more costs occupancy: measured slower)
   const int lane = threadIdx.x & 63;
   const int part = blockIdx.x % parts;
   const int64_t i = i0 + (int64_t)(blockIdx.x / parts) * 4 + (threadIdx.x >> 6);
@@ -163,14 +163,19 @@ __global__ __launch_bounds__(256) void ffn_up_kernel(FwdArgs a, int parts, int64
 // ------------------------------------------------------------------ down: y_i[slice] = sum z * W_down[c][slice]
 
 // Wave per (row i, d_model slice p); the slice is read 16 bytes per lane, so a
-// load instruction covers RPI rows of W_down (see pick_slices).
+// load instruction covers RPI rows of W_down (see pick_l2_slices). Slices go
+// G8 (8, one per XCD, when P is a multiple of 8, else all P) at a time:
+// workgroup b works on slice
+// pass * G8 + b % G8, passes in grid order, so an XCD holds one slice of
+// W_down at a time.
 template <typename TS, int EPL, int RPI>
-__global__ __launch_bounds__(256) void ffn_down_kernel(FwdArgs a, int P, int64_t i0, int64_t i1) {
+__global__ __launch_bounds__(256) void ffn_down_kernel(FwdArgs a, int G8, int64_t tblocks, int64_t i0, int64_t i1) {
   constexpr int LPR = 64 / RPI;
   constexpr int U = RPI >= 8 ? 1 : 8 / RPI;  // load instructions in flight
   const int lane = threadIdx.x & 63;
-  const int p = blockIdx.x % P;
-  const int64_t i = i0 + (int64_t)(blockIdx.x / P) * 4 + (threadIdx.x >> 6);
+  const int64_t r = blockIdx.x / G8;
+  const int p = (int)(r / tblocks) * G8 + blockIdx.x % G8;
+  const int64_t i = i0 + (r % tblocks) * 4 + (threadIdx.x >> 6);
   if (i >= i1 || a.ovf_flag[i]) return;
   const int D = a.D;
   const int d0 = p * (LPR * EPL) + (lane % LPR) * EPL;
@@ -291,8 +296,9 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t s, int64_t chunk) {
   // up: (column, z) list of the non-overflow rows; down: their y rows, d_model
   // cut into P slices (pick_slices)
   const int parts = a.n_tiles < kParts ? a.n_tiles : kParts;
-  const SliceGeom geom = pick_slices(a.D, (int)sizeof(TS));
-  const int P = geom.P;
+  const SliceGeom geom = pick_l2_slices(a.D, (int)sizeof(TS), a.F);
+  // Passes of kParts slices when P divides into them, else one pass of P.
+  const int P = geom.P, G8 = P % kParts == 0 ? kParts : P;
   if (chunk <= 0) chunk = a.N;
   for (int64_t i0 = 0; i0 < a.N; i0 += chunk) {
     const int64_t i1 = i0 + chunk < a.N ? i0 + chunk : a.N;
@@ -308,7 +314,8 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t s, int64_t chunk) {
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;
     const dim3 gdn((unsigned)(tblocks * P));
-#define TWELL_DOWN(E, R) TWELL_LAUNCH("ffn_down_kernel", (ffn_down_kernel<TS, E, R>), gdn, blk, 0, s, a, P, i0, i1)
+#define TWELL_DOWN(E, R) \
+  TWELL_LAUNCH("ffn_down_kernel", (ffn_down_kernel<TS, E, R>), gdn, blk, 0, s, a, G8, tblocks, i0, i1)
     if constexpr (sizeof(TS) == 2) {
       TWELL_SLICED_CASES(8, TWELL_DOWN)
     } else {

@@ -178,6 +178,21 @@ inline SliceGeom pick_slices(int D, int esz) {
   return {P, slice / lpr, 64 / lpr};
 }
 
+// Slicing for a pass that gathers slices of the rows of one [rows x D] matrix:
+// the slice is the widest power of two (down to 64 elements, and never wider
+// than pick_slices gives) whose column of the matrix, rows x slice, fits about
+// 3 MB of an XCD's 4 MB L2. geom.P is then the total number of slices; they
+// are processed 8 at a time (one per XCD), in P/8 successive passes.
+inline SliceGeom pick_l2_slices(int D, int esz, int64_t rows) {
+  SliceGeom g = pick_slices(D, esz);
+  const int e16 = 16 / esz;
+  int slice = D / g.P;
+  const int64_t budget = 3ll << 20;
+  while (slice > 64 && slice % 2 == 0 && (int64_t)slice / 2 >= e16 && rows * slice * esz > budget) slice /= 2;
+  const int lpr = slice / e16 >= 64 ? 64 : slice / e16;
+  return {D / slice, slice / lpr, 64 / lpr};
+}
+
 // acc += sum over the list entries k < n of z_k * row(c_k)[slice], where lane
 // k of (c_l, z_l) holds entry k and `base` already points at this lane's slice
 // elements. Lane group g = lane / (64/RPI) takes entries g, g+RPI, ...; U load
