@@ -256,19 +256,21 @@ __device__ __forceinline__ float entry_f(float v, int k) {
 }
 
 // Every row (ELL and dense-backup alike): its records are contiguous in CSR
-// order. Part p owns a d_model slice of dx (pick_slices), so each XCD gathers
-// only that slice, 16 bytes per lane. Two passes, one weight each, so that an
-// XCD's working set is a single 1/8 slice:
+// order. Part p owns a d_model slice of dx (pick_l2_slices; slices go G8 at a
+// time, slice_block), so each XCD gathers only a slice of the weight that
+// fits its L2, 16 bytes per lane. Two launches, one weight each:
 //   GATE = false:  dx_i[slice]  = sum over records da * W_up^T[c][slice]
 //   GATE = true:   dx_i[slice] += sum over records dg * W_gate^T[c][slice]
 // Dense rows beyond the dense capacity have no records and get dx = 0.
 template <typename TS, int EPL, int RPI, bool GATE>
-__global__ __launch_bounds__(256) void bwd_dx(BwdArgs a, int P) {
+__global__ __launch_bounds__(256) void bwd_dx(BwdArgs a, int G8, int64_t rblocks) {
   constexpr int LPR = 64 / RPI;
-  constexpr int U = RPI >= 8 ? 1 : 8 / RPI;
+  constexpr int U = sliced_inflight<RPI>();
   const int lane = threadIdx.x & 63;
-  const int p = blockIdx.x % P;
-  const int64_t i = (int64_t)(blockIdx.x / P) * 4 + (threadIdx.x >> 6);
+  int p;
+  int64_t rb;
+  slice_block(blockIdx.x, G8, rblocks, p, rb);
+  const int64_t i = rb * 4 + (threadIdx.x >> 6);
   if (i >= a.N) return;
   const int D = a.D;
   const int d0 = p * (LPR * EPL) + (lane % LPR) * EPL;
@@ -386,18 +388,20 @@ __global__ __launch_bounds__(64) void csc_fill(const int32_t* __restrict__ row_p
 // --------------------------------------------------------------- weight gradients
 
 // Wave per (column c, d_model slice p): the column's records in ascending row
-// order (from the column transpose), token-row slices read 16 bytes per lane.
-// Two passes, one token matrix each (an XCD's working set is one 1/8 slice):
+// order (from the column transpose), token-row slices read 16 bytes per lane,
+// one slice per XCD (slice_block). Two launches, one token matrix each:
 //   X = false:  dW_down[c][slice]   = sum z  * dy_i[slice]
 //   X = true:   dW_up^T[c][slice]   = sum da * x_i[slice],
 //               dW_gate^T[c][slice] = sum dg * x_i[slice].
 template <typename TS, int EPL, int RPI, bool X>
-__global__ __launch_bounds__(256) void bwd_dw(BwdArgs a, int P) {
+__global__ __launch_bounds__(256) void bwd_dw(BwdArgs a, int G8, int64_t cblocks) {
   constexpr int LPR = 64 / RPI;
-  constexpr int U = RPI >= 8 ? 1 : 8 / RPI;
+  constexpr int U = sliced_inflight<RPI>();
   const int lane = threadIdx.x & 63, g = lane / LPR;
-  const int p = blockIdx.x % P;
-  const int64_t c = (int64_t)(blockIdx.x / P) * 4 + (threadIdx.x >> 6);
+  int p;
+  int64_t cb;
+  slice_block(blockIdx.x, G8, cblocks, p, cb);
+  const int64_t c = cb * 4 + (threadIdx.x >> 6);
   if (c >= a.F) return;
   const int D = a.D;
   const int d0 = p * (LPR * EPL) + (lane % LPR) * EPL;
@@ -496,12 +500,14 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t s) {
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
 
-  // dx: every row, d_model sliced
-  const SliceGeom geom = pick_slices(a.D, (int)sizeof(TS));
-  const int P = geom.P;
-  const dim3 gdx((unsigned)(((a.N + 3) / 4) * P));
-#define TWELL_DX(E, R) TWELL_LAUNCH("bwd_dx", (bwd_dx<TS, E, R, false>), gdx, blk, 0, s, a, P)
-#define TWELL_DXG(E, R) TWELL_LAUNCH("bwd_dx_gate", (bwd_dx<TS, E, R, true>), gdx, blk, 0, s, a, P)
+  // dx: every row, d_model sliced to fit a slice of W_up (F rows) in L2
+  {
+  const SliceGeom geom = pick_l2_slices(a.D, (int)sizeof(TS), a.F);
+  const int P = geom.P, G8 = slice_group(P);
+  const int64_t rblocks = (a.N + 3) / 4;
+  const dim3 gdx((unsigned)(rblocks * P));
+#define TWELL_DX(E, R) TWELL_LAUNCH("bwd_dx", (bwd_dx<TS, E, R, false>), gdx, blk, 0, s, a, G8, rblocks)
+#define TWELL_DXG(E, R) TWELL_LAUNCH("bwd_dx_gate", (bwd_dx<TS, E, R, true>), gdx, blk, 0, s, a, G8, rblocks)
   if constexpr (sizeof(TS) == 2) {
     TWELL_SLICED_CASES(8, TWELL_DX)
     TWELL_SLICED_CASES(8, TWELL_DXG)
@@ -511,6 +517,7 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t s) {
   }
 #undef TWELL_DX
 #undef TWELL_DXG
+  }
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
   // column transpose of the records (stable: rows ascend within a column)
@@ -523,10 +530,15 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t s) {
                a.ws.csc_pair, a.ws.csc_row);
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
-  // weight gradients: column-owned, d_model sliced
-  const dim3 gdw((unsigned)(((a.F + 3) / 4) * (int64_t)P));
-#define TWELL_DWD(E, R) TWELL_LAUNCH("bwd_dw_down", (bwd_dw<TS, E, R, false>), gdw, blk, 0, s, a, P)
-#define TWELL_DW(E, R) TWELL_LAUNCH("bwd_dw", (bwd_dw<TS, E, R, true>), gdw, blk, 0, s, a, P)
+  // weight gradients: column-owned, d_model in 1/8 slices (slicing x / dy
+  // further to fit L2 measured slower here: a column's tokens ascend, so its
+  // gathers already fall close together)
+  const SliceGeom geom = pick_slices(a.D, (int)sizeof(TS));
+  const int P = geom.P, G8 = slice_group(P);
+  const int64_t cblocks = (a.F + 3) / 4;
+  const dim3 gdw((unsigned)(cblocks * P));
+#define TWELL_DWD(E, R) TWELL_LAUNCH("bwd_dw_down", (bwd_dw<TS, E, R, false>), gdw, blk, 0, s, a, G8, cblocks)
+#define TWELL_DW(E, R) TWELL_LAUNCH("bwd_dw", (bwd_dw<TS, E, R, true>), gdw, blk, 0, s, a, G8, cblocks)
   if constexpr (sizeof(TS) == 2) {
     TWELL_SLICED_CASES(8, TWELL_DWD)
     TWELL_SLICED_CASES(8, TWELL_DW)

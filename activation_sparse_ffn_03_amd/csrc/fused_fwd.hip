@@ -17,8 +17,11 @@
 //                    One wave per token: x_i in registers, the token's packed
 //                    entries in those tiles collected into a register list,
 //                    W_up rows gathered a few at a time, a = x_i . W_up^T[c]
-//                    reduced with DPP, z = h * a stored at the entry's slot
-//                    (the sparse z, nnz x 4 B; never a dense hidden state).
+//                    reduced with DPP, z = h * a stored in the token's
+//                    (column, z) list (the sparse z, never a dense hidden
+//                    state). When a 1/8 block of W_up exceeds the L2, d_model
+//                    is taken in up_nq ranges, one after another in grid
+//                    order, and ffn_up_finish adds their partial a.
 //   ffn_down_kernel  part p = b % P owns the d_model slice of y
 //                    [p*D/P, (p+1)*D/P). One wave per token: its (c, z) list,
 //                    the slice of each W_down row, y slice in registers.
@@ -35,22 +38,6 @@ namespace twell {
 namespace {
 
 constexpr int kParts = 8;  // one part per XCD
-
-// Per-row tile offsets: offs[j][i] = number of packed entries of row i in
-// tiles before j (offs[n_t][i] = the row's total), i.e. where tile j's entries
-// start in the row's (column, z) list.
-__global__ __launch_bounds__(64) void ffn_row_offsets(FwdArgs a) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= a.N) return;
-  const int64_t N = a.N;
-  int32_t run = 0;
-#pragma unroll 8
-  for (int j = 0; j < a.n_tiles; ++j) {
-    a.offs[(size_t)j * N + i] = run;
-    run += min((int)a.counts[(size_t)j * N + i], a.slots);
-  }
-  a.offs[(size_t)a.n_tiles * N + i] = run;
-}
 
 // Walk TwELL tiles [j0, j1) of token i (not an overflow row) and hand its
 // packed entries to `flush` in lists of at most 64: lane k of the list holds
@@ -110,25 +97,46 @@ __device__ __forceinline__ void collect_pairs(const FwdArgs& a, int64_t i, int j
 
 // ------------------------------------------------------------------ up: z = h * (x_i . W_up^T[c])
 
+// Entries of token i in tiles [0, j0): where tile j0's entries start in the
+// token's (column, z) list. Counts are small integers, so the float wave sum
+// is exact.
+__device__ __forceinline__ int entries_before(const FwdArgs& a, int64_t i, int j0, int lane) {
+  int before = 0;
+  for (int jb = 0; jb < j0; jb += 64) {
+    const int jl = jb + lane;
+    const int c = jl < j0 ? min((int)a.counts[(size_t)jl * a.N + i], a.slots) : 0;
+    before += (int)wave_sum_dpp((float)c);
+  }
+  return before;
+}
+
+// Workgroup b: part p = b % parts (the XCD's TwELL tiles), d_model range
+// q = (b / parts) / tblocks (ranges in grid order, one W_up block per XCD in
+// L2 at a time), four tokens of the block row. With one range the wave stores
+// (c, z = h*a) and a_save itself; with several it stores its partial a, range
+// 0 also (c, h) and the entry's slot, and ffn_up_finish adds the ranges.
 template <typename TS, int M>
-__global__ __launch_bounds__(256) void ffn_up_kernel(FwdArgs a, int parts, int64_t i0, int64_t i1) {
+__global__ __launch_bounds__(256) void ffn_up_kernel(FwdArgs a, int parts, int64_t tblocks, int64_t i0, int64_t i1) {
   constexpr int E = ChunkElems<TS>::E;
   constexpr int U = M <= 4 ? 2 : 1;  // rows in flight per wave (more costs occupancy: measured slower)
   const int lane = threadIdx.x & 63;
   const int part = blockIdx.x % parts;
-  const int64_t i = i0 + (int64_t)(blockIdx.x / parts) * 4 + (threadIdx.x >> 6);
+  const int64_t r = blockIdx.x / parts;
+  const int q = (int)(r / tblocks);
+  const int64_t i = i0 + (r % tblocks) * 4 + (threadIdx.x >> 6);
   if (i >= i1 || a.ovf_flag[i]) return;
   const int j0 = (int)((int64_t)part * a.n_tiles / parts), j1 = (int)((int64_t)(part + 1) * a.n_tiles / parts);
-  const int D = a.D, nch = D / E;
+  const int D = a.D, Dq = D / a.up_nq, nch = Dq / E;
   const size_t L = (size_t)a.n_tiles * a.slots;
-  const TS* __restrict__ w_up = reinterpret_cast<const TS*>(a.w_up);
+  const TS* __restrict__ w_up = reinterpret_cast<const TS*>(a.w_up) + (size_t)q * Dq;
   uint2* __restrict__ zl = a.zlist + (size_t)i * L;
-  int lbase = a.offs[(size_t)j0 * a.N + i];  // list position of this part's first entry
+  float* __restrict__ up = a.upart + ((size_t)q * a.N + i) * L;
+  int lbase = entries_before(a, i, j0, lane);  // list position of this part's first entry
   u32x4_t xr[M];
   bool have_x = false;
   auto flush = [&](int c_l, float h_l, int slot_l, int n) {
     if (!have_x) {
-      load_row<TS, M>(xr, reinterpret_cast<const TS*>(a.x) + (size_t)i * D, nch, lane);
+      load_row<TS, M>(xr, reinterpret_cast<const TS*>(a.x) + (size_t)i * D + (size_t)q * Dq, nch, lane);
       have_x = true;
     }
     float a_l = 0.f;
@@ -150,38 +158,66 @@ __global__ __launch_bounds__(256) void ffn_up_kernel(FwdArgs a, int parts, int64
       for (int u = 0; u < U; ++u)
         if (lane == k + u) a_l = ok[u] ? dot[u] : 0.f;
     }
-    // lane k holds entry k: one coalesced store of the (column, z) pairs
+    // lane k holds entry k: one coalesced store per list
     if (lane < n) {
-      zl[lbase + lane] = make_uint2((uint32_t)c_l, __float_as_uint(h_l * a_l));
-      if (a.a_save) a.a_save[(size_t)slot_l * a.N + i] = a_l;
+      if (a.up_nq == 1) {
+        zl[lbase + lane] = make_uint2((uint32_t)c_l, __float_as_uint(h_l * a_l));
+        if (a.a_save) a.a_save[(size_t)slot_l * a.N + i] = a_l;
+      } else {
+        up[lbase + lane] = a_l;
+        if (q == 0) {
+          zl[lbase + lane] = make_uint2((uint32_t)c_l, __float_as_uint(h_l));
+          if (a.a_save) a.uslot[(size_t)i * L + lbase + lane] = slot_l;
+        }
+      }
     }
     lbase += n;
   };
   collect_pairs<TS>(a, i, j0, j1, lane, flush);
+  if (j1 == a.n_tiles && q == 0 && lane == 0) a.offs[i] = lbase;  // the row's total
+}
+
+// a = sum of the up passes' partials in range order; z = h * a into the
+// (column, h) list written by range 0, a into a_save at the entry's slot.
+// Wave per token, 64 entries per step: a plain streaming pass.
+__global__ __launch_bounds__(256) void ffn_up_finish(FwdArgs a, int64_t i0, int64_t i1) {
+  const int lane = threadIdx.x & 63;
+  const int64_t i = i0 + (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (i >= i1 || a.ovf_flag[i]) return;
+  const size_t L = (size_t)a.n_tiles * a.slots;
+  const size_t qstride = (size_t)a.N * L;
+  uint2* __restrict__ zl = a.zlist + (size_t)i * L;
+  const float* __restrict__ up = a.upart + (size_t)i * L;
+  const int total = a.offs[i];
+  for (int k = lane; k < total; k += 64) {
+    float sum = 0.f;
+    for (int q = 0; q < a.up_nq; ++q) sum += up[q * qstride + k];
+    const uint2 e = zl[k];
+    zl[k] = make_uint2(e.x, __float_as_uint(__uint_as_float(e.y) * sum));
+    if (a.a_save) a.a_save[(size_t)a.uslot[(size_t)i * L + k] * a.N + i] = sum;
+  }
 }
 
 // ------------------------------------------------------------------ down: y_i[slice] = sum z * W_down[c][slice]
 
 // Wave per (row i, d_model slice p); the slice is read 16 bytes per lane, so a
 // load instruction covers RPI rows of W_down (see pick_l2_slices). Slices go
-// G8 (8, one per XCD, when P is a multiple of 8, else all P) at a time:
-// workgroup b works on slice
-// pass * G8 + b % G8, passes in grid order, so an XCD holds one slice of
-// W_down at a time.
+// G8 at a time (slice_block), so an XCD holds one slice of W_down at a time.
 template <typename TS, int EPL, int RPI>
 __global__ __launch_bounds__(256) void ffn_down_kernel(FwdArgs a, int G8, int64_t tblocks, int64_t i0, int64_t i1) {
   constexpr int LPR = 64 / RPI;
-  constexpr int U = RPI >= 8 ? 1 : 8 / RPI;  // load instructions in flight
+  constexpr int U = sliced_inflight<RPI>();
   const int lane = threadIdx.x & 63;
-  const int64_t r = blockIdx.x / G8;
-  const int p = (int)(r / tblocks) * G8 + blockIdx.x % G8;
-  const int64_t i = i0 + (r % tblocks) * 4 + (threadIdx.x >> 6);
+  int p;
+  int64_t rb;
+  slice_block(blockIdx.x, G8, tblocks, p, rb);
+  const int64_t i = i0 + rb * 4 + (threadIdx.x >> 6);
   if (i >= i1 || a.ovf_flag[i]) return;
   const int D = a.D;
   const int d0 = p * (LPR * EPL) + (lane % LPR) * EPL;
   const TS* __restrict__ w_down = reinterpret_cast<const TS*>(a.w_down) + d0;
   const uint2* __restrict__ zl = a.zlist + (size_t)i * a.n_tiles * a.slots;
-  const int total = a.offs[(size_t)a.n_tiles * a.N + i];
+  const int total = a.offs[i];
   float acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
@@ -287,32 +323,34 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t s, int64_t chunk) {
   constexpr int E = ChunkElems<TS>::E;
   const int nch = a.D / E;
   const int M = pick_m(nch);
+  if (a.up_nq < 1 || a.D % (a.up_nq * E) != 0) return hipErrorInvalidValue;
+  const int Mq = pick_m(nch / a.up_nq);  // chunks per lane of one d_model range
   const dim3 blk(256);
   hipError_t err;
 
-  TWELL_LAUNCH("ffn_row_offsets", ffn_row_offsets, dim3((unsigned)((a.N + 63) / 64)), dim3(64), 0, s, a);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-
-  // up: (column, z) list of the non-overflow rows; down: their y rows, d_model
-  // cut into P slices (pick_slices)
+  // up: (column, z) list of the non-overflow rows, in up_nq d_model ranges;
+  // down: their y rows, d_model cut into P slices (pick_l2_slices)
   const int parts = a.n_tiles < kParts ? a.n_tiles : kParts;
   const SliceGeom geom = pick_l2_slices(a.D, (int)sizeof(TS), a.F);
-  // Passes of kParts slices when P divides into them, else one pass of P.
-  const int P = geom.P, G8 = P % kParts == 0 ? kParts : P;
+  const int P = geom.P, G8 = slice_group(P);
   if (chunk <= 0) chunk = a.N;
   for (int64_t i0 = 0; i0 < a.N; i0 += chunk) {
     const int64_t i1 = i0 + chunk < a.N ? i0 + chunk : a.N;
     const int64_t tblocks = (i1 - i0 + 3) / 4;
-    const dim3 gup((unsigned)(tblocks * parts));
-    switch (M) {
-      case 1: TWELL_LAUNCH("ffn_up_kernel", (ffn_up_kernel<TS, 1>), gup, blk, 0, s, a, parts, i0, i1); break;
-      case 2: TWELL_LAUNCH("ffn_up_kernel", (ffn_up_kernel<TS, 2>), gup, blk, 0, s, a, parts, i0, i1); break;
-      case 4: TWELL_LAUNCH("ffn_up_kernel", (ffn_up_kernel<TS, 4>), gup, blk, 0, s, a, parts, i0, i1); break;
-      case 8: TWELL_LAUNCH("ffn_up_kernel", (ffn_up_kernel<TS, 8>), gup, blk, 0, s, a, parts, i0, i1); break;
-      case 16: TWELL_LAUNCH("ffn_up_kernel", (ffn_up_kernel<TS, 16>), gup, blk, 0, s, a, parts, i0, i1); break;
+    const dim3 gup((unsigned)(tblocks * parts * a.up_nq));
+#define TWELL_UP(MM) \
+  case MM:           \
+    TWELL_LAUNCH("ffn_up_kernel", (ffn_up_kernel<TS, MM>), gup, blk, 0, s, a, parts, tblocks, i0, i1); break;
+    switch (Mq) {
+      TWELL_UP(1) TWELL_UP(2) TWELL_UP(4) TWELL_UP(8) TWELL_UP(16)
       default: return hipErrorInvalidValue;
     }
+#undef TWELL_UP
     if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (a.up_nq > 1) {
+      TWELL_LAUNCH("ffn_up_finish", ffn_up_finish, dim3((unsigned)tblocks), blk, 0, s, a, i0, i1);
+      if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
     const dim3 gdn((unsigned)(tblocks * P));
 #define TWELL_DOWN(E, R) \
   TWELL_LAUNCH("ffn_down_kernel", (ffn_down_kernel<TS, E, R>), gdn, blk, 0, s, a, G8, tblocks, i0, i1)

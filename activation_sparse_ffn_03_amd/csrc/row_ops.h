@@ -193,6 +193,24 @@ inline SliceGeom pick_l2_slices(int D, int esz, int64_t rows) {
   return {D / slice, slice / lpr, 64 / lpr};
 }
 
+// Workgroup b of a sliced launch over `blocks` row blocks and P slices that go
+// G8 at a time (slice_group): slice pass * G8 + b % G8 and row block
+// (b / G8) % blocks, passes in grid order. Workgroups are dealt to the 8 XCDs
+// round-robin, so with G8 = 8 each XCD holds one slice at a time.
+__device__ __forceinline__ void slice_block(int64_t b, int G8, int64_t blocks, int& p, int64_t& rb) {
+  const int64_t r = b / G8;
+  p = (int)(r / blocks) * G8 + (int)(b % G8);
+  rb = r % blocks;
+}
+// Slices per pass: 8 (one per XCD) when they divide P, else all P in one pass.
+inline int slice_group(int P) { return P % 8 == 0 ? 8 : P; }
+
+// Load instructions a sliced gather keeps in flight per wave: 4 KB per wave
+// whatever the slice width (RPI = 1 loads one row per instruction), but no
+// more rows than one 64-entry list holds.
+template <int RPI>
+constexpr int sliced_inflight() { return RPI == 1 ? 8 : (64 / RPI < 4 ? 64 / RPI : 4); }
+
 // acc += sum over the list entries k < n of z_k * row(c_k)[slice], where lane
 // k of (c_l, z_l) holds entry k and `base` already points at this lane's slice
 // elements. Lane group g = lane / (64/RPI) takes entries g, g+RPI, ...; U load

@@ -176,6 +176,9 @@ twell_status twell_ffn_fwd(const twell_dims* dims, twell_dtype dtype, const twel
   char* base = reinterpret_cast<char*>(ws);
   a.offs = reinterpret_cast<int32_t*>(base + L.offs);
   a.zlist = reinterpret_cast<uint2*>(base + L.zlist);
+  a.upart = reinterpret_cast<float*>(base + L.upart);
+  a.uslot = reinterpret_cast<int32_t*>(base + L.uslot);
+  a.up_nq = twell::up_passes(s);
   a.part = reinterpret_cast<float*>(base + L.part);
   return hip_status(twell::launch_ffn_fwd(a, (hipStream_t)stream), "twell_ffn_fwd");
 }

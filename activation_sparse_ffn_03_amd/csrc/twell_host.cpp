@@ -84,11 +84,25 @@ twell_status check_shape(const twell_dims* d, int dtype, Shape* s, std::string* 
   return TWELL_OK;
 }
 
+int up_passes(const Shape& s) {
+  const int parts = s.n_tiles < 8 ? s.n_tiles : 8;
+  if (parts <= 0) return 1;
+  const int64_t rows = ((int64_t)s.F + parts - 1) / parts;
+  const int64_t wave_elems = 64 * (16 / s.esz);  // one 16-byte load per lane
+  int nq = 1;
+  while (rows * (s.D / nq) * s.esz > (4ll << 20) && s.D % (2 * nq * wave_elems) == 0) nq *= 2;
+  return nq;
+}
+
 FwdLayout fwd_layout(const Shape& s) {
   FwdLayout L{};
+  const size_t entries = (size_t)s.N * s.n_tiles * s.slots;
+  const int nq = up_passes(s);
   L.offs = 0;
-  L.zlist = align_up(((size_t)s.n_tiles + 1) * (size_t)s.N * 4);
-  L.part = L.zlist + align_up((size_t)s.N * s.n_tiles * s.slots * 8);
+  L.zlist = align_up((size_t)s.N * 4);
+  L.upart = L.zlist + align_up(entries * 8);
+  L.uslot = L.upart + (nq > 1 ? align_up((size_t)nq * entries * 4) : 0);
+  L.part = L.uslot + (nq > 1 ? align_up(entries * 4) : 0);
   L.total = L.part + (size_t)s.ovf_cap * s.G * s.D * 4;
   return L;
 }

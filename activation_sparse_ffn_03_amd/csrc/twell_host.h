@@ -33,10 +33,19 @@ struct BwdLayout {
 twell_status check_shape(const twell_dims* dims, int dtype, Shape* out, std::string* why);
 void compute_sizes(const Shape& s, twell_sizes* out);
 BwdLayout bwd_layout(const Shape& s);
-// Forward workspace, in order: per-row tile offsets ([n_t+1][N] int32), the
-// row-major (column, z) list ([N][n_t*S] x 8 bytes), the dense-row partials.
+// Passes over d_model of the up projection. W_up's columns are dealt to the 8
+// XCDs (F/8 rows of W_up each); when such a block is larger than the XCD's
+// 4 MB L2, d_model is cut into up_passes power-of-two ranges (each a whole
+// number of 16-byte loads of a 64-lane wave) so that one range's block fits,
+// and the partial dot products of the ranges go through the workspace.
+int up_passes(const Shape& s);
+// Forward workspace, in order: per-row entry totals ([N] int32), the
+// row-major (column, z) list ([N][n_t*S] x 8 bytes), and only when
+// up_passes > 1 the passes' partial dot products ([up_passes][N][n_t*S] fp32)
+// and the slot of every list entry ([N][n_t*S] int32); then the dense-row
+// partials.
 struct FwdLayout {
-  size_t offs, zlist, part, total;
+  size_t offs, zlist, upart, uslot, part, total;
 };
 FwdLayout fwd_layout(const Shape& s);
 size_t fwd_ws_bytes(const Shape& s);

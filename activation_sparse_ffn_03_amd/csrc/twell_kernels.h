@@ -58,8 +58,11 @@ struct FwdArgs {
   const void* w_down;
   float* y;
   float* a_save;
-  int32_t* offs;  // [n_t+1][N]: entries of the row's tiles before tile j (workspace)
+  int32_t* offs;  // [N]: number of packed entries of each row (workspace)
   uint2* zlist;   // [N][n_t*S]: (column, z = h*a) of every packed entry, row-major (workspace)
+  float* upart;   // [up_nq][N][n_t*S]: partial a over each d_model range (workspace, up_nq > 1)
+  int32_t* uslot; // [N][n_t*S]: slot of each list entry, for a_save (workspace, up_nq > 1)
+  int up_nq;      // passes of the up projection over d_model (up_passes)
   float* part;    // [ovf_cap][G][D] fp32 partial outputs of dense-row chunks (workspace)
 };
 

@@ -167,10 +167,12 @@ twell_status twell_pack_preact(const twell_dims* dims, twell_dtype dtype, const 
  * left unwritten; the pack's status says so).
  * a_save: optional [n_t][S][N] fp32; when given, a = x_i · w_up_t[c] is stored
  * at the slot of every packed entry of non-overflow rows (training).
- * ws: workspace of at least twell_sizes.ws_fwd bytes: per-row tile offsets,
+ * ws: workspace of at least twell_sizes.ws_fwd bytes: per-row entry totals,
  * the (column, z = h·a) pair of every packed entry in row-major order (the
  * sparse intermediate between the up and the down projection, never a dense
- * hidden state) and the partial rows of the overflow-row chunks. */
+ * hidden state), for large d_model x d_ff the partial a of every entry over
+ * each of a few d_model ranges, and the partial rows of the overflow-row
+ * chunks. */
 twell_status twell_ffn_fwd(const twell_dims* dims, twell_dtype dtype, const twell_pack* pack,
                            const void* x, const void* w_up_t, const void* w_down, float* y,
                            float* a_save, void* ws, size_t ws_bytes, void* stream);
