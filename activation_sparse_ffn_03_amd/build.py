@@ -26,7 +26,8 @@ HIP_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", INCLUDE, "-I", CSRC,
 ]
-SOURCES = ["twell_host.cpp", "twell_api.hip", "trace.hip", "scan.hip", "gate_pack.hip", "fused_fwd.hip", "route.hip", "bwd.hip"]
+SOURCES = ["twell_host.cpp", "twell_api.hip", "trace.hip", "side_stream.hip", "scan.hip", "gate_pack.hip",
+           "fused_fwd.hip", "route.hip", "bwd.hip"]
 
 
 def _hipcc() -> str:

@@ -459,6 +459,40 @@ __global__ __launch_bounds__(256) void bwd_dw(BwdArgs a, int G8, int64_t cblocks
   }
 }
 
+// Column transpose of the records (stable: rows ascend within a column).
+hipError_t launch_csc(const BwdArgs& a, hipStream_t s, int nrb) {
+  const size_t lds = (size_t)((a.F + 1) / 2) * 4;
+  TWELL_LAUNCH("csc_hist", csc_hist, dim3(nrb), 256, lds, s, a.ws.row_ptr, a.ws.pair_col, a.N, a.F, a.ws.blk_cnt);
+  TWELL_LAUNCH("csc_coltotal", csc_coltotal, dim3((a.F + 255) / 256), 256, 0, s, a.ws.blk_cnt, nrb, a.F, a.ws.col_ptr);
+  TWELL_LAUNCH("csc_colscan", csc_colscan, 1, 1024, 0, s, a.ws.col_ptr, a.F);
+  TWELL_LAUNCH("csc_offsets", csc_offsets, dim3((a.F + 255) / 256), 256, 0, s, a.ws.blk_cnt, a.ws.col_ptr, nrb, a.F);
+  TWELL_LAUNCH("csc_fill", csc_fill, dim3(nrb), 64, lds, s, a.ws.row_ptr, a.ws.pair_col, a.ws.blk_cnt, a.N, a.F,
+               a.ws.csc_pair, a.ws.csc_row);
+  return hipGetLastError();
+}
+
+// dx: every row, d_model sliced to fit a slice of W_up (F rows) in L2.
+template <typename TS>
+hipError_t launch_dx(const BwdArgs& a, hipStream_t s) {
+  const dim3 blk(256);
+  const SliceGeom geom = pick_l2_slices(a.D, (int)sizeof(TS), a.F);
+  const int P = geom.P, G8 = slice_group(P);
+  const int64_t rblocks = (a.N + 3) / 4;
+  const dim3 gdx((unsigned)(rblocks * P));
+#define TWELL_DX(E, R) TWELL_LAUNCH("bwd_dx", (bwd_dx<TS, E, R, false>), gdx, blk, 0, s, a, G8, rblocks)
+#define TWELL_DXG(E, R) TWELL_LAUNCH("bwd_dx_gate", (bwd_dx<TS, E, R, true>), gdx, blk, 0, s, a, G8, rblocks)
+  if constexpr (sizeof(TS) == 2) {
+    TWELL_SLICED_CASES(8, TWELL_DX)
+    TWELL_SLICED_CASES(8, TWELL_DXG)
+  } else {
+    TWELL_SLICED_CASES(4, TWELL_DX)
+    TWELL_SLICED_CASES(4, TWELL_DXG)
+  }
+#undef TWELL_DX
+#undef TWELL_DXG
+  return hipGetLastError();
+}
+
 template <typename TS>
 hipError_t launch_t(const BwdArgs& a, hipStream_t s) {
   constexpr int E = ChunkElems<TS>::E;
@@ -475,7 +509,25 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t s) {
   }
   TWELL_LAUNCH("row_scan", row_scan, 1, 1024, 0, s, a, dense_nnz);
 
-  // dz records: ELL rows by column part, dense rows by column chunk
+  // dz records: ELL rows by column part (main stream), dense rows by column
+  // chunk (side stream: disjoint record ranges)
+  hipStream_t side = s;
+  if (a.dense_cap > 0) {
+    if ((err = fork_side(s, &side)) != hipSuccess) return err;
+    const dim3 gdd((unsigned)(((int64_t)a.dense_cap * G + 3) / 4));
+    switch (M) {
+      case 1: TWELL_LAUNCH("bwd_dz_dense", (bwd_dz_dense<TS, 1>), gdd, blk, 0, side, a, G); break;
+      case 2: TWELL_LAUNCH("bwd_dz_dense", (bwd_dz_dense<TS, 2>), gdd, blk, 0, side, a, G); break;
+      case 4: TWELL_LAUNCH("bwd_dz_dense", (bwd_dz_dense<TS, 4>), gdd, blk, 0, side, a, G); break;
+      case 8: TWELL_LAUNCH("bwd_dz_dense", (bwd_dz_dense<TS, 8>), gdd, blk, 0, side, a, G); break;
+      case 16: TWELL_LAUNCH("bwd_dz_dense", (bwd_dz_dense<TS, 16>), gdd, blk, 0, side, a, G); break;
+      default: (void)join_side(s, side); return hipErrorInvalidValue;
+    }
+    if ((err = hipGetLastError()) != hipSuccess) {
+      (void)join_side(s, side);
+      return err;
+    }
+  }
   const int parts = 8;
   const dim3 gdz((unsigned)(((a.N + 3) / 4) * parts));
   switch (M) {
@@ -484,51 +536,25 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t s) {
     case 4: TWELL_LAUNCH("bwd_dz_ell", (bwd_dz_ell<TS, 4>), gdz, blk, 0, s, a, parts); break;
     case 8: TWELL_LAUNCH("bwd_dz_ell", (bwd_dz_ell<TS, 8>), gdz, blk, 0, s, a, parts); break;
     case 16: TWELL_LAUNCH("bwd_dz_ell", (bwd_dz_ell<TS, 16>), gdz, blk, 0, s, a, parts); break;
-    default: return hipErrorInvalidValue;
+    default: (void)join_side(s, side); return hipErrorInvalidValue;
   }
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  if (a.dense_cap > 0) {
-    const dim3 gdd((unsigned)(((int64_t)a.dense_cap * G + 3) / 4));
-    switch (M) {
-      case 1: TWELL_LAUNCH("bwd_dz_dense", (bwd_dz_dense<TS, 1>), gdd, blk, 0, s, a, G); break;
-      case 2: TWELL_LAUNCH("bwd_dz_dense", (bwd_dz_dense<TS, 2>), gdd, blk, 0, s, a, G); break;
-      case 4: TWELL_LAUNCH("bwd_dz_dense", (bwd_dz_dense<TS, 4>), gdd, blk, 0, s, a, G); break;
-      case 8: TWELL_LAUNCH("bwd_dz_dense", (bwd_dz_dense<TS, 8>), gdd, blk, 0, s, a, G); break;
-      case 16: TWELL_LAUNCH("bwd_dz_dense", (bwd_dz_dense<TS, 16>), gdd, blk, 0, s, a, G); break;
-      default: return hipErrorInvalidValue;
-    }
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+  err = hipGetLastError();
+  const hipError_t ej = join_side(s, side);
+  if (err != hipSuccess) return err;
+  if (ej != hipSuccess) return ej;
+
+  // column transpose of the records on the side stream (only the weight
+  // gradients read it), beside dx on the main stream
+  if ((err = fork_side(s, &side)) != hipSuccess) return err;
+  if ((err = launch_csc(a, side, nrb)) != hipSuccess) {
+    (void)join_side(s, side);
+    return err;
   }
 
-  // dx: every row, d_model sliced to fit a slice of W_up (F rows) in L2
-  {
-  const SliceGeom geom = pick_l2_slices(a.D, (int)sizeof(TS), a.F);
-  const int P = geom.P, G8 = slice_group(P);
-  const int64_t rblocks = (a.N + 3) / 4;
-  const dim3 gdx((unsigned)(rblocks * P));
-#define TWELL_DX(E, R) TWELL_LAUNCH("bwd_dx", (bwd_dx<TS, E, R, false>), gdx, blk, 0, s, a, G8, rblocks)
-#define TWELL_DXG(E, R) TWELL_LAUNCH("bwd_dx_gate", (bwd_dx<TS, E, R, true>), gdx, blk, 0, s, a, G8, rblocks)
-  if constexpr (sizeof(TS) == 2) {
-    TWELL_SLICED_CASES(8, TWELL_DX)
-    TWELL_SLICED_CASES(8, TWELL_DXG)
-  } else {
-    TWELL_SLICED_CASES(4, TWELL_DX)
-    TWELL_SLICED_CASES(4, TWELL_DXG)
-  }
-#undef TWELL_DX
-#undef TWELL_DXG
-  }
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-
-  // column transpose of the records (stable: rows ascend within a column)
-  const size_t lds = (size_t)((a.F + 1) / 2) * 4;
-  TWELL_LAUNCH("csc_hist", csc_hist, dim3(nrb), 256, lds, s, a.ws.row_ptr, a.ws.pair_col, a.N, a.F, a.ws.blk_cnt);
-  TWELL_LAUNCH("csc_coltotal", csc_coltotal, dim3((a.F + 255) / 256), 256, 0, s, a.ws.blk_cnt, nrb, a.F, a.ws.col_ptr);
-  TWELL_LAUNCH("csc_colscan", csc_colscan, 1, 1024, 0, s, a.ws.col_ptr, a.F);
-  TWELL_LAUNCH("csc_offsets", csc_offsets, dim3((a.F + 255) / 256), 256, 0, s, a.ws.blk_cnt, a.ws.col_ptr, nrb, a.F);
-  TWELL_LAUNCH("csc_fill", csc_fill, dim3(nrb), 64, lds, s, a.ws.row_ptr, a.ws.pair_col, a.ws.blk_cnt, a.N, a.F,
-               a.ws.csc_pair, a.ws.csc_row);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
+  err = launch_dx<TS>(a, s);
+  const hipError_t ej2 = join_side(s, side);
+  if (err != hipSuccess) return err;
+  if (ej2 != hipSuccess) return ej2;
 
   // weight gradients: column-owned, d_model in 1/8 slices (slicing x / dy
   // further to fit L2 measured slower here: a column's tokens ascend, so its

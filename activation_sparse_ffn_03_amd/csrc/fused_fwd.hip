@@ -319,10 +319,9 @@ __global__ __launch_bounds__(256) void dense_reduce(const float* __restrict__ pa
 constexpr int64_t kTokenChunk = 0;
 
 template <typename TS>
-hipError_t launch_t(const FwdArgs& a, hipStream_t s, int64_t chunk) {
+hipError_t launch_sparse_rows(const FwdArgs& a, hipStream_t s, int64_t chunk) {
   constexpr int E = ChunkElems<TS>::E;
   const int nch = a.D / E;
-  const int M = pick_m(nch);
   if (a.up_nq < 1 || a.D % (a.up_nq * E) != 0) return hipErrorInvalidValue;
   const int Mq = pick_m(nch / a.up_nq);  // chunks per lane of one d_model range
   const dim3 blk(256);
@@ -362,11 +361,15 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t s, int64_t chunk) {
 #undef TWELL_DOWN
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
+  return hipSuccess;
+}
 
-  // overflow rows: dense chunks + fixed-order reduction into y
-  if (a.ovf_cap == 0) return hipSuccess;
+// Overflow rows: dense chunks + fixed-order reduction into y.
+template <typename TS>
+hipError_t launch_overflow_rows(const FwdArgs& a, hipStream_t s) {
+  const int M = pick_m(a.D / ChunkElems<TS>::E);
   const int G = (a.F + kDenseChunk - 1) / kDenseChunk;
-  const dim3 gov((unsigned)(((int64_t)a.ovf_cap * G + 3) / 4));
+  const dim3 gov((unsigned)(((int64_t)a.ovf_cap * G + 3) / 4)), blk(256);
   switch (M) {
     case 1: TWELL_LAUNCH("ffn_dense_rows", (ffn_dense_rows<TS, 1>), gov, blk, 0, s, a, G); break;
     case 2: TWELL_LAUNCH("ffn_dense_rows", (ffn_dense_rows<TS, 2>), gov, blk, 0, s, a, G); break;
@@ -375,8 +378,25 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t s, int64_t chunk) {
     case 16: TWELL_LAUNCH("ffn_dense_rows", (ffn_dense_rows<TS, 16>), gov, blk, 0, s, a, G); break;
     default: return hipErrorInvalidValue;
   }
-  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
   return launch_dense_reduce(a.part, a.ovf_rows, a.n_ovf, a.ovf_cap, G, a.D, a.y, s);
+}
+
+// The two row kinds share no buffer (the sparse rows' list workspace vs the
+// overflow partials; disjoint rows of y), so the overflow rows run on the side
+// stream beside the up / down launches.
+template <typename TS>
+hipError_t launch_t(const FwdArgs& a, hipStream_t s, int64_t chunk) {
+  hipStream_t side = s;
+  hipError_t err = hipSuccess, err2 = hipSuccess;
+  if (a.ovf_cap > 0) {
+    if ((err = fork_side(s, &side)) != hipSuccess) return err;
+    err = launch_overflow_rows<TS>(a, side);
+  }
+  if (err == hipSuccess) err = launch_sparse_rows<TS>(a, s, chunk);
+  err2 = join_side(s, side);
+  return err != hipSuccess ? err : err2;
 }
 
 }  // namespace

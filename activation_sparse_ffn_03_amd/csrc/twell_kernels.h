@@ -68,6 +68,13 @@ struct FwdArgs {
 
 hipError_t launch_ffn_fwd(const FwdArgs& a, hipStream_t s);
 
+// Side stream of the current device for the independent branch of a call
+// (side_stream.hip): fork_side makes it wait for the work enqueued on `main`
+// and returns it (or `main` itself when no side stream could be created);
+// join_side makes `main` wait for the work enqueued on it.
+hipError_t fork_side(hipStream_t main, hipStream_t* side);
+hipError_t join_side(hipStream_t main, hipStream_t side);
+
 // out[rows[o]] = sum_g part[o][g] for o < min(*n_rows, cap), part [cap][G][D].
 hipError_t launch_dense_reduce(const float* part, const int32_t* rows, const int32_t* n_rows, int cap, int G,
                                int D, float* out, hipStream_t s);
