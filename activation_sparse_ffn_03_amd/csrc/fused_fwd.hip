@@ -44,9 +44,12 @@ constexpr int kParts = 8;  // one part per XCD
 // entry k as (global column c, stored activation h, slot id j*S+s). The slot
 // loads of all tiles are issued back to back into raw registers and decoded
 // once per list, so a token's metadata costs a couple of memory round trips
-// rather than one per tile.
+// rather than one per tile. cnt_first, when not negative, is the caller's
+// already loaded count of tile j0 + lane (clamped to S; 0 past j1), so the
+// first batch needs no load of its own.
 template <typename TS, typename Flush>
-__device__ __forceinline__ void collect_pairs(const FwdArgs& a, int64_t i, int j0, int j1, int lane, Flush&& flush) {
+__device__ __forceinline__ void collect_pairs(const FwdArgs& a, int64_t i, int j0, int j1, int lane, Flush&& flush,
+                                              int cnt_first = -1) {
   const int64_t N = a.N;
   const TS* __restrict__ vals = reinterpret_cast<const TS*>(a.vals);
   int n = 0;
@@ -63,7 +66,9 @@ __device__ __forceinline__ void collect_pairs(const FwdArgs& a, int64_t i, int j
   };
   for (int jb = j0; jb < j1; jb += 64) {
     const int jl = jb + lane;
-    const int cnt_l = jl < j1 ? min((int)a.counts[(size_t)jl * N + i], a.slots) : 0;
+    const int cnt_l = (jb == j0 && cnt_first >= 0) ? cnt_first
+                      : jl < j1                    ? min((int)a.counts[(size_t)jl * N + i], a.slots)
+                                                   : 0;
     uint64_t nz = ballot(cnt_l > 0);
     while (nz) {
       const int t = __ffsll((unsigned long long)nz) - 1;
@@ -97,12 +102,13 @@ __device__ __forceinline__ void collect_pairs(const FwdArgs& a, int64_t i, int j
 
 // ------------------------------------------------------------------ up: z = h * (x_i . W_up^T[c])
 
-// Entries of token i in tiles [0, j0): where tile j0's entries start in the
-// token's (column, z) list. Counts are small integers, so the float wave sum
-// is exact.
-__device__ __forceinline__ int entries_before(const FwdArgs& a, int64_t i, int j0, int lane) {
+// Entries of token i in tiles [64, j0) (the first 64 tiles are summed by the
+// caller from counts it loaded up front): where tile j0's entries start in the
+// token's (column, z) list. Counts are small integers, so the float wave sums
+// are exact.
+__device__ __forceinline__ int entries_before_rest(const FwdArgs& a, int64_t i, int j0, int lane) {
   int before = 0;
-  for (int jb = 0; jb < j0; jb += 64) {
+  for (int jb = 64; jb < j0; jb += 64) {
     const int jl = jb + lane;
     const int c = jl < j0 ? min((int)a.counts[(size_t)jl * a.N + i], a.slots) : 0;
     before += (int)wave_sum_dpp((float)c);
@@ -124,21 +130,25 @@ __global__ __launch_bounds__(256) void ffn_up_kernel(FwdArgs a, int parts, int64
   const int64_t r = blockIdx.x / parts;
   const int q = (int)(r / tblocks);
   const int64_t i = i0 + (r % tblocks) * 4 + (threadIdx.x >> 6);
-  if (i >= i1 || a.ovf_flag[i]) return;
+  if (i >= i1) return;
   const int j0 = (int)((int64_t)part * a.n_tiles / parts), j1 = (int)((int64_t)(part + 1) * a.n_tiles / parts);
   const int D = a.D, Dq = D / a.up_nq, nch = Dq / E;
+  const int64_t N = a.N;
+  // Independent loads first, in one memory round trip: the overflow flag, the
+  // counts of the tiles before this part and of its own tiles, the x slice.
+  const bool ovf = a.ovf_flag[i] != 0;
+  const int cb = lane < j0 ? (int)a.counts[(size_t)lane * N + i] : 0;
+  const int cf = j0 + lane < j1 ? (int)a.counts[(size_t)(j0 + lane) * N + i] : 0;
+  u32x4_t xr[M];
+  load_row<TS, M>(xr, reinterpret_cast<const TS*>(a.x) + (size_t)i * D + (size_t)q * Dq, nch, lane);
+  if (ovf) return;
   const size_t L = (size_t)a.n_tiles * a.slots;
   const TS* __restrict__ w_up = reinterpret_cast<const TS*>(a.w_up) + (size_t)q * Dq;
   uint2* __restrict__ zl = a.zlist + (size_t)i * L;
   float* __restrict__ up = a.upart + ((size_t)q * a.N + i) * L;
-  int lbase = entries_before(a, i, j0, lane);  // list position of this part's first entry
-  u32x4_t xr[M];
-  bool have_x = false;
+  // list position of this part's first entry
+  int lbase = (int)wave_sum_dpp((float)min(cb, a.slots)) + entries_before_rest(a, i, j0, lane);
   auto flush = [&](int c_l, float h_l, int slot_l, int n) {
-    if (!have_x) {
-      load_row<TS, M>(xr, reinterpret_cast<const TS*>(a.x) + (size_t)i * D + (size_t)q * Dq, nch, lane);
-      have_x = true;
-    }
     float a_l = 0.f;
     for (int k = 0; k < n; k += U) {
       u32x4_t wr[U][M];
@@ -173,7 +183,7 @@ __global__ __launch_bounds__(256) void ffn_up_kernel(FwdArgs a, int parts, int64
     }
     lbase += n;
   };
-  collect_pairs<TS>(a, i, j0, j1, lane, flush);
+  collect_pairs<TS>(a, i, j0, j1, lane, flush, min(cf, a.slots));
   if (j1 == a.n_tiles && q == 0 && lane == 0) a.offs[i] = lbase;  // the row's total
 }
 
@@ -212,18 +222,25 @@ __global__ __launch_bounds__(256) void ffn_down_kernel(FwdArgs a, int G8, int64_
   int64_t rb;
   slice_block(blockIdx.x, G8, tblocks, p, rb);
   const int64_t i = i0 + rb * 4 + (threadIdx.x >> 6);
-  if (i >= i1 || a.ovf_flag[i]) return;
+  if (i >= i1) return;
   const int D = a.D;
   const int d0 = p * (LPR * EPL) + (lane % LPR) * EPL;
   const TS* __restrict__ w_down = reinterpret_cast<const TS*>(a.w_down) + d0;
-  const uint2* __restrict__ zl = a.zlist + (size_t)i * a.n_tiles * a.slots;
+  const int L = a.n_tiles * a.slots;
+  const uint2* __restrict__ zl = a.zlist + (size_t)i * L;
+  // Independent loads first, in one memory round trip: the overflow flag, the
+  // row's entry total and (speculatively, inside the row's list) its first 64
+  // entries.
+  const bool ovf = a.ovf_flag[i] != 0;
   const int total = a.offs[i];
+  const uint2 ent0 = lane < L ? zl[lane] : make_uint2(0u, 0u);
+  if (ovf) return;
   float acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
   for (int kb = 0; kb < total; kb += 64) {
     const int n = min(64, total - kb);
-    const uint2 ent = lane < n ? zl[kb + lane] : make_uint2(0u, 0u);
+    const uint2 ent = lane >= n ? make_uint2(0u, 0u) : kb == 0 ? ent0 : zl[kb + lane];
     sliced_axpy<TS, EPL, RPI, U>(w_down, D, a.F, (int)ent.x, __uint_as_float(ent.y), n, lane, acc);
   }
   combine_groups<EPL, RPI>(acc);
