@@ -53,15 +53,20 @@ struct Epi {
 
 __device__ __forceinline__ uint64_t mask_below(int n) { return n >= 64 ? ~0ull : ((1ull << n) - 1ull); }
 
+// Workgroup barrier that orders LDS accesses only (waits for this wave's
+// outstanding LDS operations, not for its global loads or stores).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 __device__ __forceinline__ int dense_valid(const Epi& e) { return min(*e.n_ovf, e.cap); }
 
 // Stage the threshold and the token of logical rows [m0, m0 + nrows) of a tile
 // in LDS (token -1 past the last valid row), so the epilogue reads them
 // without a dependent global load per row. Logical rows are tokens
 // (MODE_PACK) or positions in the overflow list (MODE_DENSE).
+template <int NT>
 __device__ void stage_rows(int64_t m0, int nrows, const Epi& e, float* ts, int32_t* toks) {
   const int64_t limit = (e.mode == MODE_DENSE) ? (int64_t)dense_valid(e) : e.N;
-  for (int r = threadIdx.x; r < nrows; r += blockDim.x) {
+  for (int r = threadIdx.x; r < nrows; r += NT) {
     const int64_t lr = m0 + r;
     int32_t tok = -1;
     float tv = 0.f;
@@ -76,10 +81,10 @@ __device__ void stage_rows(int64_t m0, int nrows, const Epi& e, float* ts, int32
 
 // Dense activation rows of overflow rows (MODE_DENSE): one wave per row of the
 // fp32 tile Gs, lane l writing columns n0+l and n0+64+l of ovf_h row row0+r.
-template <typename TS>
+template <typename TS, int NW>
 __device__ void dense_rows_out(const float* Gs, int rows, int64_t row0, int n0, const Epi& e, const float* ts,
                                const int32_t* toks) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = NW;
   for (int r = wave; r < rows; r += nw) {
     if (toks[r] < 0) break;  // rows past the last valid one
     const float tv = ts[r];
@@ -94,8 +99,9 @@ __device__ void dense_rows_out(const float* Gs, int rows, int64_t row0, int n0, 
 }
 
 // Debug copy of g (g_dump): one wave per row, coalesced.
+template <int NW>
 __device__ void dump_rows(const float* Gs, int rows, int n0, const Epi& e, const int32_t* toks) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = NW;
   for (int r = wave; r < rows; r += nw) {
     const int32_t tok = toks[r];
     if (tok < 0) break;
@@ -108,84 +114,102 @@ __device__ void dump_rows(const float* Gs, int rows, int n0, const Epi& e, const
   }
 }
 
+// Stores the active columns of one TwELL tile of one lane's row: `bits` are
+// the lane's active columns (bit b = column colofs + b of the 128-column group
+// in Gs, i.e. tile column tcol + b), its slots start at `base`, and iteration
+// k of a wave-uniform loop stores every lane's k-th remaining column into slot
+// base + k (slots >= S are not stored: such a row is an overflow row).
+template <typename TS>
+__device__ __forceinline__ void store_slots(uint64_t bits, int base, int colofs, int tcol, int jt, size_t tok,
+                                            bool valid, const float* grow, float tv, const Epi& e) {
+  const int S = e.slots;
+  const int64_t N = e.N;
+  TS* vals = reinterpret_cast<TS*>(e.vals);
+  for (int k = 0;; ++k) {
+    const bool more = valid && bits != 0ull && base + k < S;
+    if (!ballot(more)) break;
+    if (more) {
+      const int b = __ffsll((unsigned long long)bits) - 1;
+      bits &= bits - 1;
+      const size_t pos = ((size_t)jt * S + base + k) * N + tok;
+      vals[pos] = Store<TS>::from_f32(grow[colofs + b] - tv);
+      e.cols[pos] = (uint16_t)(tcol + b);
+    }
+  }
+}
+
 // TwELL pack of `rows` rows of the fp32 tile Gs (row stride GS) whose first
 // column is n0; ts / toks hold the threshold and token of each row (staged by
-// stage_rows). One lane per row: the lane reads its row four columns at a time
-// and builds the row's 128-bit active mask (g > t, columns < F); then, for each
-// TwELL tile of the 128 columns, iteration s of a wave-uniform loop pops every
-// lane's lowest remaining set bit into slot s. Lanes are consecutive tokens,
-// so the slot-major stores of one iteration are contiguous.
-template <typename TS>
-__device__ void pack_lanes(const float* Gs, int rows, int n0, const Epi& e, const float* ts, const int32_t* toks) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  const int tn = e.tile_n, S = e.slots;
+// stage_rows). Two lanes per row, so every wave of the block takes part: lane
+// l of a wave takes row (l & 31) of the wave's 32 rows and the 64 columns of
+// half l >> 5, reads them four at a time and builds their 64-bit active mask
+// (g > t, columns < F). A 128-column TwELL tile spans both halves: the upper
+// half's slots start after the lower half's entries (one exchange of the two
+// popcounts across the halves of the wave); narrower tiles lie inside one
+// half. Slot s of a tile holds its s-th active column in ascending order.
+// Lanes of a half are consecutive tokens, so the slot-major stores of one
+// iteration are contiguous runs.
+template <typename TS, int NW>
+__device__ void pack_rows(const float* Gs, int rows, int n0, const Epi& e, const float* ts, const int32_t* toks) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = NW;
+  const int h = lane >> 5;
+  const int tn = e.tile_n;
   const int64_t N = e.N;
   const int ncol = min(kPackCols, e.F - n0);
   if (ncol <= 0) return;  // a 128-column group past the last column of d_ff
-  TS* vals = reinterpret_cast<TS*>(e.vals);
-  for (int rb = wave * 64; rb < rows; rb += nw * 64) {
-    const int r = rb + lane;
+  const int hcols = ncol - 64 * h;  // valid columns of this lane's half (may be <= 0)
+  for (int rb = wave * 32; rb < rows; rb += nw * 32) {
+    const int r = rb + (lane & 31);
     const int32_t tk = r < rows ? toks[r] : -1;
     const bool valid = tk >= 0;
     if (!ballot(valid)) break;  // rows past the last valid one
     const float tv = valid ? ts[r] : 0.f;
-    uint64_t m[2] = {0ull, 0ull};
-    if (valid) {
-      const float* g = Gs + r * GS;
+    const float* grow = Gs + (valid ? r : 0) * GS;
+    uint64_t m = 0ull;
+    if (valid && hcols > 0) {
+      const float* g = grow + 64 * h;
 #pragma unroll
-      for (int q = 0; q < kPackCols / 4; ++q) {
+      for (int q = 0; q < 16; ++q) {
         const float4 v = *reinterpret_cast<const float4*>(g + 4 * q);
         const uint64_t b = (uint64_t)(v.x > tv) | ((uint64_t)(v.y > tv) << 1) | ((uint64_t)(v.z > tv) << 2) |
                            ((uint64_t)(v.w > tv) << 3);
-        m[q / 16] |= b << (4 * (q % 16));
+        m |= b << (4 * q);
       }
-      m[0] &= mask_below(ncol);
-      m[1] &= ncol > 64 ? mask_below(ncol - 64) : 0ull;
+      m &= mask_below(hcols);
     }
-    for (int t0 = 0; t0 < kPackCols; t0 += tn) {
-      const int jt = (n0 + t0) / tn;
-      if (jt * tn >= e.F) break;
-      uint64_t s0, s1;
-      if (tn == 128) {
-        s0 = m[0];
-        s1 = m[1];
-      } else {
-        s0 = (m[t0 >> 6] >> (t0 & 63)) & mask_below(tn);
-        s1 = 0ull;
-      }
-      const size_t tok = (size_t)(valid ? tk : 0);
-      if (valid) e.counts[(size_t)jt * N + tok] = (uint16_t)(__popcll(s0) + __popcll(s1));
-      for (int sl = 0; sl < S; ++sl) {
-        const bool more = valid && (s0 | s1);
-        if (!ballot(more)) break;
-        if (more) {
-          int bit;
-          if (s0) {
-            bit = __ffsll((unsigned long long)s0) - 1;
-            s0 &= s0 - 1;
-          } else {
-            bit = 64 + __ffsll((unsigned long long)s1) - 1;
-            s1 &= s1 - 1;
-          }
-          const size_t pos = ((size_t)jt * S + sl) * N + tok;
-          vals[pos] = Store<TS>::from_f32(Gs[r * GS + t0 + bit] - tv);
-          e.cols[pos] = (uint16_t)bit;
-        }
+    const size_t tok = (size_t)(valid ? tk : 0);
+    if (tn == kPackCols) {
+      const int jt = n0 / kPackCols;
+      const int pc = __popcll(m);
+      const int other = __shfl_xor(pc, 32, 64);  // the other half's entries
+      if (valid && h == 0) e.counts[(size_t)jt * N + tok] = (uint16_t)(pc + other);
+      store_slots<TS>(m, h ? other : 0, 64 * h, 64 * h, jt, tok, valid, grow, tv, e);
+    } else {
+      for (int t0 = 0; t0 < 64; t0 += tn) {
+        const int col0 = 64 * h + t0;  // first column of the tile in the group
+        const bool exists = n0 + col0 < e.F;
+        const int jt = (n0 + col0) / tn;
+        const uint64_t sb = (m >> t0) & mask_below(tn);
+        if (valid && exists) e.counts[(size_t)jt * N + tok] = (uint16_t)__popcll(sb);
+        store_slots<TS>(sb, 0, col0, 0, jt, tok, valid && exists, grow, tv, e);
       }
     }
   }
 }
 
 // Epilogue of one (rows x 128-column) block of g held in LDS.
-template <typename TS>
+// NW: waves of the calling workgroup (a compile-time constant: reading the
+// block size at run time costs a load whose wait also waits for every
+// outstanding store of the wave).
+template <typename TS, int NW>
 __device__ void pack_epilogue(const float* Gs, int rows, int64_t row0, int n0, const Epi& e, const float* ts,
                               const int32_t* toks) {
   if (e.mode == MODE_DENSE) {
-    dense_rows_out<TS>(Gs, rows, row0, n0, e, ts, toks);
+    dense_rows_out<TS, NW>(Gs, rows, row0, n0, e, ts, toks);
     return;
   }
-  if (e.g_dump) dump_rows(Gs, rows, n0, e, toks);
-  pack_lanes<TS>(Gs, rows, n0, e, ts, toks);
+  if (e.g_dump) dump_rows<NW>(Gs, rows, n0, e, toks);
+  pack_rows<TS, NW>(Gs, rows, n0, e, ts, toks);
 }
 
 // ---------------------------------------------------------------- bf16 MFMA GEMM
@@ -261,7 +285,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gate_mfma_bf16(const uint16_t* 
   } else {
     mlimit = e.N;
   }
-  stage_rows(m0, C::BM, e, ts, toks);  // visible after the first barrier below
+  stage_rows<C::NT>(m0, C::BM, e, ts, toks);  // visible after the first barrier below
 
   // Rows past the last token (or overflow row) and columns past d_ff load row
   // 0 instead: their g is never stored (the epilogue skips those rows and
@@ -368,9 +392,11 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gate_mfma_bf16(const uint16_t* 
           for (int r = 0; r < 4; ++r)
             Gs[(rbase + 4 * (lane >> 4) + r) * GS + cbase + (lane & 15)] = acc[i][j][r];
         }
-      __syncthreads();
-      pack_epilogue<uint16_t>(Gs, C::EPI_ROWS, m0 + p0, n0 + cg * kPackCols, e, ts + p0, toks + p0);
-      __syncthreads();
+      // LDS-only barriers: the epilogue's global stores need no ordering
+      // between waves, and a full __syncthreads would wait for them to finish
+      lds_barrier();
+      pack_epilogue<uint16_t, C::NT / 64>(Gs, C::EPI_ROWS, m0 + p0, n0 + cg * kPackCols, e, ts + p0, toks + p0);
+      lds_barrier();
     }
   }
 }
@@ -423,7 +449,6 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 template <class C, int MODE>
 __global__ __launch_bounds__(C::NT, C::OCC) void gate_mfma_dma(const uint16_t* __restrict__ x,
@@ -445,7 +470,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gate_mfma_dma(const uint16_t* _
   } else {
     mlimit = e.N;
   }
-  stage_rows(m0, C::BM, e, ts, toks);
+  stage_rows<C::NT>(m0, C::BM, e, ts, toks);
 
   // Sources of this wave's DMA groups (rows past the last token / column past
   // d_ff read row 0: never stored).
@@ -537,9 +562,11 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gate_mfma_dma(const uint16_t* _
           for (int r = 0; r < 4; ++r)
             Gs[(rbase + 4 * (lane >> 4) + r) * GS + cbase + (lane & 15)] = acc[i][j][r];
         }
-      __syncthreads();
-      pack_epilogue<uint16_t>(Gs, C::EPI_ROWS, m0 + p0, n0 + cg * kPackCols, e, ts + p0, toks + p0);
-      __syncthreads();
+      // LDS-only barriers: the epilogue's global stores need no ordering
+      // between waves, and a full __syncthreads would wait for them to finish
+      lds_barrier();
+      pack_epilogue<uint16_t, C::NT / 64>(Gs, C::EPI_ROWS, m0 + p0, n0 + cg * kPackCols, e, ts + p0, toks + p0);
+      lds_barrier();
     }
   }
 }
@@ -574,7 +601,7 @@ __global__ __launch_bounds__(256) void gate_simt_f32(const float* __restrict__ x
     mlimit = dense_valid(e);
     if (m0 >= mlimit) return;
   }
-  stage_rows(m0, SBM, e, ts, toks);  // visible after the first barrier of the K loop
+  stage_rows<256>(m0, SBM, e, ts, toks);  // visible after the first barrier of the K loop
   float acc[4][8];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -619,7 +646,7 @@ __global__ __launch_bounds__(256) void gate_simt_f32(const float* __restrict__ x
 #pragma unroll
     for (int j = 0; j < 8; ++j) Gs[(ty * 4 + i) * GS + tx * 8 + j] = acc[i][j];
   __syncthreads();
-  pack_epilogue<float>(Gs, SBM, m0, n0, e, ts, toks);
+  pack_epilogue<float, 4>(Gs, SBM, m0, n0, e, ts, toks);
 }
 
 // ---------------------------------------------------------------- pack from a given g
@@ -637,7 +664,7 @@ __global__ __launch_bounds__(256) void pack_from_g(const float* __restrict__ g, 
     mlimit = dense_valid(e);
     if (m0 >= mlimit) return;
   }
-  stage_rows(m0, SBM, e, ts, toks);
+  stage_rows<256>(m0, SBM, e, ts, toks);
   for (int q = tid; q < SBM * BN; q += 256) {
     const int row = q / BN, col = q % BN;
     const int64_t lr = m0 + row;
@@ -649,7 +676,7 @@ __global__ __launch_bounds__(256) void pack_from_g(const float* __restrict__ g, 
     Gs[row * GS + col] = v;
   }
   __syncthreads();
-  pack_epilogue<TS>(Gs, SBM, m0, n0, e, ts, toks);
+  pack_epilogue<TS, 4>(Gs, SBM, m0, n0, e, ts, toks);
 }
 
 // ---------------------------------------------------------------- overflow rows
