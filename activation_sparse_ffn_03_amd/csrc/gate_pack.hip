@@ -421,16 +421,20 @@ struct DmaCfg {
   static constexpr int FM = WM / 16, FN = WN / 16;
   static constexpr int ROWB = 64;                    // LDS bytes per row per stage (32 bf16)
   static constexpr int STAGE = (BM + BN) * ROWB;     // bytes per stage: A rows then B rows
-  static constexpr int LDS = ST * STAGE;
+  static constexpr int RING = ST * STAGE;
   static constexpr int GROUPS = (BM + BN) / 16;      // 1 KB DMA groups per stage
   static constexpr int GPW = GROUPS / NW;            // DMA instructions per wave per stage
-  static constexpr int EPI_FIT = LDS / (GS * 4);
-  static constexpr int EPI_ROWS = EPI_FIT >= 256 && BM >= 256 ? 256 : EPI_FIT >= 128 && BM >= 128 ? 128 : 64;
+  // The epilogue stages min(BM, 128) rows of fp32 g at a time in the same LDS
+  // (more rows per pass keep all waves of the pack busy; a 128-row pass needs
+  // a little more LDS than a 128x384 ring holds, which still leaves room for
+  // two workgroups per CU).
+  static constexpr int EPI_ROWS = BM >= 128 ? 128 : 64;
+  static constexpr int LDS = RING > EPI_ROWS * GS * 4 ? RING : EPI_ROWS * GS * 4;
   static_assert(WM % 16 == 0 && WN % 16 == 0 && BM % 16 == 0 && BN % 16 == 0, "whole fragments");
   static_assert(GROUPS % NW == 0, "DMA groups must split evenly over waves");
   static_assert(BN % 128 == 0, "N tile must be whole 128-column pack groups");
   static_assert(ST >= 2 && ST <= 4, "ring depth");
-  static_assert(BM % EPI_ROWS == 0 && EPI_ROWS * GS * 4 <= LDS, "epilogue staging must fit");
+  static_assert(BM % EPI_ROWS == 0, "epilogue passes must tile BM");
   static_assert(LDS + BM * 8 <= 160 * 1024, "LDS budget of a gfx950 workgroup");
 };
 
