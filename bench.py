@@ -316,6 +316,31 @@ def main():
         torch.cuda.synchronize()
         dense = d0.elapsed_time(d1) / args.steps
 
+    # per-step times (each step bracketed by its own events): warm caches, and
+    # cold ones (a 512 MB write between steps evicts the 4 MB L2s and the 256 MB
+    # Infinity Cache), median and minimum over `steps` steps each
+    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def per_step(fn, cold):
+        times = []
+        for _ in range(args.steps):
+            if cold:
+                flush_buf.fill_(1)
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record(stream)
+            fn()
+            a1.record(stream)
+            torch.cuda.synchronize()
+            times.append(a0.elapsed_time(a1))
+        times.sort()
+        return {"median": times[len(times) // 2], "min": times[0]}
+
+    step_ms = {"warm": per_step(step, False), "cold": per_step(step, True)}
+    dense_step_ms = None
+    if dense is not None:
+        dense_step_ms = {"warm": per_step(dense_step, False), "cold": per_step(dense_step, True)}
+    del flush_buf
+
     flops_dense = 6.0 * w.N * w.D * w.F * (3 if train else 1)
     out = {
         "metric": METRIC,
@@ -335,6 +360,8 @@ def main():
                    "parallelism": "none (1 GPU)"},
         "speedup_vs_dense": (dense / ms) if dense else None,
         "dense_bf16_ms_per_step": dense,
+        "step_ms": step_ms,
+        "dense_step_ms": dense_step_ms,
         "dense_equivalent_tflops": flops_dense / (ms / 1e3) / 1e12,
         "roofline": roof,
         "kernels": kernels,

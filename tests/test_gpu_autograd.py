@@ -1,0 +1,92 @@
+"""The torch.autograd wrapper of the libtwell path against the oracle.
+
+Inputs are on the exact grid (g is exact in fp32 everywhere), so the mask and
+the stored activations are unique; the wrapper's y and parameter gradients
+are compared with the oracle's fp64 forward and backward like the direct
+calls of the C ABI are.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from activation_sparse_ffn_03_amd.autograd import TwellConfig, TwellFFNFunction, TwellGatedFFN
+from oracle import twell_oracle as orc
+from synth import make_inputs
+
+from gpu_util import f64, require_gpu, rowwise_ok
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(dtype):
+    if dtype == "f32":
+        w = make_inputs("c1", N=512, D=128, F=512, grid=True)
+        w.lam = 1e-3
+    else:
+        w = make_inputs("c5", N=768, D=256, F=1024, row_cap=24, grid=True)
+    w.dy = np.random.default_rng(7).integers(-16, 17, (w.N, w.D)).astype(np.float32) / 8  # exact in bf16
+    return w
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_autograd_function_matches_oracle(dtype):
+    require_gpu()
+    w = _case(dtype)
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+
+    def dev(a, grad=False):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda().to(tdt).requires_grad_(grad)
+
+    x, wg, wu, wd = dev(w.x, True), dev(w.w_gate_t, True), dev(w.w_up_t, True), dev(w.w_down, True)
+    t = torch.from_numpy(w.t.astype(np.float32)).cuda()
+    K = 28 if dtype == "f32" else w.row_cap
+    cfg = TwellConfig(tile_n=w.tile_n, slots=w.slots, row_cap=K, ovf_frac=1.0, dense_frac=1.0)
+    y = TwellFFNFunction.apply(x, wg, wu, wd, t, w.lam, cfg)
+    dy = torch.from_numpy(w.dy).cuda()
+    (y * dy).sum().backward()
+    torch.cuda.synchronize()
+
+    fw = orc.ffn_forward(w.x, w.w_gate_t, w.w_up_t, w.w_down, w.t, store=w.dtype, arith="f32")
+    bw = orc.ffn_backward(w.x, w.dy, w.w_gate_t, w.w_up_t, w.w_down, fw["mask"], fw["hq"], w.lam)
+    rowwise_ok(f64(y), fw["y"], 1e-4, "y")
+    got = {"dx": x.grad, "dw_gate_t": wg.grad, "dw_up_t": wu.grad, "dw_down": wd.grad}
+    for k, g in got.items():
+        if dtype == "f32":  # fp32 parameters get the kernels' fp32 gradients
+            rowwise_ok(f64(g), bw[k], 1e-4, k)
+        else:
+            # bf16 parameters get them rounded to bf16: within one bf16 step
+            # (2^-8 relative) of the fp64 value, plus the fp32 tolerance of the row
+            ref, gg = bw[k], f64(g)
+            rms = np.sqrt(np.mean(ref * ref, axis=1, keepdims=True))
+            bad = np.abs(gg - ref) > 2.0 ** -8 * np.abs(ref) + 1e-4 * rms
+            assert not bad.any(), f"{k}: {int(bad.sum())} elements beyond one bf16 step"
+
+
+def test_module_trains_and_two_forwards_before_backward():
+    """Each call keeps its own sparse state: two forwards, then both backwards,
+    give the same gradients as running them one after the other."""
+    require_gpu()
+    torch.manual_seed(0)
+    # thresholds of 2 leave about 2 % of the 1024 units active (about 23 per row)
+    m = TwellGatedFFN(256, 1024, l1_lambda=1e-4, cfg=TwellConfig(row_cap=64, dense_frac=0.5))
+    xa = torch.randn(300, 256, device="cuda").to(torch.bfloat16)
+    xb = torch.randn(200, 256, device="cuda").to(torch.bfloat16)
+    ta = torch.full((300,), 2.0, device="cuda")
+    tb = torch.full((200,), 2.0, device="cuda")
+
+    def grads(loss):
+        m.zero_grad(set_to_none=True)
+        loss.backward()
+        return [p.grad.float().clone() for p in (m.w_gate_t, m.w_up_t, m.w_down)]
+
+    ya, yb = m(xa, ta), m(xb, tb)
+    g_both = grads(ya.square().sum() + yb.square().sum())
+    g_a = grads(m(xa, ta).square().sum())
+    g_b = grads(m(xb, tb).square().sum())
+    for gab, ga, gb in zip(g_both, g_a, g_b):
+        assert torch.isfinite(gab).all()
+        ref = ga + gb
+        err = (gab - ref).abs().max().item()
+        assert err <= 2 ** -6 * ref.abs().max().item(), err
