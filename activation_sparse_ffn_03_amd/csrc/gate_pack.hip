@@ -581,9 +581,14 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gate_mfma_dma(const uint16_t* _
 // 128x384 tile (four waves of 128x96, two workgroups per CU; a 256x384 tile
 // of eight waves runs its main loop faster but its pack epilogue, with two of
 // eight waves busy per 128-row pass, costs more than that gains), the
-// overflow rows the register-staged 128x128 kernel (a few rows, gathered).
+// overflow rows the register-staged kernel (a few rows, gathered): 64x128
+// tiles for d_model <= 2048 (half the padding rows of a 128-row tile), 128x128
+// above (with a long K the better operand reuse of the larger wave tiles wins;
+// measured 46 -> 35 us at d_model 2048 and 80 -> 109 us at 4096 for 64-row
+// tiles).
 using GatePack = DmaCfg<128, 384, 1, 4, 2, 2>;
-using GateRows = MfmaCfg<128, 128, 2, 2>;
+using GateRowsS = MfmaCfg<64, 128, 1, 4>;
+using GateRowsL = MfmaCfg<128, 128, 2, 2>;
 
 
 // ---------------------------------------------------------------- fp32 SIMT GEMM
@@ -749,9 +754,16 @@ hipError_t launch_gate_pack(const GateArgs& a, hipStream_t s) {
     else
       TWELL_LAUNCH("pack_from_g_rows", (pack_from_g<float, MODE_DENSE>), dim3(mb * ncb), 256, 0, s, a.g_in, ncb, e);
   } else if (a.is_bf16) {
-    const int mbc = (a.ovf_cap + GateRows::BM - 1) / GateRows::BM, nbc = (a.F + GateRows::BN - 1) / GateRows::BN;
-    TWELL_LAUNCH("gate_mfma_bf16_rows", (gate_mfma_bf16<GateRows, MODE_DENSE>), dim3(mbc * nbc), GateRows::NT, 0, s,
-                 (const uint16_t*)a.x, (const uint16_t*)a.w, a.D, mbc, nbc, e);
+    auto rows = [&](auto cfg) {
+      using R = decltype(cfg);
+      const int mbc = (a.ovf_cap + R::BM - 1) / R::BM, nbc = (a.F + R::BN - 1) / R::BN;
+      TWELL_LAUNCH("gate_mfma_bf16_rows", (gate_mfma_bf16<R, MODE_DENSE>), dim3(mbc * nbc), R::NT, 0, s,
+                   (const uint16_t*)a.x, (const uint16_t*)a.w, a.D, mbc, nbc, e);
+    };
+    if (a.D <= 2048)
+      rows(GateRowsS{});
+    else
+      rows(GateRowsL{});
   } else {
     const int64_t mb = (a.ovf_cap + SBM - 1) / SBM;
     TWELL_LAUNCH("gate_simt_f32_rows", gate_simt_f32<MODE_DENSE>, dim3(mb * ncb), 256, 0, s, (const float*)a.x, (const float*)a.w, a.D, ncb, e);
