@@ -146,6 +146,72 @@ def ffn_forward(x, w_gate_t, w_up_t, w_down, t, store: str = "bf16", arith: str 
 
 
 # ---------------------------------------------------------------------------
+# 8-bit gate operands (OCP FP8 E4M3)
+# ---------------------------------------------------------------------------
+# "How TwELL by Sakana AI and NVIDIA Accelerates LLMs by 20% Using Unstructured
+# Sparsity", "Long-term Impact": TwELL combined with 8-bit quantisation is named
+# as a direction. Reading taken here (the page fixes no scheme): only the gate
+# projection's operands are quantised, to FP8 E4M3 with one fp32 scale per row
+# (per token for x, per hidden unit for W_gate) equal to the row's largest
+# magnitude / 448; g = s_x,i * s_w,c * sum_k q_x[i,k] q_w[c,k]; everything after
+# g (threshold, TwELL, up/down, backward) is unchanged.
+
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(q) -> np.ndarray:
+    """FP8 E4M3 ("FN" variant) code -> value: sign bit, 4 exponent bits with
+    bias 7, 3 mantissa bits; exponent field 0 holds subnormals m * 2^-9; there
+    are no infinities and S.1111.111 is NaN (so the largest value is 448)."""
+    q = np.asarray(q, dtype=np.uint8).astype(np.int64)
+    sign = np.where((q & 0x80) != 0, -1.0, 1.0)
+    e = (q >> 3) & 0xF
+    m = (q & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    mag = np.where((e == 15) & ((q & 0x7) == 7), np.nan, mag)
+    return sign * mag
+
+
+def e4m3_encode(v) -> np.ndarray:
+    """Value -> FP8 E4M3 code, rounding to the nearest representable value with
+    ties to the even code, and saturating magnitudes beyond 448 to 448 (NaN ->
+    0x7F). The quantum of a magnitude a is 2^(e - 3) for 2^e <= a < 2^(e+1)
+    (e >= -6) and 2^-9 below 2^-6 (subnormals)."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    _, ex = np.frexp(a)  # a = f * 2^ex, f in [0.5, 1): floor(log2 a) = ex - 1
+    e = np.clip(ex - 1, -6, 8).astype(np.float64)
+    quantum = np.exp2(e - 3.0)
+    r = np.minimum(np.rint(a / quantum) * quantum, E4M3_MAX)  # np.rint: ties to even
+    # encode the representable magnitude r
+    _, er = np.frexp(np.where(r > 0, r, 1.0))
+    er = (er - 1).astype(np.int64)
+    sub = r < 2.0 ** -6
+    m_sub = np.rint(r / 2.0 ** -9).astype(np.int64)
+    m_nrm = np.rint((r / np.exp2(er.astype(np.float64)) - 1.0) * 8.0).astype(np.int64)
+    code = np.where(sub, m_sub, ((er + 7) << 3) | m_nrm)
+    code = np.where(np.signbit(v), code | 0x80, code)
+    code = np.where(np.isnan(v), 0x7F, code)
+    return code.astype(np.uint8)
+
+
+def quantize_rows_e4m3(a):
+    """Per-row FP8 quantisation: scale = float32(max|row|) / 448 in float32
+    (1 for an all-zero row), q = e4m3(float32(a / scale)). Returns (q uint8,
+    scale float32)."""
+    a32 = np.asarray(a, dtype=np.float32)
+    amax = np.max(np.abs(a32), axis=1) if a32.shape[1] else np.zeros(a32.shape[0], np.float32)
+    scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    scaled = (a32 / scale[:, None]).astype(np.float32)
+    return e4m3_encode(scaled), scale
+
+
+def gate_preact_fp8(xq, x_scale, wq, w_scale) -> np.ndarray:
+    """g[i, c] = s_x[i] * s_w[c] * sum_k e4m3(q_x[i, k]) * e4m3(q_w[c, k]), fp64."""
+    return (_f64(x_scale)[:, None] * _f64(w_scale)[None, :]) * (e4m3_decode(xq) @ e4m3_decode(wq).T)
+
+
+# ---------------------------------------------------------------------------
 # TwELL: tile-wise ELLPACK pack / unpack
 # ---------------------------------------------------------------------------
 

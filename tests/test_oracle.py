@@ -428,3 +428,73 @@ def test_store_ulp_and_rounding_ambiguity():
     assert not orc.rounding_ambiguous(np.array([mid + 1e-6]), 1e-9)[0]
     assert orc.rounding_ambiguous(np.array([mid + 1e-6]), 2e-6)[0]
     assert not orc.rounding_ambiguous(np.array([0.0]), 1.0)[0]
+
+
+# ----------------------------------------------------------------- FP8 E4M3 gate operands
+
+def test_e4m3_decode_known_codes():
+    """Values fixed by the format (sign, 4 exponent bits with bias 7, 3
+    mantissa bits, subnormals m * 2^-9, S.1111.111 = NaN)."""
+    known = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0, 0x39: 1.125,
+             0x3F: 1.875, 0x40: 2.0, 0x70: 128.0, 0x7E: 448.0, 0xB8: -1.0, 0xFE: -448.0}
+    codes = np.array(list(known), dtype=np.uint8)
+    np.testing.assert_array_equal(orc.e4m3_decode(codes), np.array(list(known.values())))
+    assert np.isnan(orc.e4m3_decode(np.array([0x7F, 0xFF], np.uint8))).all()
+    assert np.signbit(orc.e4m3_decode(np.array([0x80], np.uint8)))[0]
+
+
+def test_e4m3_encode_matches_torch_cast():
+    """Independent implementation: torch's float8_e4m3fn cast (round to
+    nearest even) on values spanning the subnormal and normal ranges."""
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal(300000) * np.exp2(rng.integers(-14, 9, 300000))).astype(np.float32)
+    x = np.clip(x, -448, 448)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(orc.e4m3_encode(x), ref)
+
+
+def test_e4m3_round_trip_ties_and_saturation():
+    codes = np.arange(256, dtype=np.uint8)
+    v = orc.e4m3_decode(codes)
+    ok = ~np.isnan(v)
+    np.testing.assert_array_equal(orc.e4m3_encode(v[ok]), codes[ok])
+    # ties go to the even code: 1 + 1/16 between 0x38 and 0x39, 1 + 3/16 between 0x39 and 0x3A,
+    # half the smallest subnormal between 0 and 0x01, 1.5 x it between 0x01 and 0x02
+    ties = np.array([1.0625, 1.1875, 2.0 ** -10, 3 * 2.0 ** -10, -1.0625])
+    np.testing.assert_array_equal(orc.e4m3_encode(ties), np.array([0x38, 0x3A, 0x00, 0x02, 0xB8], np.uint8))
+    # beyond the largest value: saturate
+    np.testing.assert_array_equal(orc.e4m3_encode(np.array([460.0, 1e6, -1e6])), np.array([0x7E, 0x7E, 0xFE], np.uint8))
+    assert orc.e4m3_encode(np.array([np.nan]))[0] == 0x7F
+
+
+def test_quantize_rows_e4m3():
+    rng = np.random.default_rng(4)
+    a = (rng.standard_normal((37, 300)) * np.exp2(rng.integers(-6, 6, (37, 1)))).astype(np.float32)
+    a[5] = 0.0
+    q, s = orc.quantize_rows_e4m3(a)
+    assert q.dtype == np.uint8 and s.dtype == np.float32
+    assert s[5] == 1.0 and (q[5] == 0).all()
+    deq = orc.e4m3_decode(q) * s[:, None].astype(np.float64)
+    # each magnitude keeps 4 significant bits: error <= half a quantum = 2^-4 relative (plus the subnormal floor)
+    err = np.abs(deq - a)
+    assert (err <= 2.0 ** -4 * np.abs(a) + 2.0 ** -10 * s[:, None]).all()
+    # the largest magnitude of each row maps to (about) 448
+    big = np.abs(orc.e4m3_decode(q)).max(axis=1)
+    assert np.all((big[np.arange(37) != 5] >= 416) & (big[np.arange(37) != 5] <= 448))
+
+
+def test_gate_preact_fp8_closed_form():
+    """With operands that are already E4M3 values and unit scales the FP8 gate
+    is the plain product of the dequantised operands; scales factor out."""
+    rng = np.random.default_rng(5)
+    xq = rng.integers(0, 0x7F, (9, 64)).astype(np.uint8)
+    wq = rng.integers(0, 0x7F, (13, 64)).astype(np.uint8)
+    xq[xq == 0x7F] = 0
+    wq[wq == 0x7F] = 0
+    one_x, one_w = np.ones(9, np.float32), np.ones(13, np.float32)
+    g = orc.gate_preact_fp8(xq, one_x, wq, one_w)
+    ref = orc.e4m3_decode(xq) @ orc.e4m3_decode(wq).T
+    np.testing.assert_array_equal(g, ref)
+    sx = np.float32(2.0) ** rng.integers(-3, 3, 9).astype(np.float32)
+    sw = np.float32(2.0) ** rng.integers(-3, 3, 13).astype(np.float32)
+    np.testing.assert_allclose(orc.gate_preact_fp8(xq, sx, wq, sw), ref * np.outer(sx, sw), rtol=0, atol=0)
