@@ -6,4 +6,5 @@ declared in include/twell.h); `twell` is its thin ctypes binding and
 """
 from . import twell  # noqa: F401
 from .twell import (BF16, F32, TwellError, TwellFFN, alloc_hybrid, alloc_pack, alloc_workspace, ffn_bwd,  # noqa: F401
-                    ffn_fwd, gate_pack, make_dims, n_tiles, pack_preact, query_sizes, route_hybrid)
+                    ffn_fwd, gate_pack, gate_pack_fp8, make_dims, n_tiles, pack_preact, quantize_e4m3, query_sizes,
+                    route_hybrid)

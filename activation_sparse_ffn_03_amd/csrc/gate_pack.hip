@@ -49,6 +49,8 @@ struct Epi {
   const int32_t* n_ovf;  // MODE_DENSE: true count (device)
   int cap;               // MODE_DENSE: capacity
   void* ovf_h;           // MODE_DENSE: [cap][F]
+  const float* x_scale;  // FP8 operands: per-token scale of x (else null)
+  const float* w_scale;  // FP8 operands: per-unit scale of w_gate_t (else null)
 };
 
 __device__ __forceinline__ uint64_t mask_below(int n) { return n >= 64 ? ~0ull : ((1ull << n) - 1ull); }
@@ -64,18 +66,20 @@ __device__ __forceinline__ int dense_valid(const Epi& e) { return min(*e.n_ovf, 
 // without a dependent global load per row. Logical rows are tokens
 // (MODE_PACK) or positions in the overflow list (MODE_DENSE).
 template <int NT>
-__device__ void stage_rows(int64_t m0, int nrows, const Epi& e, float* ts, int32_t* toks) {
+__device__ void stage_rows(int64_t m0, int nrows, const Epi& e, float* ts, int32_t* toks, float* xs = nullptr) {
   const int64_t limit = (e.mode == MODE_DENSE) ? (int64_t)dense_valid(e) : e.N;
   for (int r = threadIdx.x; r < nrows; r += NT) {
     const int64_t lr = m0 + r;
     int32_t tok = -1;
-    float tv = 0.f;
+    float tv = 0.f, sx = 0.f;
     if (lr < limit) {
       tok = (e.mode == MODE_DENSE) ? e.rows[lr] : (int32_t)lr;
       tv = e.t[tok];
+      if (xs != nullptr) sx = e.x_scale[tok];
     }
     ts[r] = tv;
     toks[r] = tok;
+    if (xs != nullptr) xs[r] = sx;
   }
 }
 
@@ -454,13 +458,22 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <class C, int MODE>
-__global__ __launch_bounds__(C::NT, C::OCC) void gate_mfma_dma(const uint16_t* __restrict__ x,
-                                                               const uint16_t* __restrict__ w, int D, int mbc,
+// FP8: x and w hold E4M3 codes (one byte per element) and each 16-byte
+// operand chunk feeds two v_mfma_f32_16x16x32_fp8_fp8 (its low and high 8
+// bytes: the k values of a stage are split between the two MFMAs the same way
+// for both operands); the epilogue scales g by the row's and the column's
+// scales. Otherwise x and w are bf16.
+template <class C, int MODE, bool FP8 = false>
+__global__ __launch_bounds__(C::NT, C::OCC) void gate_mfma_dma(const void* __restrict__ xv,
+                                                               const void* __restrict__ wv, int D, int mbc,
                                                                int ncb, Epi e) {
+  constexpr int ESZ = FP8 ? 1 : 2;  // bytes per element
+  const char* __restrict__ x = reinterpret_cast<const char*>(xv);
+  const char* __restrict__ w = reinterpret_cast<const char*>(wv);
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
   __shared__ float ts[C::BM];
   __shared__ int32_t toks[C::BM];
+  __shared__ float xs[FP8 ? C::BM : 1];  // FP8: per-row scale of x
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WGN, wn = wave % C::WGN;
   int mb_id, nb_id;
@@ -474,30 +487,31 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gate_mfma_dma(const uint16_t* _
   } else {
     mlimit = e.N;
   }
-  stage_rows<C::NT>(m0, C::BM, e, ts, toks);
+  stage_rows<C::NT>(m0, C::BM, e, ts, toks, FP8 ? xs : nullptr);
 
   // Sources of this wave's DMA groups (rows past the last token / column past
   // d_ff read row 0: never stored).
   const char* src[C::GPW];
   uint32_t grp_off[C::GPW];
   const int rin = lane >> 2, p = lane & 3;
+  const int64_t rowb = (int64_t)D * ESZ;  // bytes per operand row
 #pragma unroll
   for (int t = 0; t < C::GPW; ++t) {
     const int g = wave + C::NW * t;
-    const uint16_t* base;
+    const char* base;
     int lrow;
     if (g < C::BM / 16) {
       lrow = g * 16 + rin;
       const int64_t lr = m0 + lrow;
       int64_t tok = lr < mlimit ? lr : 0;
       if (MODE == MODE_DENSE) tok = lr < mlimit ? (int64_t)e.rows[lr] : 0;
-      base = x + tok * (int64_t)D;
+      base = x + tok * rowb;
     } else {
       const int r = (g - C::BM / 16) * 16 + rin;
       lrow = C::BM + r;
-      base = w + (int64_t)((n0 + r) < e.F ? n0 + r : 0) * D;
+      base = w + (int64_t)((n0 + r) < e.F ? n0 + r : 0) * rowb;
     }
-    src[t] = reinterpret_cast<const char*>(base) + ((p ^ dma_swz(lrow & 15)) << 4);
+    src[t] = base + ((p ^ dma_swz(lrow & 15)) << 4);
     grp_off[t] = (uint32_t)((lrow - rin) * C::ROWB);
   }
   const uint32_t lds0 =
@@ -514,7 +528,7 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gate_mfma_dma(const uint16_t* _
 #pragma unroll
     for (int j = 0; j < C::FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int KT = D / 32;
+  const int KT = (int)(rowb / 64);  // 64-byte stages
 #pragma unroll
   for (int st = 0; st < C::ST - 1; ++st)
     if (st < KT) issue(st);
@@ -544,8 +558,17 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gate_mfma_dma(const uint16_t* _
 #pragma unroll
     for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < C::FN; ++j) {
+        if constexpr (FP8) {
+          const u32x4_t av = __builtin_bit_cast(u32x4_t, af[i]), bv = __builtin_bit_cast(u32x4_t, bfr[j]);
+          const long alo = (long)(((uint64_t)av.y << 32) | av.x), ahi = (long)(((uint64_t)av.w << 32) | av.z);
+          const long blo = (long)(((uint64_t)bv.y << 32) | bv.x), bhi = (long)(((uint64_t)bv.w << 32) | bv.z);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(alo, blo, acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(ahi, bhi, acc[i][j], 0, 0, 0);
+        } else {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        }
+      }
   }
   wait_vmcnt<0>();
   lds_barrier();  // the ring is reused for the epilogue below
@@ -562,9 +585,19 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gate_mfma_dma(const uint16_t* _
           const int rbase = wm * C::WM + i * 16 - p0;
           const int cbase = wn * C::WN + j * 16 - cg * kPackCols;
           if (rbase < 0 || rbase >= C::EPI_ROWS || cbase < 0 || cbase >= kPackCols) continue;
+          if constexpr (FP8) {
+            const int col = n0 + cg * kPackCols + cbase + (lane & 15);
+            const float sw = col < e.F ? e.w_scale[col] : 0.f;
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            Gs[(rbase + 4 * (lane >> 4) + r) * GS + cbase + (lane & 15)] = acc[i][j][r];
+            for (int r = 0; r < 4; ++r) {
+              const int row = rbase + 4 * (lane >> 4) + r;
+              Gs[row * GS + cbase + (lane & 15)] = acc[i][j][r] * xs[p0 + row] * sw;
+            }
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              Gs[(rbase + 4 * (lane >> 4) + r) * GS + cbase + (lane & 15)] = acc[i][j][r];
+          }
         }
       // LDS-only barriers: the epilogue's global stores need no ordering
       // between waves, and a full __syncthreads would wait for them to finish
@@ -719,11 +752,17 @@ hipError_t launch_gate_pack(const GateArgs& a, hipStream_t s) {
   e.n_ovf = a.n_ovf;
   e.cap = a.ovf_cap;
   e.ovf_h = a.ovf_h;
+  e.x_scale = a.x_scale;
+  e.w_scale = a.w_scale;
   const int ncb = (a.F + BN - 1) / BN;
 
   // 1. GEMM (or given g) + TwELL pack epilogue
   e.mode = MODE_PACK;
-  if (a.g_in) {
+  if (a.fp8) {
+    const int mbc = (int)((a.N + GatePack::BM - 1) / GatePack::BM), nbc = (a.F + GatePack::BN - 1) / GatePack::BN;
+    TWELL_LAUNCH("gate_mfma_fp8", (gate_mfma_dma<GatePack, MODE_PACK, true>), dim3(mbc * nbc), GatePack::NT, 0, s,
+                 a.x, a.w, a.D, mbc, nbc, e);
+  } else if (a.g_in) {
     const int64_t mb = (a.N + SBM - 1) / SBM;
     if (a.is_bf16)
       TWELL_LAUNCH("pack_from_g", (pack_from_g<uint16_t, MODE_PACK>), dim3(mb * ncb), 256, 0, s, a.g_in, ncb, e);
@@ -747,7 +786,11 @@ hipError_t launch_gate_pack(const GateArgs& a, hipStream_t s) {
 
   // 3. dense activation rows of the overflow rows, same arithmetic as step 1
   e.mode = MODE_DENSE;
-  if (a.g_in) {
+  if (a.fp8) {
+    const int mbc = (a.ovf_cap + GatePack::BM - 1) / GatePack::BM, nbc = (a.F + GatePack::BN - 1) / GatePack::BN;
+    TWELL_LAUNCH("gate_mfma_fp8_rows", (gate_mfma_dma<GatePack, MODE_DENSE, true>), dim3(mbc * nbc), GatePack::NT, 0,
+                 s, a.x, a.w, a.D, mbc, nbc, e);
+  } else if (a.g_in) {
     const int64_t mb = (a.ovf_cap + SBM - 1) / SBM;
     if (a.is_bf16)
       TWELL_LAUNCH("pack_from_g_rows", (pack_from_g<uint16_t, MODE_DENSE>), dim3(mb * ncb), 256, 0, s, a.g_in, ncb, e);

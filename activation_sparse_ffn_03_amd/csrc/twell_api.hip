@@ -126,6 +126,63 @@ twell_status twell_gate_pack(const twell_dims* dims, twell_dtype dtype, const vo
   return gate_common(dims, dtype, x, w_gate_t, nullptr, t, out, g_dump, stream);
 }
 
+twell_status twell_quantize_e4m3(int64_t rows, int32_t cols, twell_dtype dtype, const void* in, uint8_t* q,
+                                 float* scale, void* stream) {
+  if (rows < 0 || cols <= 0) return fail(TWELL_ERR_INVALID_ARG, "rows must be >= 0 and cols > 0");
+  if (dtype != TWELL_BF16 && dtype != TWELL_F32) return fail(TWELL_ERR_INVALID_ARG, "dtype must be bf16 or fp32");
+  if (rows > 0x7FFFFFFFll) return fail(TWELL_ERR_UNSUPPORTED, "rows above 2^31 - 1");
+  const size_t esz = dtype == TWELL_BF16 ? 2 : 4;
+  TWELL_CHECK_PTR(in, (size_t)rows * cols * esz, "in");
+  TWELL_CHECK_PTR(q, (size_t)rows * cols, "q");
+  TWELL_CHECK_PTR(scale, (size_t)rows * 4, "scale");
+  g_last_error.clear();
+  return hip_status(twell::launch_quantize_e4m3(in, dtype == TWELL_BF16, rows, cols, q, scale, (hipStream_t)stream),
+                    "twell_quantize_e4m3");
+}
+
+twell_status twell_gate_pack_fp8(const twell_dims* dims, const uint8_t* x_q, const float* x_scale,
+                                 const uint8_t* w_q, const float* w_scale, const float* t, const twell_pack* out,
+                                 float* g_dump, void* stream) {
+  twell::Shape s;
+  twell_sizes z;
+  twell_status st = prepare(dims, TWELL_BF16, &s, &z);
+  if (st != TWELL_OK) return st;
+  if (s.D % 64 != 0) return fail(TWELL_ERR_UNSUPPORTED, "the FP8 gate needs d_model to be a multiple of 64");
+  TWELL_CHECK_PTR(x_q, (size_t)s.N * s.D, "x_q");
+  TWELL_CHECK_PTR(x_scale, (size_t)s.N * 4, "x_scale");
+  TWELL_CHECK_PTR(w_q, (size_t)s.F * s.D, "w_q");
+  TWELL_CHECK_PTR(w_scale, (size_t)s.F * 4, "w_scale");
+  TWELL_CHECK_PTR(t, (size_t)s.N * 4, "t");
+  if ((st = check_pack(out, z)) != TWELL_OK) return st;
+  if (g_dump != nullptr) TWELL_CHECK_PTR(g_dump, (size_t)s.N * s.F * 4, "g_dump");
+  if (s.N == 0) return TWELL_OK;
+  twell::GateArgs a{};
+  a.N = s.N;
+  a.D = s.D;
+  a.F = s.F;
+  a.tile_n = s.tile_n;
+  a.slots = s.slots;
+  a.n_tiles = s.n_tiles;
+  a.is_bf16 = 1;  // TwELL values and overflow rows are stored in bf16
+  a.fp8 = 1;
+  a.x = x_q;
+  a.w = w_q;
+  a.x_scale = x_scale;
+  a.w_scale = w_scale;
+  a.t = t;
+  a.vals = out->vals;
+  a.cols = out->cols;
+  a.counts = out->counts;
+  a.ovf_flag = out->ovf_flag;
+  a.ovf_rows = out->ovf_rows;
+  a.ovf_h = out->ovf_h;
+  a.n_ovf = out->n_ovf;
+  a.status = out->status;
+  a.ovf_cap = s.ovf_cap;
+  a.g_dump = g_dump;
+  return hip_status(twell::launch_gate_pack(a, (hipStream_t)stream), "twell_gate_pack_fp8");
+}
+
 twell_status twell_pack_preact(const twell_dims* dims, twell_dtype dtype, const float* g, const float* t,
                                const twell_pack* out, void* stream) {
   if (g == nullptr) return fail(TWELL_ERR_INVALID_ARG, "g is NULL");

@@ -37,9 +37,16 @@ struct GateArgs {
   uint32_t* status;
   int ovf_cap;
   float* g_dump;       // optional
+  int fp8;                // x and w hold E4M3 codes with per-row scales
+  const float* x_scale;   // fp8: [N]
+  const float* w_scale;   // fp8: [F]
 };
 
 hipError_t launch_gate_pack(const GateArgs& a, hipStream_t s);
+
+// Per-row E4M3 quantisation: q [rows][cols] codes, scale [rows] (quant.hip).
+hipError_t launch_quantize_e4m3(const void* in, int is_bf16, int64_t rows, int cols, uint8_t* q, float* scale,
+                                hipStream_t s);
 
 struct FwdArgs {
   int64_t N;

@@ -88,6 +88,10 @@ def lib() -> ctypes.CDLL:
         L.twell_gate_pack.argtypes = [pd, ctypes.c_int, vp, vp, vp, pp, vp, vp]
         L.twell_pack_preact.restype = ctypes.c_int
         L.twell_pack_preact.argtypes = [pd, ctypes.c_int, vp, vp, pp, vp]
+        L.twell_quantize_e4m3.restype = ctypes.c_int
+        L.twell_quantize_e4m3.argtypes = [ctypes.c_int64, i32, ctypes.c_int, vp, vp, vp, vp]
+        L.twell_gate_pack_fp8.restype = ctypes.c_int
+        L.twell_gate_pack_fp8.argtypes = [pd, vp, vp, vp, vp, vp, pp, vp, vp]
         L.twell_ffn_fwd.restype = ctypes.c_int
         L.twell_ffn_fwd.argtypes = [pd, ctypes.c_int, pp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.twell_route_hybrid.restype = ctypes.c_int
@@ -212,6 +216,26 @@ def gate_pack(dims: Dims, dtype: int, x, w_gate_t, t, pack: TwellPack, g_dump=No
     p = pack.struct()
     _check(lib().twell_gate_pack(ctypes.byref(dims), int(dtype), _ptr(x), _ptr(w_gate_t), _ptr(t),
                                  ctypes.byref(p), _ptr(g_dump), _stream(stream)), "twell_gate_pack")
+
+
+def quantize_e4m3(a, stream=None):
+    """Per-row FP8 E4M3 quantisation of a [rows, cols] bf16 / fp32 tensor:
+    returns (codes as a uint8 tensor, fp32 row scales)."""
+    if a.dim() != 2 or not a.is_contiguous():
+        raise ValueError("quantize_e4m3 takes a contiguous [rows, cols] tensor")
+    dt = BF16 if a.dtype == torch.bfloat16 else F32
+    q = torch.empty(a.shape, dtype=torch.uint8, device=a.device)
+    scale = torch.empty(a.shape[0], dtype=torch.float32, device=a.device)
+    _check(lib().twell_quantize_e4m3(int(a.shape[0]), int(a.shape[1]), dt, _ptr(a), _ptr(q), _ptr(scale),
+                                     _stream(stream)), "twell_quantize_e4m3")
+    return q, scale
+
+
+def gate_pack_fp8(dims: Dims, x_q, x_scale, w_q, w_scale, t, pack: TwellPack, g_dump=None, stream=None) -> None:
+    """Gate projection on FP8 operands + the TwELL pack (pack buffers of BF16)."""
+    p = pack.struct()
+    _check(lib().twell_gate_pack_fp8(ctypes.byref(dims), _ptr(x_q), _ptr(x_scale), _ptr(w_q), _ptr(w_scale),
+                                     _ptr(t), ctypes.byref(p), _ptr(g_dump), _stream(stream)), "twell_gate_pack_fp8")
 
 
 def pack_preact(dims: Dims, dtype: int, g, t, pack: TwellPack, stream=None) -> None:

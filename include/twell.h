@@ -159,6 +159,31 @@ twell_status twell_gate_pack(const twell_dims* dims, twell_dtype dtype, const vo
 twell_status twell_pack_preact(const twell_dims* dims, twell_dtype dtype, const float* g,
                                const float* t, const twell_pack* out, void* stream);
 
+/* 8-bit gate operands ("How TwELL by Sakana AI and NVIDIA Accelerates LLMs by
+ * 20% Using Unstructured Sparsity", "Long-term Impact": TwELL combined with
+ * 8-bit quantisation). Per-row FP8 E4M3 quantisation:
+ *   scale[r] = max_k |in[r,k]| / 448 in fp32 (1 for an all-zero row),
+ *   q[r,k]   = E4M3(in[r,k] / scale[r]), nearest value with ties to even,
+ *              magnitudes of 448 and above saturated to 448.
+ * in: [rows][cols] bf16 or fp32; q: [rows][cols] bytes (codes: sign bit, 4
+ * exponent bits with bias 7, 3 mantissa bits, subnormals m * 2^-9, 0x7F NaN);
+ * scale: [rows] fp32. Device pointers, 16-byte aligned; the caller owns them.
+ * Use it on x for every call and once on w_gate_t. */
+twell_status twell_quantize_e4m3(int64_t rows, int32_t cols, twell_dtype dtype, const void* in, uint8_t* q,
+                                 float* scale, void* stream);
+
+/* Stage 1 with FP8 gate operands: g[i,c] = x_scale[i] · w_scale[c] · sum_k
+ * E4M3(x_q[i,k]) · E4M3(w_q[c,k]) (products exact, fp32 accumulation on the
+ * matrix cores), then exactly the TwELL pack, overflow list and overflow rows
+ * of twell_gate_pack (recomputed by the same kernel, so bit-identical). The
+ * pack buffers are those of dtype TWELL_BF16 (twell_query_sizes with
+ * TWELL_BF16); d_model must be a multiple of 64. x_q [N][D], w_q [F][D] bytes;
+ * x_scale [N], w_scale [F] fp32 (from twell_quantize_e4m3). The up / down
+ * projection and the backward take the bf16 x and weights as before. */
+twell_status twell_gate_pack_fp8(const twell_dims* dims, const uint8_t* x_q, const float* x_scale,
+                                 const uint8_t* w_q, const float* w_scale, const float* t,
+                                 const twell_pack* out, float* g_dump, void* stream);
+
 /* Stage 2: fused up + down projection from TwELL.
  *   y_i = sum over active (i,c) of h_ic · (x_i · w_up_t[c]) · w_down[c]
  * with h read from TwELL (or from ovf_h for overflow rows); z = h·a is kept in
