@@ -6,18 +6,26 @@
 // to the row's largest magnitude / 448, elements rounded to the nearest E4M3
 // value with ties to even) is this library's reading.
 //
-// One workgroup per row: the row's largest magnitude (exact), scale =
-// max / 448 in fp32 (1 for an all-zero row), then every element x / scale
-// (IEEE fp32 division) encoded to E4M3: sign bit, 4 exponent bits with bias
-// 7, 3 mantissa bits, subnormals m * 2^-9, magnitudes of 448 and above
-// saturated to 448, NaN to 0x7F. Memory-bound: reads the row once from L2
-// after the reduction pass.
+// One wavefront per row (four rows per workgroup): the row is read once with
+// 16-byte loads and kept in registers (rows longer than 64 * 16 * kRegChunks
+// bytes re-read the rest from L2), its largest magnitude is reduced across
+// the wave, scale = max / 448 in fp32 (1 for an all-zero row, and for a row
+// holding NaN: the maximum is taken on the magnitudes' bit patterns, so NaN
+// wins it and fails the > 0 test), then every element x / scale (IEEE fp32
+// division) is encoded: sign bit, 4 exponent bits with bias 7, 3 mantissa
+// bits, subnormals m * 2^-9, magnitudes of 448 and above saturated to 448,
+// NaN to 0x7F. Rows whose width or base address does not allow 16-byte loads
+// take a scalar path with the same arithmetic. HBM-bound: 2 (bf16) or 4
+// (fp32) bytes read and 1 written per element.
 #include "twell_device.h"
 #include "twell_kernels.h"
 #include "twell_trace.h"
 
 namespace twell {
 namespace {
+
+constexpr int kRowsPerBlock = 4;
+constexpr int kRegChunks = 8;  // 16-byte chunks per lane held in registers
 
 // Nearest E4M3 code of v, ties to the even code (integer arithmetic on the
 // fp32 encoding).
@@ -41,34 +49,125 @@ __device__ __forceinline__ uint32_t e4m3_code(float v) {
   return sign | code;
 }
 
+// Element access on raw 32-bit words: bf16 packs two elements per word.
 template <typename TS>
-__global__ __launch_bounds__(256) void quantize_rows_e4m3(const TS* __restrict__ in, int64_t rows, int cols,
-                                                          uint8_t* __restrict__ q, float* __restrict__ scale) {
-  __shared__ float wmax[4];
-  const int64_t r = blockIdx.x;
-  if (r >= rows) return;
-  const TS* row = in + (size_t)r * cols;
-  float m = 0.f;
-  for (int c = threadIdx.x; c < cols; c += 256) m = fmaxf(m, fabsf(Store<TS>::load(row, c)));
+struct Words;
+template <>
+struct Words<uint16_t> {
+  static constexpr int kPerWord = 2;
+  // largest |x| bit pattern of the word, as an fp32 bit pattern
+  __device__ static uint32_t mag_bits(uint32_t w) { return max((w & 0x7FFFu) << 16, w & 0x7FFF0000u); }
+  __device__ static float elem(uint32_t w, int k) { return __uint_as_float(k ? (w & 0xFFFF0000u) : (w << 16)); }
+  __device__ static uint32_t mag_scalar(uint16_t h) { return ((uint32_t)h & 0x7FFFu) << 16; }
+  __device__ static float scalar(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+};
+template <>
+struct Words<float> {
+  static constexpr int kPerWord = 1;
+  __device__ static uint32_t mag_bits(uint32_t w) { return w & 0x7FFFFFFFu; }
+  __device__ static float elem(uint32_t w, int) { return __uint_as_float(w); }
+  __device__ static uint32_t mag_scalar(float f) { return __float_as_uint(f) & 0x7FFFFFFFu; }
+  __device__ static float scalar(float f) { return f; }
+};
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t m) {
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
-  __syncthreads();
-  m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-  const float sc = m > 0.f ? m / 448.0f : 1.0f;
-  if (threadIdx.x == 0) scale[r] = sc;
-  uint8_t* qrow = q + (size_t)r * cols;
-  // four codes per 32-bit store where the row allows it
-  if ((cols & 3) == 0) {
-    for (int c4 = threadIdx.x; c4 < cols / 4; c4 += 256) {
-      uint32_t w = 0;
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+  return m;
+}
+
+// scale of a row from the bit pattern of its largest magnitude
+__device__ __forceinline__ float row_scale(uint32_t mbits) {
+  const float m = __uint_as_float(mbits);
+  return m > 0.f ? m / 448.0f : 1.0f;  // NaN fails the test
+}
+
+template <typename TS>
+__device__ __forceinline__ void encode_chunk(const u32x4_t& v, float sc, uint8_t* dst) {
+  using W = Words<TS>;
+  if constexpr (W::kPerWord == 2) {
+    uint32_t lo = 0, hi = 0;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) w |= e4m3_code(Store<TS>::load(row, 4 * c4 + k) / sc) << (8 * k);
-      reinterpret_cast<uint32_t*>(qrow)[c4] = w;
+    for (int k = 0; k < 4; ++k) {
+      lo |= e4m3_code(W::elem(v[k >> 1], k & 1) / sc) << (8 * k);
+      hi |= e4m3_code(W::elem(v[2 + (k >> 1)], k & 1) / sc) << (8 * k);
     }
+    *reinterpret_cast<uint2*>(dst) = uint2{lo, hi};
   } else {
-    for (int c = threadIdx.x; c < cols; c += 256) qrow[c] = (uint8_t)e4m3_code(Store<TS>::load(row, c) / sc);
+    uint32_t w = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w |= e4m3_code(W::elem(v[k], 0) / sc) << (8 * k);
+    *reinterpret_cast<uint32_t*>(dst) = w;
   }
+}
+
+// 16-byte path: cols * sizeof(TS) % 16 == 0 and 16-byte aligned rows.
+template <typename TS>
+__global__ __launch_bounds__(64 * kRowsPerBlock) void quantize_rows_vec(const TS* __restrict__ in, int64_t rows,
+                                                                         int cols, uint8_t* __restrict__ q,
+                                                                         float* __restrict__ scale) {
+  using W = Words<TS>;
+  constexpr int EPC = 16 / (int)sizeof(TS);  // elements per 16-byte chunk
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (r >= rows) return;  // wave-uniform
+  const u32x4_t* row = reinterpret_cast<const u32x4_t*>(in + r * cols);
+  const int nch = cols / EPC;
+  u32x4_t v[kRegChunks];
+  uint32_t mb = 0;
+#pragma unroll
+  for (int c = 0; c < kRegChunks; ++c) {
+    const int i = lane + 64 * c;
+    v[c] = i < nch ? row[i] : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) mb = max(mb, W::mag_bits(v[c][k]));
+  }
+  for (int i = lane + 64 * kRegChunks; i < nch; i += 64) {
+    const u32x4_t t = row[i];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) mb = max(mb, W::mag_bits(t[k]));
+  }
+  const float sc = row_scale(wave_max_u32(mb));
+  if (lane == 0) scale[r] = sc;
+  uint8_t* qrow = q + r * cols;
+#pragma unroll
+  for (int c = 0; c < kRegChunks; ++c) {
+    const int i = lane + 64 * c;
+    if (i < nch) encode_chunk<TS>(v[c], sc, qrow + (size_t)i * EPC);
+  }
+  for (int i = lane + 64 * kRegChunks; i < nch; i += 64) encode_chunk<TS>(row[i], sc, qrow + (size_t)i * EPC);
+}
+
+// Any width and alignment: one element per lane per step, read twice.
+template <typename TS>
+__global__ __launch_bounds__(64 * kRowsPerBlock) void quantize_rows_scalar(const TS* __restrict__ in, int64_t rows,
+                                                                            int cols, uint8_t* __restrict__ q,
+                                                                            float* __restrict__ scale) {
+  using W = Words<TS>;
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (r >= rows) return;  // wave-uniform
+  const TS* row = in + r * cols;
+  uint32_t mb = 0;
+  for (int c = lane; c < cols; c += 64) mb = max(mb, W::mag_scalar(row[c]));
+  const float sc = row_scale(wave_max_u32(mb));
+  if (lane == 0) scale[r] = sc;
+  uint8_t* qrow = q + r * cols;
+  for (int c = lane; c < cols; c += 64) qrow[c] = (uint8_t)e4m3_code(W::scalar(row[c]) / sc);
+}
+
+template <typename TS>
+hipError_t launch_typed(const void* in, int64_t rows, int cols, uint8_t* q, float* scale, hipStream_t s) {
+  const dim3 grid((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock));
+  const int epc = 16 / (int)sizeof(TS);
+  const bool vec = cols % epc == 0 && (uintptr_t)in % 16 == 0 && (uintptr_t)q % 8 == 0;
+  if (vec)
+    TWELL_LAUNCH("quantize_e4m3", quantize_rows_vec<TS>, grid, 64 * kRowsPerBlock, 0, s, (const TS*)in, rows, cols, q,
+                 scale);
+  else
+    TWELL_LAUNCH("quantize_e4m3", quantize_rows_scalar<TS>, grid, 64 * kRowsPerBlock, 0, s, (const TS*)in, rows, cols,
+                 q, scale);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -76,13 +175,8 @@ __global__ __launch_bounds__(256) void quantize_rows_e4m3(const TS* __restrict__
 hipError_t launch_quantize_e4m3(const void* in, int is_bf16, int64_t rows, int cols, uint8_t* q, float* scale,
                                 hipStream_t s) {
   if (rows == 0) return hipSuccess;
-  if (is_bf16)
-    TWELL_LAUNCH("quantize_e4m3", quantize_rows_e4m3<uint16_t>, dim3((unsigned)rows), 256, 0, s,
-                 (const uint16_t*)in, rows, cols, q, scale);
-  else
-    TWELL_LAUNCH("quantize_e4m3", quantize_rows_e4m3<float>, dim3((unsigned)rows), 256, 0, s, (const float*)in,
-                 rows, cols, q, scale);
-  return hipGetLastError();
+  return is_bf16 ? launch_typed<uint16_t>(in, rows, cols, q, scale, s)
+                 : launch_typed<float>(in, rows, cols, q, scale, s);
 }
 
 }  // namespace twell

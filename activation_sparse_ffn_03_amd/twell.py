@@ -218,14 +218,21 @@ def gate_pack(dims: Dims, dtype: int, x, w_gate_t, t, pack: TwellPack, g_dump=No
                                  ctypes.byref(p), _ptr(g_dump), _stream(stream)), "twell_gate_pack")
 
 
-def quantize_e4m3(a, stream=None):
+def quantize_e4m3(a, stream=None, out=None):
     """Per-row FP8 E4M3 quantisation of a [rows, cols] bf16 / fp32 tensor:
-    returns (codes as a uint8 tensor, fp32 row scales)."""
+    returns (codes as a uint8 tensor, fp32 row scales), written into `out`
+    (a (codes, scales) pair of those shapes) when given."""
     if a.dim() != 2 or not a.is_contiguous():
         raise ValueError("quantize_e4m3 takes a contiguous [rows, cols] tensor")
     dt = BF16 if a.dtype == torch.bfloat16 else F32
-    q = torch.empty(a.shape, dtype=torch.uint8, device=a.device)
-    scale = torch.empty(a.shape[0], dtype=torch.float32, device=a.device)
+    if out is None:
+        q = torch.empty(a.shape, dtype=torch.uint8, device=a.device)
+        scale = torch.empty(a.shape[0], dtype=torch.float32, device=a.device)
+    else:
+        q, scale = out
+        if tuple(q.shape) != tuple(a.shape) or q.dtype != torch.uint8 or not q.is_contiguous() or \
+                tuple(scale.shape) != (a.shape[0],) or scale.dtype != torch.float32:
+            raise ValueError("out must be (uint8 [rows, cols], float32 [rows]) contiguous tensors")
     _check(lib().twell_quantize_e4m3(int(a.shape[0]), int(a.shape[1]), dt, _ptr(a), _ptr(q), _ptr(scale),
                                      _stream(stream)), "twell_quantize_e4m3")
     return q, scale
@@ -291,14 +298,22 @@ class TwellFFN:
 
     forward(): gate_pack -> ffn_fwd (with a_save when training)
     backward(): route_hybrid -> ffn_bwd
+    With fp8_gate (bf16 forward only), forward() takes the gate weight as
+    (E4M3 codes, row scales) from quantize_e4m3 and runs
+    quantize_e4m3(x) -> gate_pack_fp8 -> ffn_fwd.
     All buffers are allocated once here, with torch, on `device`.
     """
 
-    def __init__(self, dims: Dims, dtype: int, train: bool = False, device="cuda"):
-        self.dims, self.dtype, self.train = dims, dtype, train
+    def __init__(self, dims: Dims, dtype: int, train: bool = False, device="cuda", fp8_gate: bool = False):
+        if fp8_gate and (train or dtype != BF16):
+            raise ValueError("the FP8 gate is a bf16 forward path")
+        self.dims, self.dtype, self.train, self.fp8_gate = dims, dtype, train, fp8_gate
         self.sizes = query_sizes(dims, dtype)
         self.pack = alloc_pack(dims, dtype, device)
         N, D, F = dims.n_tokens, dims.d_model, dims.d_ff
+        if fp8_gate:
+            self.x_q = torch.empty((N, D), dtype=torch.uint8, device=device)
+            self.x_scale = torch.empty(N, dtype=torch.float32, device=device)
         self.y = torch.empty((N, D), dtype=torch.float32, device=device)
         self.ws_fwd = alloc_workspace(self.sizes["ws_fwd"], device)
         self.a_save = None
@@ -312,7 +327,12 @@ class TwellFFN:
             self.dw_down = torch.empty((F, D), dtype=torch.float32, device=device)
 
     def forward(self, x, w_gate_t, w_up_t, w_down, t, g_dump=None, stream=None):
-        gate_pack(self.dims, self.dtype, x, w_gate_t, t, self.pack, g_dump=g_dump, stream=stream)
+        if self.fp8_gate:
+            w_q, w_scale = w_gate_t
+            quantize_e4m3(x, stream=stream, out=(self.x_q, self.x_scale))
+            gate_pack_fp8(self.dims, self.x_q, self.x_scale, w_q, w_scale, t, self.pack, g_dump=g_dump, stream=stream)
+        else:
+            gate_pack(self.dims, self.dtype, x, w_gate_t, t, self.pack, g_dump=g_dump, stream=stream)
         ffn_fwd(self.dims, self.dtype, self.pack, x, w_up_t, w_down, self.y, a_save=self.a_save, ws=self.ws_fwd,
                 stream=stream)
         return self.y

@@ -6,8 +6,9 @@ The default workload is the 1B-class forward (4096 tokens, d_model 2048, d_ff
 5632, uniform gate density 1%): gate GEMM with the TwELL pack epilogue,
 overflow rows, and the fused up/down projection. The other workloads are
 picked with --workload: the 7B-class forward at three densities, the
-skewed-density forward, and the training step (forward saving a, hybrid
-routing and the sparse backward).
+skewed-density forward, the training step (forward saving a, hybrid
+routing and the sparse backward), and the 1B / 7B forwards with the gate
+projection on FP8 E4M3 operands (x quantised per step, W_gate once).
 
 Prints ONE JSON line: throughput in tokens/s, the dense bf16 FFN on the same
 GPU and inputs as reference, the roofline of the dominant kernel (device time
@@ -28,16 +29,19 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, published
+MFMA_FP8_PEAK_TFS = 5000.0   # MI355X dense fp8 MFMA, published
 METRIC = "sparse FFN tokens/s and speedup vs dense bf16 FFN; HBM GB/s / MFMA % of peak"
 
 WORKLOADS = {
-    # name: (config, density override, train)
-    "c5": ("c5", None, True),
-    "c2": ("c2", None, False),
-    "c3_5": ("c3", 0.05, False),
-    "c3_1": ("c3", 0.01, False),
-    "c3_05": ("c3", 0.005, False),
-    "c4": ("c4", None, False),
+    # name: (config, density override, train, FP8 gate)
+    "c5": ("c5", None, True, False),
+    "c2": ("c2", None, False, False),
+    "c3_5": ("c3", 0.05, False, False),
+    "c3_1": ("c3", 0.01, False, False),
+    "c3_05": ("c3", 0.005, False, False),
+    "c4": ("c4", None, False, False),
+    "c2_fp8": ("c2", None, False, True),
+    "c3_1_fp8": ("c3", 0.01, False, True),
 }
 
 
@@ -60,11 +64,11 @@ def capacities(w, train):
     return max(64, w.N // 8), (max(64, w.N // 8) if train else 0)
 
 
-def describe(w, train):
+def describe(w, train, fp8=False):
     dens = w.density
     d = f"uniform {dens[1] * 100:g}%" if dens[0] == "uniform" else \
         f"lognormal mean {dens[1] * 100:g}% sigma {dens[2]:g} clip [{dens[3] * 100:g}%, {dens[4] * 100:g}%]"
-    kind = "training step (fwd + route + bwd)" if train else "forward"
+    kind = "training step (fwd + route + bwd)" if train else ("forward, FP8 E4M3 gate" if fp8 else "forward")
     return f"{kind}: {w.N} tokens x d_model {w.D} x d_ff {w.F}, T_n {w.tile_n}, S {w.slots}, density {d}"
 
 
@@ -74,7 +78,13 @@ def kernel_work(name, w, st, train):
     nnz, nnz_ell, n_t = st["nnz"], st["nnz_ell"], w.n_tiles
     if name == "gate_mfma_bf16":
         twell = n_t * w.slots * N * (e + 2) + n_t * N * 2
-        return {"flops": 2.0 * N * D * F, "bytes": N * D * e + F * D * e + twell, "bound": "mfma"}
+        return {"flops": 2.0 * N * D * F, "bytes": N * D * e + F * D * e + twell, "bound": "mfma", "peak": "bf16"}
+    if name == "gate_mfma_fp8":   # one-byte operands and their row scales; TwELL written in bf16
+        twell = n_t * w.slots * N * (e + 2) + n_t * N * 2
+        return {"flops": 2.0 * N * D * F, "bytes": N * D + F * D + 4 * (N + F) + twell, "bound": "mfma",
+                "peak": "fp8"}
+    if name == "quantize_e4m3":   # x read (bf16), codes and scales written
+        return {"flops": 0.0, "bytes": N * D * e + N * D + 4 * N, "bound": "hbm"}
     if name == "ffn_up_kernel":   # x, W_up once; TwELL read; z (and a when training) written
         byt = N * D * e + F * D * e + nnz * (e + 2) + n_t * N * 2 + nnz * 4 + (nnz * 4 if train else 0)
         return {"flops": 2.0 * D * nnz, "bytes": byt, "bound": "hbm"}
@@ -99,7 +109,7 @@ def kernel_work(name, w, st, train):
     return None
 
 
-def cpu_baseline(w, train, sample, budget_s=10.0):
+def cpu_baseline(w, train, sample, budget_s=10.0, fp8=False):
     """The oracle, as it stands, on successive windows of `sample` tokens of the
     same workload (full d_model / d_ff), repeated until about `budget_s` seconds
     of CPU work have been done; returns the oracle's tokens/s."""
@@ -112,14 +122,23 @@ def cpu_baseline(w, train, sample, budget_s=10.0):
         blas_threads = None
     cores = len(os.sched_getaffinity(0))
     n = max(1, min(sample, w.N))
+    if fp8:
+        wq, wsc = orc.quantize_rows_e4m3(w.w_gate_t)   # once, as on the GPU
     done, windows = 0, 0
     t0 = time.perf_counter()
     while True:
         lo = (windows * n) % w.N
         rows = np.arange(lo, min(lo + n, w.N))
         x, t = w.x[rows], w.t[rows]
-        fw = orc.ffn_forward(x, w.w_gate_t, w.w_up_t, w.w_down, t, store=w.dtype)
-        pk = orc.pack(fw["g"], t, w.tile_n, w.slots, store=w.dtype, arith="f32")
+        if fp8:
+            xq, xsc = orc.quantize_rows_e4m3(x)
+            g = orc.gate_preact_fp8(xq, xsc, wq, wsc)
+            pk = orc.pack(g, t, w.tile_n, w.slots, store=w.dtype, arith="f32")
+            hq = orc.dense_activation(g, t, store=w.dtype, arith="f32")
+            orc.sparse_forward(pk, x, w.w_up_t, w.w_down, ovf_h=hq[pk["ovf_rows"]])
+        else:
+            fw = orc.ffn_forward(x, w.w_gate_t, w.w_up_t, w.w_down, t, store=w.dtype)
+            pk = orc.pack(fw["g"], t, w.tile_n, w.slots, store=w.dtype, arith="f32")
         if train:
             orc.route(pk, w.row_cap, a=fw["a"], ovf_h=fw["hq"][pk["ovf_rows"]])
             orc.ffn_backward(x, w.dy[rows], w.w_gate_t, w.w_up_t, w.w_down, fw["mask"], fw["hq"], w.lam)
@@ -130,7 +149,8 @@ def cpu_baseline(w, train, sample, budget_s=10.0):
     dt = time.perf_counter() - t0
     return {"value": done / dt, "unit": "tokens/s", "cores": blas_threads or cores, "kind": "oracle",
             "sample": f"{windows} windows of {n} tokens ({done} tokens) of the same workload, full d_model/d_ff, "
-                      f"fp64 NumPy, {'forward + pack + route + backward' if train else 'forward + pack'}; "
+                      f"fp64 NumPy, {'forward + pack + route + backward' if train else 'forward + pack'}"
+                      f"{' with FP8 quantisation of x and the FP8 gate' if fp8 else ''}; "
                       f"{dt:.1f} s wall; BLAS threads {blas_threads}, host affinity {cores} cores"}
 
 
@@ -138,6 +158,7 @@ def cpu_baseline(w, train, sample, budget_s=10.0):
 # summary of a kernel is only used while these files are unchanged.
 KERNEL_SOURCES = {
     "gate_mfma_bf16": ["gate_pack.hip", "twell_device.h"],
+    "gate_mfma_fp8": ["gate_pack.hip", "twell_device.h"],
     "ffn_up_kernel": ["fused_fwd.hip", "row_ops.h", "twell_device.h"],
     "ffn_down_kernel": ["fused_fwd.hip", "row_ops.h", "twell_device.h"],
     "bwd_dz_ell": ["bwd.hip", "row_ops.h", "twell_device.h"],
@@ -206,9 +227,9 @@ def main():
         copy_calibration()
         return
     tw.lib()
-    cfg, dens, train = WORKLOADS[args.workload]
+    cfg, dens, train, fp8 = WORKLOADS[args.workload]
     w = make_inputs(cfg, density=dens)
-    print(f"[bench] workload {args.workload}: {describe(w, train)}", file=sys.stderr, flush=True)
+    print(f"[bench] workload {args.workload}: {describe(w, train, fp8)}", file=sys.stderr, flush=True)
     dev = torch.device("cuda:0")
 
     def up(a):
@@ -219,10 +240,11 @@ def main():
     dy = up(w.dy) if train else None
     ovf_cap, dense_cap = capacities(w, train)
     dims = tw.make_dims(w.N, w.D, w.F, w.tile_n, w.slots, w.row_cap if train else 0, ovf_cap, dense_cap)
-    ffn = tw.TwellFFN(dims, tw.BF16, train=train)
+    ffn = tw.TwellFFN(dims, tw.BF16, train=train, fp8_gate=fp8)
+    wgate = tw.quantize_e4m3(wg) if fp8 else wg   # the weight's codes and scales: once, outside the step
 
     def step():
-        ffn.forward(x, wg, wu, wd, t)
+        ffn.forward(x, wgate, wu, wd, t)
         if train:
             ffn.backward(x, dy, wg, wu, wd, w.lam)
 
@@ -270,8 +292,9 @@ def main():
     sec = kernels[dom]["avg_ms"] / 1e3
     if wk["bound"] == "mfma":
         ach = wk["flops"] / sec / 1e12
-        roof = {"bound": "mfma", "achieved": ach, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
-                "frac": ach / MFMA_BF16_PEAK_TFS, "traffic": measured_traffic(dom, args.workload), "kernel": dom}
+        peak = MFMA_FP8_PEAK_TFS if wk["peak"] == "fp8" else MFMA_BF16_PEAK_TFS
+        roof = {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s",
+                "frac": ach / peak, "traffic": measured_traffic(dom, args.workload), "kernel": dom}
     else:
         ach = wk["bytes"] / sec / 1e9
         roof = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -353,9 +376,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8 e4m3 gate, bf16" if fp8 else "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{args.workload}: {describe(w, train)}", "n_tokens": w.N, "d_model": w.D,
+        "config": {"workload": f"{args.workload}: {describe(w, train, fp8)}", "n_tokens": w.N, "d_model": w.D,
                    "d_ff": w.F, "tile_n": w.tile_n, "slots": w.slots, "row_cap": w.row_cap if train else 0,
                    "parallelism": "none (1 GPU)"},
         "speedup_vs_dense": (dense / ms) if dense else None,
@@ -369,7 +392,7 @@ def main():
         "wall_s_timed": wall,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, train, args.cpu_sample, args.cpu_budget)
+        out["cpu_baseline"] = cpu_baseline(w, train, args.cpu_sample, args.cpu_budget, fp8)
     print(json.dumps(out), flush=True)
 
 

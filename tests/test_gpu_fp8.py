@@ -27,17 +27,18 @@ pytestmark = pytest.mark.gpu
 def fp8_gate_err_bound(xq, sx, wq, sw, g):
     """Bound on |g_gpu - g| for the FP8 gate, elementwise.
 
-    v_mfma_f32_16x16x32_fp8_fp8 sums the 8 products each lane supplies (8
-    consecutive k here) in fixed point aligned to the largest of them and
-    drops what falls below the grid 2^(E - 14), E = floor(log2 of that
-    product) (measured on gfx950: 448*448 + 20 at k = 0, 1 gives 448*448 + 16,
-    while at k = 0, 8 the sum is the fp32-rounded one); the group sums and the
-    accumulator are added in fp32. The bound takes the grid one bit coarser,
-    G = 2^(E - 13), which also covers a grid tied to the exponent sum of the
-    operands, and allows per group the products' remainders on G (a
-    per-product truncation) plus G (a truncation of the group sum); the fp32
-    additions add at most 5 ulps of the running sum per instruction, and the
-    epilogue's two scale multiplications 2 ulps of g.
+    On gfx950, v_mfma_f32_16x16x32_fp8_fp8 sums the 8 bytes each lane
+    supplies (8 consecutive k in this kernel's layout) in fixed point: every
+    product is truncated toward zero on the grid 2^(E - 14), E = floor(log2)
+    of the group's largest product (measured: 448*448 + 20 in one group gives
+    448*448 + 16, 448*448 - 5 gives 448*448, and products in different groups
+    add with fp32 rounding). The group sums and the accumulator are added in
+    fp32. The bound takes the grid one bit coarser, G = 2^(E - 13), which also
+    covers a grid tied to the exponent sum of the operands, and allows per
+    group the products' remainders on G plus G (a truncation of the group sum
+    instead); the fp32 additions, one per group and one per instruction,
+    add at most 5 ulps of the running sum per 32 k; the
+    epilogue's two scale multiplications add 2 ulps of g.
     """
     qx = orc.e4m3_decode(xq)
     qw = orc.e4m3_decode(wq)
@@ -74,23 +75,48 @@ def _bf16_exact(a):
     return orc.round_bf16(np.asarray(a, dtype=np.float64)).astype(np.float32)
 
 
-@pytest.mark.parametrize("dtype,cols", [("bf16", 1024), ("bf16", 999), ("f32", 640)])
+@pytest.mark.parametrize("dtype,cols", [
+    ("bf16", 1024),   # 16-byte loads, row held in registers
+    ("bf16", 5120),   # 16-byte loads, rest of the row re-read
+    ("f32", 640),
+    ("f32", 3000),    # 16-byte loads, rest of the row re-read
+    ("bf16", 999),    # width without 16-byte chunks: one element per lane
+    ("f32", 1023),
+])
 def test_quantize_e4m3_bit_exact(dtype, cols):
     require_gpu()
     rng = np.random.default_rng(11)
-    a = (rng.standard_normal((41, cols)) * np.exp2(rng.integers(-20, 12, (41, 1)))).astype(np.float32)
-    a[3] = 0.0
-    a[7, 5] = 1e-30  # far below the smallest code of its row
+    rows = 41
+    a = (rng.standard_normal((rows, cols)) * np.exp2(rng.integers(-20, 12, (rows, 1)))).astype(np.float32)
     if dtype == "bf16":
         a = _bf16_exact(a)
-        dev = torch.from_numpy(a).cuda().to(torch.bfloat16)
-    else:
-        dev = torch.from_numpy(a).cuda()
+    # special values (each exact in bf16)
+    a[3] = 0.0
+    a[7, 5] = 2.0 ** -100  # far below the smallest code of its row
+    a[9, 17] = np.nan      # scale 1, NaN -> 0x7F, the rest saturates or rounds
+    a[11, 2] = np.inf      # scale inf: finite elements -> +-0, inf -> 0x7F
+    a[13] = -0.0           # sign of zero kept
+    a[13, 1] = 0.0
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    dev = torch.from_numpy(a).cuda().to(tdt)
     q, s = tw.quantize_e4m3(dev)
     torch.cuda.synchronize()
-    rq, rs = orc.quantize_rows_e4m3(a)
+    with np.errstate(invalid="ignore"):
+        rq, rs = orc.quantize_rows_e4m3(a)
     np.testing.assert_array_equal(s.cpu().numpy(), rs)
     np.testing.assert_array_equal(q.cpu().numpy(), rq)
+
+
+def test_quantize_e4m3_rejects_misaligned_rows():
+    """Inputs must start on a 16-byte boundary: an error, and nothing written."""
+    require_gpu()
+    buf = torch.zeros(64 * 8 + 1, dtype=torch.bfloat16, device="cuda")
+    q = torch.full((64, 8), 0x55, dtype=torch.uint8, device="cuda")
+    sc = torch.full((64,), 7.0, dtype=torch.float32, device="cuda")
+    with pytest.raises(tw.TwellError):
+        tw.quantize_e4m3(buf[1:].view(64, 8), out=(q, sc))
+    torch.cuda.synchronize()
+    assert bool((q == 0x55).all()) and bool((sc == 7.0).all())
 
 
 def _grid_codes(rng, shape):
@@ -192,3 +218,33 @@ def test_forward_with_fp8_gate():
     np.testing.assert_array_equal(f64(pack.ovf_h[:n]), hq[pk["ovf_rows"][:n]])
     y_ref = orc.sparse_forward(pk, x, wu, wd, ovf_h=hq[pk["ovf_rows"]])
     rowwise_ok(f64(y), y_ref, 1e-4, "y (fp8 gate)")
+
+
+def test_runner_fp8_gate_matches_calls():
+    """TwellFFN(fp8_gate=True) runs quantisation, FP8 gate + pack and the
+    forward into its own buffers: y equal to the oracle on exact rows."""
+    require_gpu()
+    rng = np.random.default_rng(41)
+    N, D, F = 300, 256, 1024
+    x = _fp8_exact_rows(rng, N, D, -8, -4)
+    wg = _fp8_exact_rows(rng, F, D, -12, -8)
+    wu = _bf16_exact(rng.standard_normal((F, D)) / np.sqrt(D))
+    wd = _bf16_exact(rng.standard_normal((F, D)) / np.sqrt(F))
+    rxq, rsx = orc.quantize_rows_e4m3(x)
+    rwq, rsw = orc.quantize_rows_e4m3(wg)
+    g = orc.gate_preact_fp8(rxq, rsx, rwq, rsw)
+    t = orc.margin_thresholds(g, 0.03)
+    cu = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    dims = tw.make_dims(N, D, F, 128, 4, 0, N, 0)
+    ffn = tw.TwellFFN(dims, tw.BF16, fp8_gate=True)
+    wgate = tw.quantize_e4m3(cu(wg).to(torch.bfloat16))
+    xb = cu(x).to(torch.bfloat16)
+    for _ in range(2):   # the second call reuses every buffer
+        y = ffn.forward(xb, wgate, cu(wu).to(torch.bfloat16), cu(wd).to(torch.bfloat16), cu(t))
+        torch.cuda.synchronize()
+        pk = orc.pack(g, t, 128, 4, store="bf16", arith="f32")
+        check_pack(ffn.pack, pk, N)
+        hq = orc.dense_activation(g, t, store="bf16", arith="f32")
+        rowwise_ok(f64(y), orc.sparse_forward(pk, x, wu, wd, ovf_h=hq[pk["ovf_rows"]]), 1e-4, "y (runner)")
+    with pytest.raises(ValueError):
+        tw.TwellFFN(dims, tw.F32, fp8_gate=True)
