@@ -20,6 +20,7 @@
 //                    (the ascending list is built by launch_compact).
 // The same kernels, with MODE_DENSE, recompute the dense activation rows of
 // the overflow rows with identical arithmetic (gathered A rows).
+#include "../../include/twell.h"
 #include "twell_device.h"
 #include "twell_kernels.h"
 #include "twell_trace.h"
@@ -51,6 +52,12 @@ struct Epi {
   void* ovf_h;           // MODE_DENSE: [cap][F]
   const float* x_scale;  // FP8 operands: per-token scale of x (else null)
   const float* w_scale;  // FP8 operands: per-unit scale of w_gate_t (else null)
+  // No row can overflow (slots >= tile_n): workgroup 0 of the pack writes the
+  // all-zero overflow outputs itself, in place of the flag and compaction
+  // kernels (else null).
+  uint8_t* clear_flag;
+  int32_t* clear_n_ovf;
+  uint32_t* clear_status;
 };
 
 __device__ __forceinline__ uint64_t mask_below(int n) { return n >= 64 ? ~0ull : ((1ull << n) - 1ull); }
@@ -707,6 +714,13 @@ __global__ __launch_bounds__(256) void pack_from_g(const float* __restrict__ g, 
     if (m0 >= mlimit) return;
   }
   stage_rows<256>(m0, SBM, e, ts, toks);
+  if (MODE == MODE_PACK && e.clear_flag != nullptr && blockIdx.x == 0) {
+    for (int64_t i = tid; i < e.N; i += 256) e.clear_flag[i] = 0;
+    if (tid == 0) {
+      *e.clear_n_ovf = 0;
+      *e.clear_status = 0u;
+    }
+  }
   for (int q = tid; q < SBM * BN; q += 256) {
     const int row = q / BN, col = q % BN;
     const int64_t lr = m0 + row;
@@ -719,6 +733,83 @@ __global__ __launch_bounds__(256) void pack_from_g(const float* __restrict__ g, 
   }
   __syncthreads();
   pack_epilogue<TS, 4>(Gs, SBM, m0, n0, e, ts, toks);
+}
+
+// ---------------------------------------------------------------- small batches
+
+// Gate pre-activation of at most kSmallN tokens, written to g [N][F] fp32 for
+// pack_from_g. A workgroup owns 16 hidden units and its 8 waves split d_model
+// into 8 ranges of 32-wide k steps. Each wave issues the W_gate loads of
+// kGemvBatch steps (16 rows x 64 bytes each) before their MFMAs, so the weight
+// streams from HBM with enough bytes in flight although the grid has only
+// F / 16 workgroups; x is small and read from L2. A wave runs the 16x16x32
+// bf16 MFMA over its range in ascending k, and the 8 partial sums are added
+// in wave order through LDS: deterministic, but g may differ in its last bits
+// from the large-batch GEMM's single chain over d_model. Tokens past N read
+// zeros; columns past F read row F - 1 and are never stored.
+constexpr int kSmallN = TWELL_SMALL_BATCH_MAX;
+constexpr int kGemvWaves = 8;
+constexpr int kGemvBatch = 8;
+
+template <int NF>
+__global__ __launch_bounds__(64 * kGemvWaves) void gate_gemv_small(const uint16_t* __restrict__ x,
+                                                                    const uint16_t* __restrict__ w, int64_t N,
+                                                                    int D, int F, float* __restrict__ g) {
+  __shared__ f32x4_t part[kGemvWaves][NF][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = blockIdx.x * 16 + (lane & 15);
+  const int ke = (lane >> 4) * 8;  // element offset of this lane's 16 bytes in a 32-wide k step
+  const int S = D / 32;
+  const int s_lo = S * wave / kGemvWaves, s_hi = S * (wave + 1) / kGemvWaves;
+  const uint16_t* wrow = w + (size_t)(col < F ? col : F - 1) * D + ke;
+  const uint16_t* xrow[NF];
+  bool xok[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    const int tok = 16 * f + (lane & 15);
+    xok[f] = tok < N;
+    xrow[f] = x + (size_t)(xok[f] ? tok : 0) * D + ke;
+  }
+  f32x4_t acc[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) acc[f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const u32x4_t zero{0u, 0u, 0u, 0u};
+  for (int s0 = s_lo; s0 < s_hi; s0 += kGemvBatch) {
+    u32x4_t b[kGemvBatch], a[kGemvBatch][NF];
+#pragma unroll
+    for (int j = 0; j < kGemvBatch; ++j)
+      b[j] = s0 + j < s_hi ? *reinterpret_cast<const u32x4_t*>(wrow + (size_t)(s0 + j) * 32) : zero;
+#pragma unroll
+    for (int j = 0; j < kGemvBatch; ++j)
+#pragma unroll
+      for (int f = 0; f < NF; ++f)
+        a[j][f] = (s0 + j < s_hi && xok[f]) ? *reinterpret_cast<const u32x4_t*>(xrow[f] + (size_t)(s0 + j) * 32)
+                                             : zero;
+#pragma unroll
+    for (int j = 0; j < kGemvBatch; ++j) {
+      if (s0 + j >= s_hi) break;  // wave-uniform
+#pragma unroll
+      for (int f = 0; f < NF; ++f)
+        acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[j][f]),
+                                                         __builtin_bit_cast(bf16x8_t, b[j]), acc[f], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int f = 0; f < NF; ++f) part[wave][f][lane] = acc[f];
+  __syncthreads();
+  if (wave < NF) {
+    const int f = wave;
+    f32x4_t sum = part[0][f][lane];
+#pragma unroll
+    for (int p = 1; p < kGemvWaves; ++p) sum += part[p][f][lane];
+    if (col < F) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t tok = 16 * f + 4 * (lane >> 4) + r;
+        if (tok < N) g[tok * F + col] = sum[r];
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------- overflow rows
@@ -756,18 +847,45 @@ hipError_t launch_gate_pack(const GateArgs& a, hipStream_t s) {
   e.w_scale = a.w_scale;
   const int ncb = (a.F + BN - 1) / BN;
 
+  // Small batches (bf16, a g buffer given): g from the split GEMV, then the
+  // pack and the overflow rows both read that g.
+  const float* g_in = a.g_in;
+  if (!a.fp8 && g_in == nullptr && a.is_bf16 && a.N <= kSmallN && (a.g_ws != nullptr || a.g_dump != nullptr)) {
+    float* gb = a.g_dump != nullptr ? a.g_dump : a.g_ws;
+    const dim3 grid((unsigned)((a.F + 15) / 16));
+    const auto* xb = (const uint16_t*)a.x;
+    const auto* wb = (const uint16_t*)a.w;
+    switch ((a.N + 15) / 16) {
+      case 1: TWELL_LAUNCH("gate_gemv_small", gate_gemv_small<1>, grid, 64 * kGemvWaves, 0, s, xb, wb, a.N, a.D, a.F, gb); break;
+      case 2: TWELL_LAUNCH("gate_gemv_small", gate_gemv_small<2>, grid, 64 * kGemvWaves, 0, s, xb, wb, a.N, a.D, a.F, gb); break;
+      case 3: TWELL_LAUNCH("gate_gemv_small", gate_gemv_small<3>, grid, 64 * kGemvWaves, 0, s, xb, wb, a.N, a.D, a.F, gb); break;
+      default: TWELL_LAUNCH("gate_gemv_small", gate_gemv_small<4>, grid, 64 * kGemvWaves, 0, s, xb, wb, a.N, a.D, a.F, gb); break;
+    }
+    g_in = gb;
+    e.g_dump = nullptr;  // g is already in the caller's g_dump, or not asked for
+  }
+  // With slots >= tile_n no tile can overflow: the pack from g clears the
+  // overflow outputs and the flag, compaction and overflow-row steps are
+  // skipped (their results would be all zero).
+  const bool no_ovf = g_in != nullptr && a.slots >= a.tile_n;
+  if (no_ovf) {
+    e.clear_flag = a.ovf_flag;
+    e.clear_n_ovf = a.n_ovf;
+    e.clear_status = a.status;
+  }
+
   // 1. GEMM (or given g) + TwELL pack epilogue
   e.mode = MODE_PACK;
   if (a.fp8) {
     const int mbc = (int)((a.N + GatePack::BM - 1) / GatePack::BM), nbc = (a.F + GatePack::BN - 1) / GatePack::BN;
     TWELL_LAUNCH("gate_mfma_fp8", (gate_mfma_dma<GatePack, MODE_PACK, true>), dim3(mbc * nbc), GatePack::NT, 0, s,
                  a.x, a.w, a.D, mbc, nbc, e);
-  } else if (a.g_in) {
+  } else if (g_in) {
     const int64_t mb = (a.N + SBM - 1) / SBM;
     if (a.is_bf16)
-      TWELL_LAUNCH("pack_from_g", (pack_from_g<uint16_t, MODE_PACK>), dim3(mb * ncb), 256, 0, s, a.g_in, ncb, e);
+      TWELL_LAUNCH("pack_from_g", (pack_from_g<uint16_t, MODE_PACK>), dim3(mb * ncb), 256, 0, s, g_in, ncb, e);
     else
-      TWELL_LAUNCH("pack_from_g", (pack_from_g<float, MODE_PACK>), dim3(mb * ncb), 256, 0, s, a.g_in, ncb, e);
+      TWELL_LAUNCH("pack_from_g", (pack_from_g<float, MODE_PACK>), dim3(mb * ncb), 256, 0, s, g_in, ncb, e);
   } else if (a.is_bf16) {
     const int mbc = (int)((a.N + GatePack::BM - 1) / GatePack::BM), nbc = (a.F + GatePack::BN - 1) / GatePack::BN;
     TWELL_LAUNCH("gate_mfma_bf16", (gate_mfma_dma<GatePack, MODE_PACK>), dim3(mbc * nbc), GatePack::NT, 0, s,
@@ -777,7 +895,7 @@ hipError_t launch_gate_pack(const GateArgs& a, hipStream_t s) {
     TWELL_LAUNCH("gate_simt_f32", gate_simt_f32<MODE_PACK>, dim3(mb * ncb), 256, 0, s, (const float*)a.x, (const float*)a.w, a.D, ncb, e);
   }
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  if (err != hipSuccess || no_ovf) return err;
 
   // 2. overflow rows from the true counts
   TWELL_LAUNCH("ovf_flags", ovf_flags, dim3((a.N + 63) / 64), 64, 0, s, a.counts, a.N, a.n_tiles, a.slots, a.ovf_flag);
@@ -790,12 +908,12 @@ hipError_t launch_gate_pack(const GateArgs& a, hipStream_t s) {
     const int mbc = (a.ovf_cap + GatePack::BM - 1) / GatePack::BM, nbc = (a.F + GatePack::BN - 1) / GatePack::BN;
     TWELL_LAUNCH("gate_mfma_fp8_rows", (gate_mfma_dma<GatePack, MODE_DENSE, true>), dim3(mbc * nbc), GatePack::NT, 0,
                  s, a.x, a.w, a.D, mbc, nbc, e);
-  } else if (a.g_in) {
+  } else if (g_in) {
     const int64_t mb = (a.ovf_cap + SBM - 1) / SBM;
     if (a.is_bf16)
-      TWELL_LAUNCH("pack_from_g_rows", (pack_from_g<uint16_t, MODE_DENSE>), dim3(mb * ncb), 256, 0, s, a.g_in, ncb, e);
+      TWELL_LAUNCH("pack_from_g_rows", (pack_from_g<uint16_t, MODE_DENSE>), dim3(mb * ncb), 256, 0, s, g_in, ncb, e);
     else
-      TWELL_LAUNCH("pack_from_g_rows", (pack_from_g<float, MODE_DENSE>), dim3(mb * ncb), 256, 0, s, a.g_in, ncb, e);
+      TWELL_LAUNCH("pack_from_g_rows", (pack_from_g<float, MODE_DENSE>), dim3(mb * ncb), 256, 0, s, g_in, ncb, e);
   } else if (a.is_bf16) {
     auto rows = [&](auto cfg) {
       using R = decltype(cfg);

@@ -79,11 +79,15 @@ twell_status twell_query_sizes(const twell_dims* dims, twell_dtype dtype, twell_
 
 static twell_status gate_common(const twell_dims* dims, twell_dtype dtype, const void* x, const void* w_gate_t,
                                 const float* g_in, const float* t, const twell_pack* out, float* g_dump,
-                                void* stream) {
+                                void* ws, size_t ws_bytes, bool use_ws, void* stream) {
   twell::Shape s;
   twell_sizes z;
   twell_status st = prepare(dims, dtype, &s, &z);
   if (st != TWELL_OK) return st;
+  if (use_ws && z.ws_gate > 0) {
+    if (ws_bytes < z.ws_gate) return fail(TWELL_ERR_WORKSPACE, "gate workspace smaller than twell_sizes.ws_gate");
+    TWELL_CHECK_PTR(ws, z.ws_gate, "ws");
+  }
   const size_t xd = (size_t)s.N * s.D * s.esz, wd = (size_t)s.F * s.D * s.esz;
   if (g_in == nullptr) {
     TWELL_CHECK_PTR(x, xd, "x");
@@ -118,12 +122,19 @@ static twell_status gate_common(const twell_dims* dims, twell_dtype dtype, const
   a.status = out->status;
   a.ovf_cap = s.ovf_cap;
   a.g_dump = g_dump;
+  a.g_ws = (use_ws && z.ws_gate > 0) ? static_cast<float*>(ws) : nullptr;
   return hip_status(twell::launch_gate_pack(a, (hipStream_t)stream), "twell_gate_pack");
 }
 
 twell_status twell_gate_pack(const twell_dims* dims, twell_dtype dtype, const void* x, const void* w_gate_t,
                              const float* t, const twell_pack* out, float* g_dump, void* stream) {
-  return gate_common(dims, dtype, x, w_gate_t, nullptr, t, out, g_dump, stream);
+  return gate_common(dims, dtype, x, w_gate_t, nullptr, t, out, g_dump, nullptr, 0, false, stream);
+}
+
+twell_status twell_gate_pack_ws(const twell_dims* dims, twell_dtype dtype, const void* x, const void* w_gate_t,
+                                const float* t, const twell_pack* out, float* g_dump, void* ws, size_t ws_bytes,
+                                void* stream) {
+  return gate_common(dims, dtype, x, w_gate_t, nullptr, t, out, g_dump, ws, ws_bytes, true, stream);
 }
 
 twell_status twell_quantize_e4m3(int64_t rows, int32_t cols, twell_dtype dtype, const void* in, uint8_t* q,
@@ -186,7 +197,7 @@ twell_status twell_gate_pack_fp8(const twell_dims* dims, const uint8_t* x_q, con
 twell_status twell_pack_preact(const twell_dims* dims, twell_dtype dtype, const float* g, const float* t,
                                const twell_pack* out, void* stream) {
   if (g == nullptr) return fail(TWELL_ERR_INVALID_ARG, "g is NULL");
-  return gate_common(dims, dtype, nullptr, nullptr, g, t, out, nullptr, stream);
+  return gate_common(dims, dtype, nullptr, nullptr, g, t, out, nullptr, nullptr, 0, false, stream);
 }
 
 twell_status twell_ffn_fwd(const twell_dims* dims, twell_dtype dtype, const twell_pack* pack, const void* x,
@@ -223,7 +234,7 @@ twell_status twell_ffn_fwd(const twell_dims* dims, twell_dtype dtype, const twel
   a.ovf_rows = pack->ovf_rows;
   a.ovf_h = pack->ovf_h;
   a.n_ovf = pack->n_ovf;
-  a.ovf_cap = s.ovf_cap;
+  a.ovf_cap = s.slots >= s.tile_n ? 0 : s.ovf_cap;  // slots >= tile_n: no row can overflow
   a.x = x;
   a.w_up = w_up_t;
   a.w_down = w_down;

@@ -153,6 +153,7 @@ void compute_sizes(const Shape& s, twell_sizes* o) {
   o->a_save = nt * S * N * 4;
   o->ws_fwd = fwd_ws_bytes(s);
   o->ws_bwd = bwd_layout(s).total;
+  o->ws_gate = (s.esz == 2 && N > 0 && N <= TWELL_SMALL_BATCH_MAX) ? N * F * 4 : 0;
 }
 
 }  // namespace twell

@@ -28,8 +28,9 @@ _STATUS = {0: "TWELL_OK", 1: "TWELL_ERR_INVALID_ARG", 2: "TWELL_ERR_UNSUPPORTED"
 
 # Every symbol include/twell.h declares.
 EXPORTS = ("twell_status_str", "twell_last_error", "twell_n_tiles", "twell_query_sizes", "twell_gate_pack",
-           "twell_pack_preact", "twell_ffn_fwd", "twell_route_hybrid", "twell_ffn_bwd", "twell_trace_start",
-           "twell_trace_stop", "twell_trace_count", "twell_trace_dropped", "twell_trace_get")
+           "twell_gate_pack_ws", "twell_pack_preact", "twell_quantize_e4m3", "twell_gate_pack_fp8", "twell_ffn_fwd",
+           "twell_route_hybrid", "twell_ffn_bwd", "twell_trace_start", "twell_trace_stop", "twell_trace_count",
+           "twell_trace_dropped", "twell_trace_get")
 
 
 class TwellError(RuntimeError):
@@ -57,7 +58,7 @@ class Hybrid(ctypes.Structure):
 
 _SIZE_FIELDS = ("vals", "cols", "counts", "ovf_flag", "ovf_rows", "ovf_h", "n_ovf", "status", "ell_vals",
                 "ell_cols", "ell_a", "row_nnz", "is_dense", "dense_rows", "dense_h", "n_dense", "a_save",
-                "ws_fwd", "ws_bwd")
+                "ws_fwd", "ws_bwd", "ws_gate")
 
 
 class Sizes(ctypes.Structure):
@@ -86,6 +87,8 @@ def lib() -> ctypes.CDLL:
         L.twell_query_sizes.argtypes = [pd, ctypes.c_int, ctypes.POINTER(Sizes)]
         L.twell_gate_pack.restype = ctypes.c_int
         L.twell_gate_pack.argtypes = [pd, ctypes.c_int, vp, vp, vp, pp, vp, vp]
+        L.twell_gate_pack_ws.restype = ctypes.c_int
+        L.twell_gate_pack_ws.argtypes = [pd, ctypes.c_int, vp, vp, vp, pp, vp, vp, sz, vp]
         L.twell_pack_preact.restype = ctypes.c_int
         L.twell_pack_preact.argtypes = [pd, ctypes.c_int, vp, vp, pp, vp]
         L.twell_quantize_e4m3.restype = ctypes.c_int
@@ -212,10 +215,18 @@ def alloc_workspace(nbytes: int, device="cuda") -> torch.Tensor:
     return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
 
 
-def gate_pack(dims: Dims, dtype: int, x, w_gate_t, t, pack: TwellPack, g_dump=None, stream=None) -> None:
+def gate_pack(dims: Dims, dtype: int, x, w_gate_t, t, pack: TwellPack, g_dump=None, stream=None, ws=None) -> None:
+    """Gate GEMM + TwELL pack. With ws (a tensor of at least sizes["ws_gate"]
+    bytes) small batches take the split-GEMV gate (twell_gate_pack_ws)."""
     p = pack.struct()
-    _check(lib().twell_gate_pack(ctypes.byref(dims), int(dtype), _ptr(x), _ptr(w_gate_t), _ptr(t),
-                                 ctypes.byref(p), _ptr(g_dump), _stream(stream)), "twell_gate_pack")
+    if ws is None:
+        _check(lib().twell_gate_pack(ctypes.byref(dims), int(dtype), _ptr(x), _ptr(w_gate_t), _ptr(t),
+                                     ctypes.byref(p), _ptr(g_dump), _stream(stream)), "twell_gate_pack")
+    else:
+        nbytes = ws.numel() * ws.element_size()
+        _check(lib().twell_gate_pack_ws(ctypes.byref(dims), int(dtype), _ptr(x), _ptr(w_gate_t), _ptr(t),
+                                        ctypes.byref(p), _ptr(g_dump), _ptr(ws), nbytes, _stream(stream)),
+               "twell_gate_pack_ws")
 
 
 def quantize_e4m3(a, stream=None, out=None):
@@ -316,6 +327,8 @@ class TwellFFN:
             self.x_scale = torch.empty(N, dtype=torch.float32, device=device)
         self.y = torch.empty((N, D), dtype=torch.float32, device=device)
         self.ws_fwd = alloc_workspace(self.sizes["ws_fwd"], device)
+        # small batches: g of the split-GEMV gate
+        self.ws_gate = alloc_workspace(self.sizes["ws_gate"], device) if self.sizes["ws_gate"] else None
         self.a_save = None
         if train:
             self.a_save = torch.empty(self.sizes["a_save"] // 4, dtype=torch.float32, device=device)
@@ -332,10 +345,23 @@ class TwellFFN:
             quantize_e4m3(x, stream=stream, out=(self.x_q, self.x_scale))
             gate_pack_fp8(self.dims, self.x_q, self.x_scale, w_q, w_scale, t, self.pack, g_dump=g_dump, stream=stream)
         else:
-            gate_pack(self.dims, self.dtype, x, w_gate_t, t, self.pack, g_dump=g_dump, stream=stream)
+            gate_pack(self.dims, self.dtype, x, w_gate_t, t, self.pack, g_dump=g_dump, stream=stream, ws=self.ws_gate)
         ffn_fwd(self.dims, self.dtype, self.pack, x, w_up_t, w_down, self.y, a_save=self.a_save, ws=self.ws_fwd,
                 stream=stream)
         return self.y
+
+    def capture(self, x, w_gate_t, w_up_t, w_down, t) -> "torch.cuda.CUDAGraph":
+        """Record forward() on these tensors into a HIP graph (after one eager
+        warm-up call). Replaying it reruns the whole forward on whatever the
+        same tensors hold then; the result lands in self.y. Every launch of the
+        path is a kernel or an event (no memset or allocation), so the graph
+        holds nothing else."""
+        self.forward(x, w_gate_t, w_up_t, w_down, t)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.forward(x, w_gate_t, w_up_t, w_down, t)
+        return graph
 
     def backward(self, x, dy, w_gate_t, w_up_t, w_down, l1_lambda: float, stream=None):
         route_hybrid(self.dims, self.dtype, self.pack, self.a_save, self.hyb, stream=stream)

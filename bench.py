@@ -33,16 +33,31 @@ MFMA_FP8_PEAK_TFS = 5000.0   # MI355X dense fp8 MFMA, published
 METRIC = "sparse FFN tokens/s and speedup vs dense bf16 FFN; HBM GB/s / MFMA % of peak"
 
 WORKLOADS = {
-    # name: (config, density override, train, FP8 gate)
-    "c5": ("c5", None, True, False),
-    "c2": ("c2", None, False, False),
-    "c3_5": ("c3", 0.05, False, False),
-    "c3_1": ("c3", 0.01, False, False),
-    "c3_05": ("c3", 0.005, False, False),
-    "c4": ("c4", None, False, False),
-    "c2_fp8": ("c2", None, False, True),
-    "c3_1_fp8": ("c3", 0.01, False, True),
+    # name: (config, density override, train, FP8 gate, overrides of the config)
+    "c5": ("c5", None, True, False, {}),
+    "c2": ("c2", None, False, False, {}),
+    "c3_5": ("c3", 0.05, False, False, {}),
+    "c3_1": ("c3", 0.01, False, False, {}),
+    "c3_05": ("c3", 0.005, False, False, {}),
+    "c4": ("c4", None, False, False, {}),
+    "c2_fp8": ("c2", None, False, True, {}),
+    "c3_1_fp8": ("c3", 0.01, False, True, {}),
+    # decode / small batch: the same layers on 1-64 tokens. The TwELL arrays
+    # are then tiny, so each tile gets as many slots as it has columns
+    # (S = T_n): no row can overflow and the overflow steps are skipped.
+    "c2_dec1": ("c2", None, False, False, dict(N=1, slots=128)),
+    "c2_dec16": ("c2", None, False, False, dict(N=16, slots=128)),
+    "c2_dec64": ("c2", None, False, False, dict(N=64, slots=128)),
+    "c3_dec1": ("c3", 0.01, False, False, dict(N=1, slots=128)),
+    "c3_dec64": ("c3", 0.01, False, False, dict(N=64, slots=128)),
 }
+
+
+def workload_inputs(name):
+    """(inputs, train, fp8) of a named workload."""
+    from synth import make_inputs
+    cfg, dens, train, fp8, over = WORKLOADS[name]
+    return make_inputs(cfg, density=dens, **over), train, fp8
 
 
 def parse():
@@ -218,7 +233,6 @@ def main():
     import torch
 
     from activation_sparse_ffn_03_amd import twell as tw
-    from synth import make_inputs
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -227,8 +241,7 @@ def main():
         copy_calibration()
         return
     tw.lib()
-    cfg, dens, train, fp8 = WORKLOADS[args.workload]
-    w = make_inputs(cfg, density=dens)
+    w, train, fp8 = workload_inputs(args.workload)
     print(f"[bench] workload {args.workload}: {describe(w, train, fp8)}", file=sys.stderr, flush=True)
     dev = torch.device("cuda:0")
 
@@ -265,6 +278,23 @@ def main():
     assert int(ffn.pack.status.item()) == 0, "overflow capacity exceeded"
     if train:
         assert int(ffn.hyb.status.item()) == 0, "dense-backup capacity exceeded"
+
+    # the forward replayed from a HIP graph (the serving-loop form: no host
+    # launch cost per kernel); same inputs, same K steps
+    graph_ms = None
+    if not train:
+        graph = ffn.capture(x, wgate, wu, wd, t)
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        for _ in range(args.steps):
+            graph.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = g0.elapsed_time(g1) / args.steps
+        del graph
 
     # per-kernel device times: HIP events around every kernel on the stream it runs on
     tw.trace_start(capacity=64 * args.steps + 64)
@@ -306,7 +336,7 @@ def main():
         kernels[k]["TFLOPs"] = wk_k["flops"] / s_k / 1e12
 
     # dense bf16 FFN on the same GPU and inputs (torch / hipBLASLt), same step definition
-    dense = None
+    dense = dense_graph_ms = None
     if not args.no_dense:
         lam = w.lam
 
@@ -338,6 +368,20 @@ def main():
         d1.record(stream)
         torch.cuda.synchronize()
         dense = d0.elapsed_time(d1) / args.steps
+        if not train:   # the dense forward replayed from a graph as well
+            dgraph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(dgraph):
+                dense_step()
+            for _ in range(args.warmup):
+                dgraph.replay()
+            torch.cuda.synchronize()
+            d0.record(stream)
+            for _ in range(args.steps):
+                dgraph.replay()
+            d1.record(stream)
+            torch.cuda.synchronize()
+            dense_graph_ms = d0.elapsed_time(d1) / args.steps
+            del dgraph
 
     # per-step times (each step bracketed by its own events): warm caches, and
     # cold ones (a 512 MB write between steps evicts the 4 MB L2s and the 256 MB
@@ -381,6 +425,8 @@ def main():
         "config": {"workload": f"{args.workload}: {describe(w, train, fp8)}", "n_tokens": w.N, "d_model": w.D,
                    "d_ff": w.F, "tile_n": w.tile_n, "slots": w.slots, "row_cap": w.row_cap if train else 0,
                    "parallelism": "none (1 GPU)"},
+        "graph_ms_per_step": graph_ms,
+        "dense_graph_ms_per_step": dense_graph_ms,
         "speedup_vs_dense": (dense / ms) if dense else None,
         "dense_bf16_ms_per_step": dense,
         "step_ms": step_ms,

@@ -119,6 +119,9 @@ typedef struct twell_hybrid {
   uint32_t* status;    /* [1] overwritten by twell_route_hybrid */
 } twell_hybrid;
 
+/* Largest token count the small-batch gate of twell_gate_pack_ws serves. */
+#define TWELL_SMALL_BATCH_MAX 64
+
 /* Byte sizes of every buffer for a given shape (host-only query). */
 typedef struct twell_sizes {
   size_t vals, cols, counts, ovf_flag, ovf_rows, ovf_h, n_ovf, status;
@@ -126,6 +129,8 @@ typedef struct twell_sizes {
   size_t a_save;    /* [n_t][S][N] fp32 */
   size_t ws_fwd;    /* workspace of twell_ffn_fwd */
   size_t ws_bwd;    /* workspace of twell_ffn_bwd */
+  size_t ws_gate;   /* workspace of twell_gate_pack_ws: N * F * 4 for bf16 and
+                       1 <= N <= TWELL_SMALL_BATCH_MAX, else 0 */
 } twell_sizes;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -152,6 +157,23 @@ twell_status twell_query_sizes(const twell_dims* dims, twell_dtype dtype, twell_
 twell_status twell_gate_pack(const twell_dims* dims, twell_dtype dtype, const void* x,
                              const void* w_gate_t, const float* t, const twell_pack* out,
                              float* g_dump, void* stream);
+
+/* twell_gate_pack for small batches (the decode regime), with a workspace.
+ * For bf16 and 1 <= N <= TWELL_SMALL_BATCH_MAX the gate runs as a GEMV over
+ * all CUs (each workgroup owns 16 hidden units, d_model split in 8 ranges
+ * whose partial sums are added in a fixed order) and writes g to ws (or to
+ * g_dump when given), from which the pack epilogue and the overflow rows both
+ * read; the outputs are those of twell_gate_pack for that g. g is
+ * deterministic but may
+ * differ in its last bits from the large-batch GEMM's (a different fp32
+ * summation order over d_model). Otherwise (fp32, larger N, or
+ * twell_sizes.ws_gate == 0) this is exactly twell_gate_pack.
+ * ws: at least twell_sizes.ws_gate bytes, 16-byte aligned device memory owned
+ * by the caller (NULL allowed when ws_gate is 0). Errors as twell_gate_pack,
+ * plus TWELL_ERR_WORKSPACE when ws is too small. */
+twell_status twell_gate_pack_ws(const twell_dims* dims, twell_dtype dtype, const void* x,
+                                const void* w_gate_t, const float* t, const twell_pack* out,
+                                float* g_dump, void* ws, size_t ws_bytes, void* stream);
 
 /* Test entry: the same pack epilogue fed from a given pre-activation g [N][F]
  * fp32 instead of the GEMM. Produces exactly what twell_gate_pack would for

@@ -13,7 +13,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 
 
 def test_library_exports_every_declared_symbol():
-    decl = set(re.findall(r"\b(twell_[a-z_]+)\s*\(", open(HEADER).read()))
+    decl = set(re.findall(r"\b(twell_[a-z0-9_]+)\s*\(", open(HEADER).read()))
     assert decl == set(tw.EXPORTS), decl ^ set(tw.EXPORTS)
     L = tw.lib()
     for name in decl:

@@ -9,9 +9,8 @@ import pytest
 import torch
 
 from activation_sparse_ffn_03_amd import twell as tw
-from bench import WORKLOADS, capacities
+from bench import capacities, workload_inputs
 from oracle import twell_oracle as orc
-from synth import make_inputs
 
 from gpu_util import DELTA_REL, dev, f64, h_flip, require_gpu, rowwise_ok, u16
 
@@ -21,8 +20,7 @@ Y_TOL = 1e-2
 
 def _setup(name):
     require_gpu()
-    cfg, dens, train = WORKLOADS[name]
-    w = make_inputs(cfg, density=dens)
+    w, train, _fp8 = workload_inputs(name)
     return w, train
 
 
