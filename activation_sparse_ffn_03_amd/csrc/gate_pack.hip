@@ -738,30 +738,35 @@ __global__ __launch_bounds__(256) void pack_from_g(const float* __restrict__ g, 
 // ---------------------------------------------------------------- small batches
 
 // Gate pre-activation of at most kSmallN tokens, written to g [N][F] fp32 for
-// pack_from_g. A workgroup owns 16 hidden units and its 8 waves split d_model
-// into 8 ranges of 32-wide k steps. Each wave issues the W_gate loads of
-// kGemvBatch steps (16 rows x 64 bytes each) before their MFMAs, so the weight
+// pack_from_g. A workgroup owns 16 * UW hidden units and its 8 waves split
+// d_model into 8 ranges of 32-wide k steps. Each wave issues the W_gate loads
+// of B steps (UW x 16 rows x 64 bytes each) before their MFMAs, so the weight
 // streams from HBM with enough bytes in flight although the grid has only
-// F / 16 workgroups; x is small and read from L2. A wave runs the 16x16x32
-// bf16 MFMA over its range in ascending k, and the 8 partial sums are added
-// in wave order through LDS: deterministic, but g may differ in its last bits
-// from the large-batch GEMM's single chain over d_model. Tokens past N read
-// zeros; columns past F read row F - 1 and are never stored.
+// F / (16 UW) workgroups; x is small and read from L2, once per 16 * UW units
+// (UW grows with the token count to keep that re-read small). A wave runs the
+// 16x16x32 bf16 MFMA over its range in ascending k, and the 8 partial sums
+// are added in wave order through LDS: deterministic, but g may differ in its
+// last bits from the large-batch GEMM's single chain over d_model. Tokens past
+// N read zeros; columns past F read row F - 1 and are never stored.
 constexpr int kSmallN = TWELL_SMALL_BATCH_MAX;
 constexpr int kGemvWaves = 8;
-constexpr int kGemvBatch = 8;
 
-template <int NF>
+template <int NF, int UW, int B>
 __global__ __launch_bounds__(64 * kGemvWaves) void gate_gemv_small(const uint16_t* __restrict__ x,
                                                                     const uint16_t* __restrict__ w, int64_t N,
                                                                     int D, int F, float* __restrict__ g) {
-  __shared__ f32x4_t part[kGemvWaves][NF][64];
+  __shared__ f32x4_t red[NF][UW][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int col = blockIdx.x * 16 + (lane & 15);
+  const int c0 = blockIdx.x * 16 * UW + (lane & 15);
   const int ke = (lane >> 4) * 8;  // element offset of this lane's 16 bytes in a 32-wide k step
   const int S = D / 32;
   const int s_lo = S * wave / kGemvWaves, s_hi = S * (wave + 1) / kGemvWaves;
-  const uint16_t* wrow = w + (size_t)(col < F ? col : F - 1) * D + ke;
+  const uint16_t* wrow[UW];
+#pragma unroll
+  for (int u = 0; u < UW; ++u) {
+    const int col = c0 + 16 * u;
+    wrow[u] = w + (size_t)(col < F ? col : F - 1) * D + ke;
+  }
   const uint16_t* xrow[NF];
   bool xok[NF];
 #pragma unroll
@@ -770,38 +775,50 @@ __global__ __launch_bounds__(64 * kGemvWaves) void gate_gemv_small(const uint16_
     xok[f] = tok < N;
     xrow[f] = x + (size_t)(xok[f] ? tok : 0) * D + ke;
   }
-  f32x4_t acc[NF];
+  f32x4_t acc[NF][UW];
 #pragma unroll
-  for (int f = 0; f < NF; ++f) acc[f] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int f = 0; f < NF; ++f)
+#pragma unroll
+    for (int u = 0; u < UW; ++u) acc[f][u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const u32x4_t zero{0u, 0u, 0u, 0u};
-  for (int s0 = s_lo; s0 < s_hi; s0 += kGemvBatch) {
-    u32x4_t b[kGemvBatch], a[kGemvBatch][NF];
+  for (int s0 = s_lo; s0 < s_hi; s0 += B) {
+    u32x4_t b[B][UW], a[B][NF];
 #pragma unroll
-    for (int j = 0; j < kGemvBatch; ++j)
-      b[j] = s0 + j < s_hi ? *reinterpret_cast<const u32x4_t*>(wrow + (size_t)(s0 + j) * 32) : zero;
+    for (int j = 0; j < B; ++j)
 #pragma unroll
-    for (int j = 0; j < kGemvBatch; ++j)
+      for (int u = 0; u < UW; ++u)
+        b[j][u] = s0 + j < s_hi ? *reinterpret_cast<const u32x4_t*>(wrow[u] + (size_t)(s0 + j) * 32) : zero;
+#pragma unroll
+    for (int j = 0; j < B; ++j)
 #pragma unroll
       for (int f = 0; f < NF; ++f)
         a[j][f] = (s0 + j < s_hi && xok[f]) ? *reinterpret_cast<const u32x4_t*>(xrow[f] + (size_t)(s0 + j) * 32)
                                              : zero;
 #pragma unroll
-    for (int j = 0; j < kGemvBatch; ++j) {
+    for (int j = 0; j < B; ++j) {
       if (s0 + j >= s_hi) break;  // wave-uniform
 #pragma unroll
       for (int f = 0; f < NF; ++f)
-        acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[j][f]),
-                                                         __builtin_bit_cast(bf16x8_t, b[j]), acc[f], 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < UW; ++u)
+          acc[f][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[j][f]),
+                                                              __builtin_bit_cast(bf16x8_t, b[j][u]), acc[f][u], 0, 0, 0);
     }
   }
+  // partial sums added in wave order 0, 1, ..., 7
+  for (int p = 0; p < kGemvWaves; ++p) {
+    if (wave == p) {
 #pragma unroll
-  for (int f = 0; f < NF; ++f) part[wave][f][lane] = acc[f];
-  __syncthreads();
-  if (wave < NF) {
-    const int f = wave;
-    f32x4_t sum = part[0][f][lane];
+      for (int f = 0; f < NF; ++f)
 #pragma unroll
-    for (int p = 1; p < kGemvWaves; ++p) sum += part[p][f][lane];
+        for (int u = 0; u < UW; ++u) red[f][u][lane] = p == 0 ? acc[f][u] : red[f][u][lane] + acc[f][u];
+    }
+    __syncthreads();
+  }
+  for (int q = wave; q < NF * UW; q += kGemvWaves) {
+    const int f = q / UW, u = q % UW;
+    const int col = c0 + 16 * u;
+    const f32x4_t sum = red[f][u][lane];
     if (col < F) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -810,6 +827,13 @@ __global__ __launch_bounds__(64 * kGemvWaves) void gate_gemv_small(const uint16_
       }
     }
   }
+}
+
+template <int NF, int UW, int B>
+void launch_gemv(const GateArgs& a, float* g, hipStream_t s) {
+  const dim3 grid((unsigned)((a.F + 16 * UW - 1) / (16 * UW)));
+  TWELL_LAUNCH("gate_gemv_small", (gate_gemv_small<NF, UW, B>), grid, 64 * kGemvWaves, 0, s, (const uint16_t*)a.x,
+               (const uint16_t*)a.w, a.N, a.D, a.F, g);
 }
 
 // ---------------------------------------------------------------- overflow rows
@@ -852,14 +876,11 @@ hipError_t launch_gate_pack(const GateArgs& a, hipStream_t s) {
   const float* g_in = a.g_in;
   if (!a.fp8 && g_in == nullptr && a.is_bf16 && a.N <= kSmallN && (a.g_ws != nullptr || a.g_dump != nullptr)) {
     float* gb = a.g_dump != nullptr ? a.g_dump : a.g_ws;
-    const dim3 grid((unsigned)((a.F + 15) / 16));
-    const auto* xb = (const uint16_t*)a.x;
-    const auto* wb = (const uint16_t*)a.w;
-    switch ((a.N + 15) / 16) {
-      case 1: TWELL_LAUNCH("gate_gemv_small", gate_gemv_small<1>, grid, 64 * kGemvWaves, 0, s, xb, wb, a.N, a.D, a.F, gb); break;
-      case 2: TWELL_LAUNCH("gate_gemv_small", gate_gemv_small<2>, grid, 64 * kGemvWaves, 0, s, xb, wb, a.N, a.D, a.F, gb); break;
-      case 3: TWELL_LAUNCH("gate_gemv_small", gate_gemv_small<3>, grid, 64 * kGemvWaves, 0, s, xb, wb, a.N, a.D, a.F, gb); break;
-      default: TWELL_LAUNCH("gate_gemv_small", gate_gemv_small<4>, grid, 64 * kGemvWaves, 0, s, xb, wb, a.N, a.D, a.F, gb); break;
+    switch ((a.N + 15) / 16) {  // token fragments; units per wave and k steps per load batch
+      case 1: launch_gemv<1, 1, 8>(a, gb, s); break;
+      case 2: launch_gemv<2, 2, 8>(a, gb, s); break;
+      case 3: launch_gemv<3, 4, 4>(a, gb, s); break;
+      default: launch_gemv<4, 4, 4>(a, gb, s); break;
     }
     g_in = gb;
     e.g_dump = nullptr;  // g is already in the caller's g_dump, or not asked for
