@@ -68,6 +68,7 @@ def parse():
     p.add_argument("--workload", default="c2", choices=sorted(WORKLOADS))
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-dense", action="store_true")
+    p.add_argument("--no-graph", action="store_true", help="skip the graph-replay timings")
     p.add_argument("--cpu-sample", type=int, default=512, help="tokens per window of the CPU oracle sample")
     p.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of CPU oracle work")
     p.add_argument("--copy-calib", action="store_true", help="only run the copy kernel used to scale HBM counters")
@@ -100,6 +101,11 @@ def kernel_work(name, w, st, train):
                 "peak": "fp8"}
     if name == "quantize_e4m3":   # x read (bf16), codes and scales written
         return {"flops": 0.0, "bytes": N * D * e + N * D + 4 * N, "bound": "hbm"}
+    if name == "gate_gemv_small":  # small batches: W_gate streamed once, x read, g (fp32) written
+        return {"flops": 2.0 * N * D * F, "bytes": F * D * e + N * D * e + N * F * 4, "bound": "hbm"}
+    if name == "pack_from_g":      # g read, TwELL written
+        twell = n_t * w.slots * N * (e + 2) + n_t * N * 2
+        return {"flops": 0.0, "bytes": N * F * 4 + twell, "bound": "hbm"}
     if name == "ffn_up_kernel":   # x, W_up once; TwELL read; z (and a when training) written
         byt = N * D * e + F * D * e + nnz * (e + 2) + n_t * N * 2 + nnz * 4 + (nnz * 4 if train else 0)
         return {"flops": 2.0 * D * nnz, "bytes": byt, "bound": "hbm"}
@@ -174,6 +180,9 @@ def cpu_baseline(w, train, sample, budget_s=10.0, fp8=False):
 KERNEL_SOURCES = {
     "gate_mfma_bf16": ["gate_pack.hip", "twell_device.h"],
     "gate_mfma_fp8": ["gate_pack.hip", "twell_device.h"],
+    "gate_gemv_small": ["gate_pack.hip", "twell_device.h"],
+    "pack_from_g": ["gate_pack.hip", "twell_device.h"],
+    "quantize_e4m3": ["quant.hip", "twell_device.h"],
     "ffn_up_kernel": ["fused_fwd.hip", "row_ops.h", "twell_device.h"],
     "ffn_down_kernel": ["fused_fwd.hip", "row_ops.h", "twell_device.h"],
     "bwd_dz_ell": ["bwd.hip", "row_ops.h", "twell_device.h"],
@@ -282,7 +291,7 @@ def main():
     # the forward replayed from a HIP graph (the serving-loop form: no host
     # launch cost per kernel); same inputs, same K steps
     graph_ms = None
-    if not train:
+    if not train and not args.no_graph:
         graph = ffn.capture(x, wgate, wu, wd, t)
         for _ in range(args.warmup):
             graph.replay()
@@ -368,7 +377,7 @@ def main():
         d1.record(stream)
         torch.cuda.synchronize()
         dense = d0.elapsed_time(d1) / args.steps
-        if not train:   # the dense forward replayed from a graph as well
+        if not train and not args.no_graph:   # the dense forward replayed from a graph as well
             dgraph = torch.cuda.CUDAGraph()
             with torch.cuda.graph(dgraph):
                 dense_step()
