@@ -12,7 +12,7 @@ from activation_sparse_ffn_03_amd import twell as tw
 from bench import capacities, workload_inputs
 from oracle import twell_oracle as orc
 
-from gpu_util import DELTA_REL, dev, f64, h_flip, require_gpu, rowwise_ok, u16
+from gpu_util import DELTA_REL, dev, f64, fp8_gate_err_bound, h_flip, require_gpu, rowwise_ok, u16
 
 pytestmark = pytest.mark.gpu
 Y_TOL = 1e-2
@@ -75,6 +75,70 @@ def test_fullsize_forward(name):
     delta = np.broadcast_to((DELTA_REL * rms[clean])[None, None, :], valid.shape)[valid]
     rv = ref["vals"][valid]
     assert np.all(np.abs(vals[valid] - rv) <= 1.01 * delta + (np.abs(rv) + delta) * 2.0 ** -7)
+
+
+@pytest.mark.parametrize("name", ["c2_dec1", "c2_dec16", "c2_dec64", "c3_dec1", "c3_dec64"])
+def test_fullsize_decode(name):
+    """The small-batch workloads as the benchmark runs them (S = T_n: no row
+    can overflow, the gate is the split GEMV): every row against the oracle."""
+    w, _ = _setup(name)
+    assert w.slots >= w.tile_n and w.N <= 64
+    print(f"[fullsize] {name}: N={w.N} D={w.D} F={w.F} S={w.slots}", flush=True)
+    ovf_cap, _ = capacities(w, False)
+    dims = tw.make_dims(w.N, w.D, w.F, w.tile_n, w.slots, 0, ovf_cap, 0)
+    ffn = tw.TwellFFN(dims, tw.BF16)
+    assert ffn.ws_gate is not None
+    x, wg, wu, wd = dev(w.x, "bf16"), dev(w.w_gate_t, "bf16"), dev(w.w_up_t, "bf16"), dev(w.w_down, "bf16")
+    y = ffn.forward(x, wg, wu, wd, torch.from_numpy(w.t).cuda())
+    torch.cuda.synchronize()
+    assert int(ffn.pack.status.item()) == 0 and int(ffn.pack.n_ovf.item()) == 0
+    assert not bool(ffn.pack.ovf_flag.any())
+    fw = orc.ffn_forward(w.x, w.w_gate_t, w.w_up_t, w.w_down, w.t, store="bf16", arith="f32")
+    slack = (h_flip(fw, "bf16") * np.abs(fw["a"])) @ np.abs(w.w_down.astype(np.float64))
+    rowwise_ok(f64(y), fw["y"], Y_TOL, f"{name} y", slack)
+    # counts of every row whose units all lie outside the fp32 error of their threshold
+    g = fw["g"]
+    rms = np.sqrt(np.mean(g * g, axis=1))
+    clean = np.all(np.abs(g - w.t[:, None]) > DELTA_REL * rms[:, None], axis=1)
+    ref = orc.pack(g[clean].astype(np.float32), w.t[clean], w.tile_n, w.slots, store="bf16", arith="f32")
+    np.testing.assert_array_equal(u16(ffn.pack.counts)[:, clean], ref["counts"])
+
+
+@pytest.mark.parametrize("name,k", [("c2_fp8", 48), ("c3_1_fp8", 16)])
+def test_fullsize_forward_fp8(name, k):
+    """The FP8-gate workloads as the benchmark runs them (x quantised on the
+    GPU, W_gate quantised once): sampled rows against the oracle's FP8 gate.
+    A unit within the FP8 gate's error bound of its threshold may take either
+    side, and a stored value either bf16 neighbour where its rounding is
+    ambiguous within that bound; the slack allows both."""
+    w, train, fp8 = workload_inputs(name)
+    require_gpu()
+    assert fp8 and not train
+    print(f"[fullsize] {name}: N={w.N} D={w.D} F={w.F}", flush=True)
+    ovf_cap, _ = capacities(w, False)
+    dims = tw.make_dims(w.N, w.D, w.F, w.tile_n, w.slots, 0, ovf_cap, 0)
+    ffn = tw.TwellFFN(dims, tw.BF16, fp8_gate=True)
+    x, wg, wu, wd = dev(w.x, "bf16"), dev(w.w_gate_t, "bf16"), dev(w.w_up_t, "bf16"), dev(w.w_down, "bf16")
+    y = ffn.forward(x, tw.quantize_e4m3(wg), wu, wd, torch.from_numpy(w.t).cuda())
+    torch.cuda.synchronize()
+    assert int(ffn.pack.status.item()) == 0
+    n_ovf = int(ffn.pack.n_ovf.item())
+    rows = _sample_rows(w.N, ffn.pack.ovf_rows[:n_ovf].cpu().numpy(), k=k)
+    wq, wsc = orc.quantize_rows_e4m3(w.w_gate_t)
+    xq, xsc = orc.quantize_rows_e4m3(w.x[rows])
+    g = orc.gate_preact_fp8(xq, xsc, wq, wsc)
+    t = w.t[rows].astype(np.float64)
+    bound = fp8_gate_err_bound(xq, xsc, wq, wsc, g)
+    g32, t32 = g.astype(np.float32), w.t[rows].astype(np.float32)
+    h = np.where(g32 > t32[:, None], (g32 - t32[:, None]).astype(np.float64), 0.0)
+    hq = orc.dense_activation(g, w.t[rows], store="bf16", arith="f32")
+    a = w.x[rows].astype(np.float64) @ w.w_up_t.astype(np.float64).T
+    y_ref = (hq * a) @ w.w_down.astype(np.float64)
+    near = np.abs(g - t[:, None]) <= bound                    # may flip either way
+    amb = orc.rounding_ambiguous(h, bound + np.abs(h) * 2.0 ** -23, "bf16")
+    dev_h = np.where(near, np.abs(g - t[:, None]) + bound, np.where(amb, orc.store_ulp(h, "bf16"), 0.0))
+    slack = (dev_h * np.abs(a)) @ np.abs(w.w_down.astype(np.float64))
+    rowwise_ok(f64(y[torch.from_numpy(rows).cuda()]), y_ref, Y_TOL, f"{name} y", slack)
 
 
 def test_fullsize_training_step():
