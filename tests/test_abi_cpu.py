@@ -73,3 +73,34 @@ def test_calls_validate_before_touching_the_device():
     assert L.twell_query_sizes(ctypes.byref(d), 7, ctypes.byref(z)) == 1
     assert L.twell_n_tiles(None) == -1
     assert L.twell_trace_start(0) == 1
+
+
+def test_small_batch_gate_workspace_size():
+    """ws_gate: N * F * 4 bytes for bf16 and 1 <= N <= TWELL_SMALL_BATCH_MAX, else 0."""
+    for n in (1, 17, 64):
+        assert tw.query_sizes(tw.make_dims(n, 256, 1000, 128, 16), tw.BF16)["ws_gate"] == n * 1000 * 4
+    assert tw.query_sizes(tw.make_dims(65, 256, 1000, 128, 16), tw.BF16)["ws_gate"] == 0
+    assert tw.query_sizes(tw.make_dims(0, 256, 1000, 128, 16), tw.BF16)["ws_gate"] == 0
+    assert tw.query_sizes(tw.make_dims(8, 256, 1000, 128, 16), tw.F32)["ws_gate"] == 0
+
+
+def test_new_calls_validate_before_touching_the_device():
+    L = tw.lib()
+    d = tw.make_dims(8, 256, 1000, 128, 16, 0, 8, 0)
+    p = tw.Pack()
+    fake = ctypes.c_void_p(0x100000)  # aligned, never dereferenced: validation fails first
+    need = tw.query_sizes(d, tw.BF16)["ws_gate"]
+    # workspace too small, then missing
+    assert L.twell_gate_pack_ws(ctypes.byref(d), 0, fake, fake, fake, ctypes.byref(p), None, fake, need - 1,
+                                None) == 3
+    assert L.twell_gate_pack_ws(ctypes.byref(d), 0, fake, fake, fake, ctypes.byref(p), None, None, need, None) == 1
+    assert b"ws" in L.twell_last_error()
+    # quantiser: shapes, dtype, pointers
+    assert L.twell_quantize_e4m3(-1, 8, 0, fake, fake, fake, None) == 1
+    assert L.twell_quantize_e4m3(4, 0, 0, fake, fake, fake, None) == 1
+    assert L.twell_quantize_e4m3(4, 8, 7, fake, fake, fake, None) == 1
+    assert L.twell_quantize_e4m3(4, 8, 0, None, fake, fake, None) == 1
+    assert L.twell_quantize_e4m3(4, 8, 0, ctypes.c_void_p(0x100001), fake, fake, None) == 1
+    # FP8 gate: missing operands
+    assert L.twell_gate_pack_fp8(ctypes.byref(d), None, fake, fake, fake, fake, ctypes.byref(p), None, None) == 1
+    assert L.twell_gate_pack_fp8(ctypes.byref(d), fake, fake, fake, None, fake, ctypes.byref(p), None, None) == 1
