@@ -14,8 +14,18 @@
 //                    LDS one 128-column group at a time and packs it.
 //   gate_mfma_bf16   register-staged variant (128x128, K-steps of 64), used to
 //                    recompute the overflow rows with identical arithmetic.
+//                    With FP8 = true the operands are E4M3 codes (64 k per
+//                    64-byte LDS row, v_mfma_f32_16x16x32_fp8_fp8) and the
+//                    epilogue applies the row and column scales.
+//   gate_mfma_bf16   register-staged variant (128x128, K-steps of 64), used to
+//                    recompute the overflow rows with identical arithmetic.
 //   gate_simt_f32    64x128 fp32 tile, plain FMA (fp32 storage only).
-//   pack_from_g      64x128 tile of a given pre-activation (test entry).
+//   gate_gemv_small  small batches (N <= 64, bf16): g as a GEMV over all CUs
+//                    into a caller's buffer, then packed by pack_from_g.
+//   pack_from_g      64x128 tile of a given pre-activation (test entry and the
+//                    small-batch path); with slots >= tile_n it also writes the
+//                    all-zero overflow outputs, and the overflow steps are
+//                    skipped.
 //   ovf_flags        overflow flag of every row from its true tile counts
 //                    (the ascending list is built by launch_compact).
 // The same kernels, with MODE_DENSE, recompute the dense activation rows of
