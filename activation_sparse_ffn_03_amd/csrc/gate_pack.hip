@@ -748,42 +748,46 @@ __global__ __launch_bounds__(256) void pack_from_g(const float* __restrict__ g, 
 // ---------------------------------------------------------------- small batches
 
 // Gate pre-activation of at most kSmallN tokens, written to g [N][F] fp32 for
-// pack_from_g. A workgroup owns 16 * UW hidden units and its 8 waves split
-// d_model into 8 ranges of 32-wide k steps. Each wave issues the W_gate loads
-// of B steps (UW x 16 rows x 64 bytes each) before their MFMAs, so the weight
-// streams from HBM with enough bytes in flight although the grid has only
-// F / (16 UW) workgroups; x is small and read from L2, once per 16 * UW units
-// (UW grows with the token count to keep that re-read small). A wave runs the
-// 16x16x32 bf16 MFMA over its range in ascending k, and the 8 partial sums
-// are added in wave order through LDS: deterministic, but g may differ in its
-// last bits from the large-batch GEMM's single chain over d_model. Tokens past
-// N read zeros; columns past F read row F - 1 and are never stored.
+// pack_from_g. A workgroup owns 16 * UW hidden units and its 8 waves split the
+// operand rows into 8 ranges of 64-byte steps (32 k of bf16, or 64 k of E4M3
+// codes feeding two v_mfma_f32_16x16x32_fp8_fp8 split as in gate_mfma_dma).
+// Each wave issues the W_gate loads of B steps (UW x 16 rows x 64 bytes each)
+// before their MFMAs, so the weight streams from HBM with enough bytes in
+// flight although the grid has only F / (16 UW) workgroups; x is small and
+// read from L2, once per 16 * UW units (UW grows with the token count to keep
+// that re-read small). A wave runs the MFMAs over its range in ascending k,
+// and the 8 partial sums are added in wave order through LDS: deterministic,
+// but g may differ in its last bits from the large-batch GEMM's single chain
+// over d_model. FP8: g = (sum * x_scale[i]) * w_scale[c] in fp32, as in the
+// GEMM's epilogue. Tokens past N read zeros; columns past F read row F - 1 and
+// are never stored.
 constexpr int kSmallN = TWELL_SMALL_BATCH_MAX;
 constexpr int kGemvWaves = 8;
 
-template <int NF, int UW, int B>
-__global__ __launch_bounds__(64 * kGemvWaves) void gate_gemv_small(const uint16_t* __restrict__ x,
-                                                                    const uint16_t* __restrict__ w, int64_t N,
-                                                                    int D, int F, float* __restrict__ g) {
+template <int NF, int UW, int B, bool FP8>
+__global__ __launch_bounds__(64 * kGemvWaves) void gate_gemv_small(const char* __restrict__ x,
+                                                                    const char* __restrict__ w, int64_t N,
+                                                                    int64_t rowb, int F, const float* x_scale,
+                                                                    const float* w_scale, float* __restrict__ g) {
   __shared__ f32x4_t red[NF][UW][64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c0 = blockIdx.x * 16 * UW + (lane & 15);
-  const int ke = (lane >> 4) * 8;  // element offset of this lane's 16 bytes in a 32-wide k step
-  const int S = D / 32;
+  const int kb = (lane >> 4) * 16;  // byte offset of this lane's 16 bytes in a 64-byte step
+  const int S = (int)(rowb / 64);
   const int s_lo = S * wave / kGemvWaves, s_hi = S * (wave + 1) / kGemvWaves;
-  const uint16_t* wrow[UW];
+  const char* wrow[UW];
 #pragma unroll
   for (int u = 0; u < UW; ++u) {
     const int col = c0 + 16 * u;
-    wrow[u] = w + (size_t)(col < F ? col : F - 1) * D + ke;
+    wrow[u] = w + (int64_t)(col < F ? col : F - 1) * rowb + kb;
   }
-  const uint16_t* xrow[NF];
+  const char* xrow[NF];
   bool xok[NF];
 #pragma unroll
   for (int f = 0; f < NF; ++f) {
     const int tok = 16 * f + (lane & 15);
     xok[f] = tok < N;
-    xrow[f] = x + (size_t)(xok[f] ? tok : 0) * D + ke;
+    xrow[f] = x + (int64_t)(xok[f] ? tok : 0) * rowb + kb;
   }
   f32x4_t acc[NF][UW];
 #pragma unroll
@@ -797,12 +801,12 @@ __global__ __launch_bounds__(64 * kGemvWaves) void gate_gemv_small(const uint16_
     for (int j = 0; j < B; ++j)
 #pragma unroll
       for (int u = 0; u < UW; ++u)
-        b[j][u] = s0 + j < s_hi ? *reinterpret_cast<const u32x4_t*>(wrow[u] + (size_t)(s0 + j) * 32) : zero;
+        b[j][u] = s0 + j < s_hi ? *reinterpret_cast<const u32x4_t*>(wrow[u] + (int64_t)(s0 + j) * 64) : zero;
 #pragma unroll
     for (int j = 0; j < B; ++j)
 #pragma unroll
       for (int f = 0; f < NF; ++f)
-        a[j][f] = (s0 + j < s_hi && xok[f]) ? *reinterpret_cast<const u32x4_t*>(xrow[f] + (size_t)(s0 + j) * 32)
+        a[j][f] = (s0 + j < s_hi && xok[f]) ? *reinterpret_cast<const u32x4_t*>(xrow[f] + (int64_t)(s0 + j) * 64)
                                              : zero;
 #pragma unroll
     for (int j = 0; j < B; ++j) {
@@ -810,9 +814,19 @@ __global__ __launch_bounds__(64 * kGemvWaves) void gate_gemv_small(const uint16_
 #pragma unroll
       for (int f = 0; f < NF; ++f)
 #pragma unroll
-        for (int u = 0; u < UW; ++u)
-          acc[f][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[j][f]),
-                                                              __builtin_bit_cast(bf16x8_t, b[j][u]), acc[f][u], 0, 0, 0);
+        for (int u = 0; u < UW; ++u) {
+          if constexpr (FP8) {
+            const u32x4_t av = a[j][f], bv = b[j][u];
+            const long alo = (long)(((uint64_t)av.y << 32) | av.x), ahi = (long)(((uint64_t)av.w << 32) | av.z);
+            const long blo = (long)(((uint64_t)bv.y << 32) | bv.x), bhi = (long)(((uint64_t)bv.w << 32) | bv.z);
+            acc[f][u] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(alo, blo, acc[f][u], 0, 0, 0);
+            acc[f][u] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(ahi, bhi, acc[f][u], 0, 0, 0);
+          } else {
+            acc[f][u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[j][f]),
+                                                                __builtin_bit_cast(bf16x8_t, b[j][u]), acc[f][u], 0,
+                                                                0, 0);
+          }
+        }
     }
   }
   // partial sums added in wave order 0, 1, ..., 7
@@ -830,20 +844,32 @@ __global__ __launch_bounds__(64 * kGemvWaves) void gate_gemv_small(const uint16_
     const int col = c0 + 16 * u;
     const f32x4_t sum = red[f][u][lane];
     if (col < F) {
+      const float sw = FP8 ? w_scale[col] : 1.f;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int64_t tok = 16 * f + 4 * (lane >> 4) + r;
-        if (tok < N) g[tok * F + col] = sum[r];
+        if (tok < N) g[tok * F + col] = FP8 ? sum[r] * x_scale[tok] * sw : sum[r];
       }
     }
   }
 }
 
-template <int NF, int UW, int B>
+template <int NF, int UW, int B, bool FP8>
 void launch_gemv(const GateArgs& a, float* g, hipStream_t s) {
   const dim3 grid((unsigned)((a.F + 16 * UW - 1) / (16 * UW)));
-  TWELL_LAUNCH("gate_gemv_small", (gate_gemv_small<NF, UW, B>), grid, 64 * kGemvWaves, 0, s, (const uint16_t*)a.x,
-               (const uint16_t*)a.w, a.N, a.D, a.F, g);
+  const int64_t rowb = (int64_t)a.D * (FP8 ? 1 : 2);
+  TWELL_LAUNCH("gate_gemv_small", (gate_gemv_small<NF, UW, B, FP8>), grid, 64 * kGemvWaves, 0, s,
+               (const char*)a.x, (const char*)a.w, a.N, rowb, a.F, a.x_scale, a.w_scale, g);
+}
+
+template <bool FP8>
+void launch_gemv_n(const GateArgs& a, float* g, hipStream_t s) {
+  switch ((a.N + 15) / 16) {  // token fragments; units per wave and steps per load batch
+    case 1: launch_gemv<1, 1, 8, FP8>(a, g, s); break;
+    case 2: launch_gemv<2, 2, 8, FP8>(a, g, s); break;
+    case 3: launch_gemv<3, 4, 4, FP8>(a, g, s); break;
+    default: launch_gemv<4, 4, 4, FP8>(a, g, s); break;
+  }
 }
 
 // ---------------------------------------------------------------- overflow rows
@@ -881,17 +907,16 @@ hipError_t launch_gate_pack(const GateArgs& a, hipStream_t s) {
   e.w_scale = a.w_scale;
   const int ncb = (a.F + BN - 1) / BN;
 
-  // Small batches (bf16, a g buffer given): g from the split GEMV, then the
-  // pack and the overflow rows both read that g.
+  // Small batches (bf16 or FP8 operands, a workspace given): g from the split
+  // GEMV (into g_dump when asked for, else the workspace), then the pack and
+  // the overflow rows both read that g.
   const float* g_in = a.g_in;
-  if (!a.fp8 && g_in == nullptr && a.is_bf16 && a.N <= kSmallN && (a.g_ws != nullptr || a.g_dump != nullptr)) {
+  if (g_in == nullptr && a.is_bf16 && a.N <= kSmallN && a.g_ws != nullptr) {
     float* gb = a.g_dump != nullptr ? a.g_dump : a.g_ws;
-    switch ((a.N + 15) / 16) {  // token fragments; units per wave and k steps per load batch
-      case 1: launch_gemv<1, 1, 8>(a, gb, s); break;
-      case 2: launch_gemv<2, 2, 8>(a, gb, s); break;
-      case 3: launch_gemv<3, 4, 4>(a, gb, s); break;
-      default: launch_gemv<4, 4, 4>(a, gb, s); break;
-    }
+    if (a.fp8)
+      launch_gemv_n<true>(a, gb, s);
+    else
+      launch_gemv_n<false>(a, gb, s);
     g_in = gb;
     e.g_dump = nullptr;  // g is already in the caller's g_dump, or not asked for
   }
@@ -907,7 +932,7 @@ hipError_t launch_gate_pack(const GateArgs& a, hipStream_t s) {
 
   // 1. GEMM (or given g) + TwELL pack epilogue
   e.mode = MODE_PACK;
-  if (a.fp8) {
+  if (a.fp8 && g_in == nullptr) {
     const int mbc = (int)((a.N + GatePack::BM - 1) / GatePack::BM), nbc = (a.F + GatePack::BN - 1) / GatePack::BN;
     TWELL_LAUNCH("gate_mfma_fp8", (gate_mfma_dma<GatePack, MODE_PACK, true>), dim3(mbc * nbc), GatePack::NT, 0, s,
                  a.x, a.w, a.D, mbc, nbc, e);
@@ -935,7 +960,7 @@ hipError_t launch_gate_pack(const GateArgs& a, hipStream_t s) {
 
   // 3. dense activation rows of the overflow rows, same arithmetic as step 1
   e.mode = MODE_DENSE;
-  if (a.fp8) {
+  if (a.fp8 && g_in == nullptr) {
     const int mbc = (a.ovf_cap + GatePack::BM - 1) / GatePack::BM, nbc = (a.F + GatePack::BN - 1) / GatePack::BN;
     TWELL_LAUNCH("gate_mfma_fp8_rows", (gate_mfma_dma<GatePack, MODE_DENSE, true>), dim3(mbc * nbc), GatePack::NT, 0,
                  s, a.x, a.w, a.D, mbc, nbc, e);

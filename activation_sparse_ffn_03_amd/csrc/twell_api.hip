@@ -151,13 +151,17 @@ twell_status twell_quantize_e4m3(int64_t rows, int32_t cols, twell_dtype dtype, 
                     "twell_quantize_e4m3");
 }
 
-twell_status twell_gate_pack_fp8(const twell_dims* dims, const uint8_t* x_q, const float* x_scale,
-                                 const uint8_t* w_q, const float* w_scale, const float* t, const twell_pack* out,
-                                 float* g_dump, void* stream) {
+static twell_status fp8_common(const twell_dims* dims, const uint8_t* x_q, const float* x_scale, const uint8_t* w_q,
+                               const float* w_scale, const float* t, const twell_pack* out, float* g_dump, void* ws,
+                               size_t ws_bytes, bool use_ws, void* stream) {
   twell::Shape s;
   twell_sizes z;
   twell_status st = prepare(dims, TWELL_BF16, &s, &z);
   if (st != TWELL_OK) return st;
+  if (use_ws && z.ws_gate > 0) {
+    if (ws_bytes < z.ws_gate) return fail(TWELL_ERR_WORKSPACE, "gate workspace smaller than twell_sizes.ws_gate");
+    TWELL_CHECK_PTR(ws, z.ws_gate, "ws");
+  }
   if (s.D % 64 != 0) return fail(TWELL_ERR_UNSUPPORTED, "the FP8 gate needs d_model to be a multiple of 64");
   TWELL_CHECK_PTR(x_q, (size_t)s.N * s.D, "x_q");
   TWELL_CHECK_PTR(x_scale, (size_t)s.N * 4, "x_scale");
@@ -191,7 +195,20 @@ twell_status twell_gate_pack_fp8(const twell_dims* dims, const uint8_t* x_q, con
   a.status = out->status;
   a.ovf_cap = s.ovf_cap;
   a.g_dump = g_dump;
+  a.g_ws = (use_ws && z.ws_gate > 0) ? static_cast<float*>(ws) : nullptr;
   return hip_status(twell::launch_gate_pack(a, (hipStream_t)stream), "twell_gate_pack_fp8");
+}
+
+twell_status twell_gate_pack_fp8(const twell_dims* dims, const uint8_t* x_q, const float* x_scale,
+                                 const uint8_t* w_q, const float* w_scale, const float* t, const twell_pack* out,
+                                 float* g_dump, void* stream) {
+  return fp8_common(dims, x_q, x_scale, w_q, w_scale, t, out, g_dump, nullptr, 0, false, stream);
+}
+
+twell_status twell_gate_pack_fp8_ws(const twell_dims* dims, const uint8_t* x_q, const float* x_scale,
+                                    const uint8_t* w_q, const float* w_scale, const float* t, const twell_pack* out,
+                                    float* g_dump, void* ws, size_t ws_bytes, void* stream) {
+  return fp8_common(dims, x_q, x_scale, w_q, w_scale, t, out, g_dump, ws, ws_bytes, true, stream);
 }
 
 twell_status twell_pack_preact(const twell_dims* dims, twell_dtype dtype, const float* g, const float* t,

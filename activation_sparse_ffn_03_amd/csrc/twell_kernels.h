@@ -37,7 +37,7 @@ struct GateArgs {
   uint32_t* status;
   int ovf_cap;
   float* g_dump;       // optional
-  float* g_ws;         // optional [N][F] fp32 buffer: enables the small-batch gate (N <= 64, bf16)
+  float* g_ws;         // optional [N][F] fp32 buffer: enables the small-batch gate (N <= 64)
   int fp8;                // x and w hold E4M3 codes with per-row scales
   const float* x_scale;   // fp8: [N]
   const float* w_scale;   // fp8: [F]

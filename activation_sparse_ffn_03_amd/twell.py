@@ -28,7 +28,8 @@ _STATUS = {0: "TWELL_OK", 1: "TWELL_ERR_INVALID_ARG", 2: "TWELL_ERR_UNSUPPORTED"
 
 # Every symbol include/twell.h declares.
 EXPORTS = ("twell_status_str", "twell_last_error", "twell_n_tiles", "twell_query_sizes", "twell_gate_pack",
-           "twell_gate_pack_ws", "twell_pack_preact", "twell_quantize_e4m3", "twell_gate_pack_fp8", "twell_ffn_fwd",
+           "twell_gate_pack_ws", "twell_pack_preact", "twell_quantize_e4m3", "twell_gate_pack_fp8",
+           "twell_gate_pack_fp8_ws", "twell_ffn_fwd",
            "twell_route_hybrid", "twell_ffn_bwd", "twell_trace_start", "twell_trace_stop", "twell_trace_count",
            "twell_trace_dropped", "twell_trace_get")
 
@@ -95,6 +96,8 @@ def lib() -> ctypes.CDLL:
         L.twell_quantize_e4m3.argtypes = [ctypes.c_int64, i32, ctypes.c_int, vp, vp, vp, vp]
         L.twell_gate_pack_fp8.restype = ctypes.c_int
         L.twell_gate_pack_fp8.argtypes = [pd, vp, vp, vp, vp, vp, pp, vp, vp]
+        L.twell_gate_pack_fp8_ws.restype = ctypes.c_int
+        L.twell_gate_pack_fp8_ws.argtypes = [pd, vp, vp, vp, vp, vp, pp, vp, vp, sz, vp]
         L.twell_ffn_fwd.restype = ctypes.c_int
         L.twell_ffn_fwd.argtypes = [pd, ctypes.c_int, pp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.twell_route_hybrid.restype = ctypes.c_int
@@ -249,11 +252,21 @@ def quantize_e4m3(a, stream=None, out=None):
     return q, scale
 
 
-def gate_pack_fp8(dims: Dims, x_q, x_scale, w_q, w_scale, t, pack: TwellPack, g_dump=None, stream=None) -> None:
-    """Gate projection on FP8 operands + the TwELL pack (pack buffers of BF16)."""
+def gate_pack_fp8(dims: Dims, x_q, x_scale, w_q, w_scale, t, pack: TwellPack, g_dump=None, stream=None,
+                  ws=None) -> None:
+    """Gate projection on FP8 operands + the TwELL pack (pack buffers of BF16).
+    With ws (at least sizes["ws_gate"] bytes) small batches take the split
+    GEMV (twell_gate_pack_fp8_ws)."""
     p = pack.struct()
-    _check(lib().twell_gate_pack_fp8(ctypes.byref(dims), _ptr(x_q), _ptr(x_scale), _ptr(w_q), _ptr(w_scale),
-                                     _ptr(t), ctypes.byref(p), _ptr(g_dump), _stream(stream)), "twell_gate_pack_fp8")
+    if ws is None:
+        _check(lib().twell_gate_pack_fp8(ctypes.byref(dims), _ptr(x_q), _ptr(x_scale), _ptr(w_q), _ptr(w_scale),
+                                         _ptr(t), ctypes.byref(p), _ptr(g_dump), _stream(stream)),
+               "twell_gate_pack_fp8")
+    else:
+        nbytes = ws.numel() * ws.element_size()
+        _check(lib().twell_gate_pack_fp8_ws(ctypes.byref(dims), _ptr(x_q), _ptr(x_scale), _ptr(w_q), _ptr(w_scale),
+                                            _ptr(t), ctypes.byref(p), _ptr(g_dump), _ptr(ws), nbytes,
+                                            _stream(stream)), "twell_gate_pack_fp8_ws")
 
 
 def pack_preact(dims: Dims, dtype: int, g, t, pack: TwellPack, stream=None) -> None:
@@ -343,7 +356,8 @@ class TwellFFN:
         if self.fp8_gate:
             w_q, w_scale = w_gate_t
             quantize_e4m3(x, stream=stream, out=(self.x_q, self.x_scale))
-            gate_pack_fp8(self.dims, self.x_q, self.x_scale, w_q, w_scale, t, self.pack, g_dump=g_dump, stream=stream)
+            gate_pack_fp8(self.dims, self.x_q, self.x_scale, w_q, w_scale, t, self.pack, g_dump=g_dump, stream=stream,
+                          ws=self.ws_gate)
         else:
             gate_pack(self.dims, self.dtype, x, w_gate_t, t, self.pack, g_dump=g_dump, stream=stream, ws=self.ws_gate)
         ffn_fwd(self.dims, self.dtype, self.pack, x, w_up_t, w_down, self.y, a_save=self.a_save, ws=self.ws_fwd,

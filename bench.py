@@ -50,6 +50,9 @@ WORKLOADS = {
     "c2_dec64": ("c2", None, False, False, dict(N=64, slots=128)),
     "c3_dec1": ("c3", 0.01, False, False, dict(N=1, slots=128)),
     "c3_dec64": ("c3", 0.01, False, False, dict(N=64, slots=128)),
+    "c2_dec1_fp8": ("c2", None, False, True, dict(N=1, slots=128)),
+    "c3_dec1_fp8": ("c3", 0.01, False, True, dict(N=1, slots=128)),
+    "c3_dec64_fp8": ("c3", 0.01, False, True, dict(N=64, slots=128)),
 }
 
 

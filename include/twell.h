@@ -210,6 +210,18 @@ twell_status twell_gate_pack_fp8(const twell_dims* dims, const uint8_t* x_q, con
                                  const uint8_t* w_q, const float* w_scale, const float* t,
                                  const twell_pack* out, float* g_dump, void* stream);
 
+/* twell_gate_pack_fp8 for small batches, with a workspace: for
+ * 1 <= N <= TWELL_SMALL_BATCH_MAX the FP8 gate runs as the split GEMV of
+ * twell_gate_pack_ws (same instruction and per-step k split as the GEMM,
+ * 8 d_model ranges added in a fixed order, then the two scales), g goes
+ * through ws (or g_dump when given) into the same pack and overflow rows.
+ * ws: at least twell_sizes.ws_gate bytes of the TWELL_BF16 sizes. Otherwise
+ * exactly twell_gate_pack_fp8; errors as there, plus TWELL_ERR_WORKSPACE. */
+twell_status twell_gate_pack_fp8_ws(const twell_dims* dims, const uint8_t* x_q, const float* x_scale,
+                                    const uint8_t* w_q, const float* w_scale, const float* t,
+                                    const twell_pack* out, float* g_dump, void* ws, size_t ws_bytes,
+                                    void* stream);
+
 /* Stage 2: fused up + down projection from TwELL.
  *   y_i = sum over active (i,c) of h_ic · (x_i · w_up_t[c]) · w_down[c]
  * with h read from TwELL (or from ovf_h for overflow rows); z = h·a is kept in

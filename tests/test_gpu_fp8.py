@@ -211,3 +211,79 @@ def test_runner_fp8_gate_matches_calls():
         rowwise_ok(f64(y), orc.sparse_forward(pk, x, wu, wd, ovf_h=hq[pk["ovf_rows"]]), 1e-4, "y (runner)")
     with pytest.raises(ValueError):
         tw.TwellFFN(dims, tw.F32, fp8_gate=True)
+
+
+@pytest.mark.parametrize("N", [1, 7, 33, 64])
+def test_small_batch_fp8_gate_exact_grid(N):
+    """The split-GEMV FP8 gate (gate_pack_fp8 with a workspace) on operands
+    whose FP8 gate is exact: g, TwELL and the overflow rows bit-exact."""
+    require_gpu()
+    D, F, tile_n, slots = 512, 1000, 128, 4
+    rng = np.random.default_rng(100 + N)
+    xq, wq = _grid_codes(rng, (N, D)), _grid_codes(rng, (F, D))
+    sx = np.exp2(rng.integers(-3, 3, N)).astype(np.float32)
+    sw = np.exp2(rng.integers(-3, 3, F)).astype(np.float32)
+    g = orc.gate_preact_fp8(xq, sx, wq, sw)
+    t = orc.margin_thresholds(g, 0.05)
+    dims = tw.make_dims(N, D, F, tile_n, slots, 0, N, 0)
+    ws = tw.alloc_workspace(tw.query_sizes(dims, tw.BF16)["ws_gate"])
+    pack = tw.alloc_pack(dims, tw.BF16)
+    gd = torch.empty((N, F), dtype=torch.float32, device="cuda")
+    cu = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    tw.gate_pack_fp8(dims, cu(xq), cu(sx), cu(wq), cu(sw), cu(t), pack, g_dump=gd, ws=ws)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(gd.cpu().numpy().astype(np.float64), g)
+    pk = orc.pack(g, t, tile_n, slots, store="bf16", arith="f32")
+    check_pack(pack, pk, N)
+    hq = orc.dense_activation(g, t, store="bf16", arith="f32")
+    n = min(pk["n_ovf"], N)
+    np.testing.assert_array_equal(f64(pack.ovf_h[:n]), hq[pk["ovf_rows"][:n]])
+
+
+@pytest.mark.parametrize("N", [1, 40])
+def test_small_batch_fp8_gate_random_within_bound(N):
+    require_gpu()
+    rng = np.random.default_rng(200 + N)
+    D, F = 1024, 520
+    x = _bf16_exact(rng.standard_normal((N, D)))
+    w = _bf16_exact(rng.standard_normal((F, D)) / np.sqrt(D))
+    rxq, rsx = orc.quantize_rows_e4m3(x)
+    rwq, rsw = orc.quantize_rows_e4m3(w)
+    g = orc.gate_preact_fp8(rxq, rsx, rwq, rsw)
+    dims = tw.make_dims(N, D, F, 128, 16, 0, N, 0)
+    ws = tw.alloc_workspace(tw.query_sizes(dims, tw.BF16)["ws_gate"])
+    pack = tw.alloc_pack(dims, tw.BF16)
+    gd = torch.empty((N, F), dtype=torch.float32, device="cuda")
+    cu = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    tw.gate_pack_fp8(dims, cu(rxq), cu(rsx), cu(rwq), cu(rsw), cu(np.full(N, 1e30, np.float32)), pack,
+                     g_dump=gd, ws=ws)
+    torch.cuda.synchronize()
+    err = np.abs(gd.cpu().numpy().astype(np.float64) - g)
+    bound = fp8_gate_err_bound(rxq, rsx, rwq, rsw, g)
+    assert (err <= bound).all(), float((err / bound).max())
+
+
+def test_runner_fp8_gate_small_batch():
+    """TwellFFN(fp8_gate=True) at one token uses the small-batch FP8 gate:
+    y against the oracle on an exactly quantisable row."""
+    require_gpu()
+    rng = np.random.default_rng(43)
+    N, D, F = 1, 512, 2048
+    x = _fp8_exact_rows(rng, N, D, -8, -4)
+    wg = _fp8_exact_rows(rng, F, D, -12, -8)
+    wu = _bf16_exact(rng.standard_normal((F, D)) / np.sqrt(D))
+    wd = _bf16_exact(rng.standard_normal((F, D)) / np.sqrt(F))
+    rxq, rsx = orc.quantize_rows_e4m3(x)
+    rwq, rsw = orc.quantize_rows_e4m3(wg)
+    g = orc.gate_preact_fp8(rxq, rsx, rwq, rsw)
+    t = orc.margin_thresholds(g, 0.03)
+    cu = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    dims = tw.make_dims(N, D, F, 128, 128, 0, 8, 0)
+    ffn = tw.TwellFFN(dims, tw.BF16, fp8_gate=True)
+    assert ffn.ws_gate is not None
+    y = ffn.forward(cu(x).to(torch.bfloat16), tw.quantize_e4m3(cu(wg).to(torch.bfloat16)),
+                    cu(wu).to(torch.bfloat16), cu(wd).to(torch.bfloat16), cu(t))
+    torch.cuda.synchronize()
+    pk = orc.pack(g, t, 128, 128, store="bf16", arith="f32")
+    check_pack(ffn.pack, pk, 8)
+    rowwise_ok(f64(y), orc.sparse_forward(pk, x, wu, wd), 1e-4, "y (small-batch FP8 gate)")
