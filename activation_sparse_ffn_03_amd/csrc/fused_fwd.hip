@@ -121,10 +121,12 @@ __device__ __forceinline__ int entries_before_rest(const FwdArgs& a, int64_t i, 
 // L2 at a time), four tokens of the block row. With one range the wave stores
 // (c, z = h*a) and a_save itself; with several it stores its partial a, range
 // 0 also (c, h) and the entry's slot, and ffn_up_finish adds the ranges.
-template <typename TS, int M>
+template <typename TS, int M, bool SMALL>
 __global__ __launch_bounds__(256) void ffn_up_kernel(FwdArgs a, int parts, int64_t tblocks, int64_t i0, int64_t i1) {
   constexpr int E = ChunkElems<TS>::E;
-  constexpr int U = M <= 4 ? 2 : 1;  // rows in flight per wave (more costs occupancy: measured slower)
+  // rows in flight per wave: more costs occupancy, measured slower on large
+  // batches; small batches (few waves, weight rows from HBM) take more
+  constexpr int U = SMALL ? (M <= 4 ? 8 : (M == 8 ? 4 : 2)) : (M <= 4 ? 2 : 1);
   const int lane = threadIdx.x & 63;
   const int part = blockIdx.x % parts;
   const int64_t r = blockIdx.x / parts;
@@ -213,10 +215,12 @@ __global__ __launch_bounds__(256) void ffn_up_finish(FwdArgs a, int64_t i0, int6
 // Wave per (row i, d_model slice p); the slice is read 16 bytes per lane, so a
 // load instruction covers RPI rows of W_down (see pick_l2_slices). Slices go
 // G8 at a time (slice_block), so an XCD holds one slice of W_down at a time.
-template <typename TS, int EPL, int RPI>
+template <typename TS, int EPL, int RPI, bool SMALL>
 __global__ __launch_bounds__(256) void ffn_down_kernel(FwdArgs a, int G8, int64_t tblocks, int64_t i0, int64_t i1) {
   constexpr int LPR = 64 / RPI;
-  constexpr int U = sliced_inflight<RPI>();
+  // load instructions in flight; small batches take more (the entry order of
+  // the sums is the same either way)
+  constexpr int U = SMALL ? (RPI <= 4 ? 16 : 64 / RPI) : sliced_inflight<RPI>();
   const int lane = threadIdx.x & 63;
   int p;
   int64_t rb;
@@ -334,6 +338,8 @@ __global__ __launch_bounds__(256) void dense_reduce(const float* __restrict__ pa
 
 // Token rows per pair of up / down launches (0 = all rows in one pair).
 constexpr int64_t kTokenChunk = 0;
+// Up to this many rows the up / down launches use their small-batch forms.
+constexpr int64_t kSmallRows = 64;
 
 template <typename TS>
 hipError_t launch_sparse_rows(const FwdArgs& a, hipStream_t s, int64_t chunk) {
@@ -354,9 +360,14 @@ hipError_t launch_sparse_rows(const FwdArgs& a, hipStream_t s, int64_t chunk) {
     const int64_t i1 = i0 + chunk < a.N ? i0 + chunk : a.N;
     const int64_t tblocks = (i1 - i0 + 3) / 4;
     const dim3 gup((unsigned)(tblocks * parts * a.up_nq));
-#define TWELL_UP(MM) \
-  case MM:           \
-    TWELL_LAUNCH("ffn_up_kernel", (ffn_up_kernel<TS, MM>), gup, blk, 0, s, a, parts, tblocks, i0, i1); break;
+    const bool small = i1 - i0 <= kSmallRows;
+#define TWELL_UP(MM)                                                                                          \
+  case MM:                                                                                                    \
+    if (small)                                                                                                \
+      TWELL_LAUNCH("ffn_up_kernel", (ffn_up_kernel<TS, MM, true>), gup, blk, 0, s, a, parts, tblocks, i0, i1); \
+    else                                                                                                      \
+      TWELL_LAUNCH("ffn_up_kernel", (ffn_up_kernel<TS, MM, false>), gup, blk, 0, s, a, parts, tblocks, i0, i1); \
+    break;
     switch (Mq) {
       TWELL_UP(1) TWELL_UP(2) TWELL_UP(4) TWELL_UP(8) TWELL_UP(16)
       default: return hipErrorInvalidValue;
@@ -368,8 +379,11 @@ hipError_t launch_sparse_rows(const FwdArgs& a, hipStream_t s, int64_t chunk) {
       if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     const dim3 gdn((unsigned)(tblocks * P));
-#define TWELL_DOWN(E, R) \
-  TWELL_LAUNCH("ffn_down_kernel", (ffn_down_kernel<TS, E, R>), gdn, blk, 0, s, a, G8, tblocks, i0, i1)
+#define TWELL_DOWN(E, R)                                                                                    \
+  if (small)                                                                                                \
+    TWELL_LAUNCH("ffn_down_kernel", (ffn_down_kernel<TS, E, R, true>), gdn, blk, 0, s, a, G8, tblocks, i0, i1); \
+  else                                                                                                      \
+    TWELL_LAUNCH("ffn_down_kernel", (ffn_down_kernel<TS, E, R, false>), gdn, blk, 0, s, a, G8, tblocks, i0, i1)
     if constexpr (sizeof(TS) == 2) {
       TWELL_SLICED_CASES(8, TWELL_DOWN)
     } else {
