@@ -78,7 +78,9 @@ class TwellFFNFunction(torch.autograd.Function):
         y = torch.empty((N, D), dtype=torch.float32, device=dev)
         a_save = torch.empty(sizes["a_save"] // 4, dtype=torch.float32, device=dev) if train else None
         ws = tw.alloc_workspace(sizes["ws_fwd"], dev)
-        tw.gate_pack(dims, dt, x, w_gate_t, t, pack)
+        # small batches (bf16, up to TWELL_SMALL_BATCH_MAX tokens): the split-GEMV gate
+        ws_gate = tw.alloc_workspace(sizes["ws_gate"], dev) if sizes["ws_gate"] else None
+        tw.gate_pack(dims, dt, x, w_gate_t, t, pack, ws=ws_gate)
         tw.ffn_fwd(dims, dt, pack, x, w_up_t, w_down, y, a_save=a_save, ws=ws)
         if cfg.check and int(pack.status.item()) != 0:
             raise tw.TwellError(_ERR_CAPACITY, "TwellFFNFunction",

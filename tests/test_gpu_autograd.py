@@ -90,3 +90,37 @@ def test_module_trains_and_two_forwards_before_backward():
         ref = ga + gb
         err = (gab - ref).abs().max().item()
         assert err <= 2 ** -6 * ref.abs().max().item(), err
+
+
+@pytest.mark.parametrize("N,train", [(1, False), (40, False), (32, True)])
+def test_autograd_small_batches(N, train):
+    """At <= 64 bf16 tokens the wrapper's forward takes the split-GEMV gate;
+    on exact (grid) inputs y and, when training, the gradients still match the
+    oracle to fp32 accuracy."""
+    require_gpu()
+    w = make_inputs("c5", seed=N, N=N, D=256, F=1024, row_cap=24, grid=True)
+    w.dy = np.random.default_rng(N).integers(-16, 17, (w.N, w.D)).astype(np.float32) / 8
+
+    def dev(a, grad=False):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda().to(torch.bfloat16).requires_grad_(grad)
+
+    x, wg, wu, wd = (dev(a, train) for a in (w.x, w.w_gate_t, w.w_up_t, w.w_down))
+    t = torch.from_numpy(w.t.astype(np.float32)).cuda()
+    cfg = TwellConfig(tile_n=w.tile_n, slots=w.slots, row_cap=w.row_cap, ovf_frac=1.0, dense_frac=1.0)
+    fw = orc.ffn_forward(w.x, w.w_gate_t, w.w_up_t, w.w_down, w.t, store="bf16", arith="f32")
+    if not train:
+        with torch.no_grad():
+            y = TwellFFNFunction.apply(x, wg, wu, wd, t, w.lam, cfg)
+        torch.cuda.synchronize()
+        rowwise_ok(f64(y), fw["y"], 1e-4, "y")
+        return
+    y = TwellFFNFunction.apply(x, wg, wu, wd, t, w.lam, cfg)
+    (y * torch.from_numpy(w.dy).cuda()).sum().backward()
+    torch.cuda.synchronize()
+    rowwise_ok(f64(y), fw["y"], 1e-4, "y")
+    bw = orc.ffn_backward(w.x, w.dy, w.w_gate_t, w.w_up_t, w.w_down, fw["mask"], fw["hq"], w.lam)
+    for k, g in {"dx": x.grad, "dw_gate_t": wg.grad, "dw_up_t": wu.grad, "dw_down": wd.grad}.items():
+        ref, gg = bw[k], f64(g)
+        rms = np.sqrt(np.mean(ref * ref, axis=1, keepdims=True))
+        bad = np.abs(gg - ref) > 2.0 ** -8 * np.abs(ref) + 1e-4 * rms
+        assert not bad.any(), f"{k}: {int(bad.sum())} elements beyond one bf16 step"
