@@ -77,29 +77,19 @@ twell_status twell_query_sizes(const twell_dims* dims, twell_dtype dtype, twell_
   return prepare(dims, dtype, &s, out);
 }
 
-static twell_status gate_common(const twell_dims* dims, twell_dtype dtype, const void* x, const void* w_gate_t,
-                                const float* g_in, const float* t, const twell_pack* out, float* g_dump,
-                                void* ws, size_t ws_bytes, bool use_ws, void* stream) {
-  twell::Shape s;
-  twell_sizes z;
-  twell_status st = prepare(dims, dtype, &s, &z);
-  if (st != TWELL_OK) return st;
-  if (use_ws && z.ws_gate > 0) {
-    if (ws_bytes < z.ws_gate) return fail(TWELL_ERR_WORKSPACE, "gate workspace smaller than twell_sizes.ws_gate");
-    TWELL_CHECK_PTR(ws, z.ws_gate, "ws");
-  }
-  const size_t xd = (size_t)s.N * s.D * s.esz, wd = (size_t)s.F * s.D * s.esz;
-  if (g_in == nullptr) {
-    TWELL_CHECK_PTR(x, xd, "x");
-    TWELL_CHECK_PTR(w_gate_t, wd, "w_gate_t");
-  } else {
-    TWELL_CHECK_PTR(g_in, (size_t)s.N * s.F * 4, "g");
-  }
-  TWELL_CHECK_PTR(t, (size_t)s.N * 4, "t");
-  if ((st = check_pack(out, z)) != TWELL_OK) return st;
-  if (g_dump != nullptr) TWELL_CHECK_PTR(g_dump, (size_t)s.N * s.F * 4, "g_dump");
-  if (s.N == 0) return TWELL_OK;
+// Workspace of the small-batch gate (twell_sizes.ws_gate bytes; none needed
+// when that is 0 or the caller did not take the _ws entry point).
+static twell_status check_gate_ws(const twell_sizes& z, void* ws, size_t ws_bytes, bool use_ws) {
+  if (!use_ws || z.ws_gate == 0) return TWELL_OK;
+  if (ws_bytes < z.ws_gate) return fail(TWELL_ERR_WORKSPACE, "gate workspace smaller than twell_sizes.ws_gate");
+  TWELL_CHECK_PTR(ws, z.ws_gate, "ws");
+  return TWELL_OK;
+}
 
+// The launch arguments every gate entry point shares: shape, thresholds, the
+// pack's outputs, the optional g copy and the small-batch workspace.
+static twell::GateArgs gate_args(const twell::Shape& s, const twell_sizes& z, const float* t, const twell_pack* out,
+                                 float* g_dump, void* ws, bool use_ws) {
   twell::GateArgs a{};
   a.N = s.N;
   a.D = s.D;
@@ -107,10 +97,6 @@ static twell_status gate_common(const twell_dims* dims, twell_dtype dtype, const
   a.tile_n = s.tile_n;
   a.slots = s.slots;
   a.n_tiles = s.n_tiles;
-  a.is_bf16 = dtype == TWELL_BF16;
-  a.x = x;
-  a.w = w_gate_t;
-  a.g_in = g_in;
   a.t = t;
   a.vals = out->vals;
   a.cols = out->cols;
@@ -123,6 +109,34 @@ static twell_status gate_common(const twell_dims* dims, twell_dtype dtype, const
   a.ovf_cap = s.ovf_cap;
   a.g_dump = g_dump;
   a.g_ws = (use_ws && z.ws_gate > 0) ? static_cast<float*>(ws) : nullptr;
+  return a;
+}
+
+static twell_status gate_common(const twell_dims* dims, twell_dtype dtype, const void* x, const void* w_gate_t,
+                                const float* g_in, const float* t, const twell_pack* out, float* g_dump,
+                                void* ws, size_t ws_bytes, bool use_ws, void* stream) {
+  twell::Shape s;
+  twell_sizes z;
+  twell_status st = prepare(dims, dtype, &s, &z);
+  if (st != TWELL_OK) return st;
+  if ((st = check_gate_ws(z, ws, ws_bytes, use_ws)) != TWELL_OK) return st;
+  const size_t xd = (size_t)s.N * s.D * s.esz, wd = (size_t)s.F * s.D * s.esz;
+  if (g_in == nullptr) {
+    TWELL_CHECK_PTR(x, xd, "x");
+    TWELL_CHECK_PTR(w_gate_t, wd, "w_gate_t");
+  } else {
+    TWELL_CHECK_PTR(g_in, (size_t)s.N * s.F * 4, "g");
+  }
+  TWELL_CHECK_PTR(t, (size_t)s.N * 4, "t");
+  if ((st = check_pack(out, z)) != TWELL_OK) return st;
+  if (g_dump != nullptr) TWELL_CHECK_PTR(g_dump, (size_t)s.N * s.F * 4, "g_dump");
+  if (s.N == 0) return TWELL_OK;
+
+  twell::GateArgs a = gate_args(s, z, t, out, g_dump, ws, use_ws);
+  a.is_bf16 = dtype == TWELL_BF16;
+  a.x = x;
+  a.w = w_gate_t;
+  a.g_in = g_in;
   return hip_status(twell::launch_gate_pack(a, (hipStream_t)stream), "twell_gate_pack");
 }
 
@@ -158,10 +172,7 @@ static twell_status fp8_common(const twell_dims* dims, const uint8_t* x_q, const
   twell_sizes z;
   twell_status st = prepare(dims, TWELL_BF16, &s, &z);
   if (st != TWELL_OK) return st;
-  if (use_ws && z.ws_gate > 0) {
-    if (ws_bytes < z.ws_gate) return fail(TWELL_ERR_WORKSPACE, "gate workspace smaller than twell_sizes.ws_gate");
-    TWELL_CHECK_PTR(ws, z.ws_gate, "ws");
-  }
+  if ((st = check_gate_ws(z, ws, ws_bytes, use_ws)) != TWELL_OK) return st;
   if (s.D % 64 != 0) return fail(TWELL_ERR_UNSUPPORTED, "the FP8 gate needs d_model to be a multiple of 64");
   TWELL_CHECK_PTR(x_q, (size_t)s.N * s.D, "x_q");
   TWELL_CHECK_PTR(x_scale, (size_t)s.N * 4, "x_scale");
@@ -171,31 +182,13 @@ static twell_status fp8_common(const twell_dims* dims, const uint8_t* x_q, const
   if ((st = check_pack(out, z)) != TWELL_OK) return st;
   if (g_dump != nullptr) TWELL_CHECK_PTR(g_dump, (size_t)s.N * s.F * 4, "g_dump");
   if (s.N == 0) return TWELL_OK;
-  twell::GateArgs a{};
-  a.N = s.N;
-  a.D = s.D;
-  a.F = s.F;
-  a.tile_n = s.tile_n;
-  a.slots = s.slots;
-  a.n_tiles = s.n_tiles;
+  twell::GateArgs a = gate_args(s, z, t, out, g_dump, ws, use_ws);
   a.is_bf16 = 1;  // TwELL values and overflow rows are stored in bf16
   a.fp8 = 1;
   a.x = x_q;
   a.w = w_q;
   a.x_scale = x_scale;
   a.w_scale = w_scale;
-  a.t = t;
-  a.vals = out->vals;
-  a.cols = out->cols;
-  a.counts = out->counts;
-  a.ovf_flag = out->ovf_flag;
-  a.ovf_rows = out->ovf_rows;
-  a.ovf_h = out->ovf_h;
-  a.n_ovf = out->n_ovf;
-  a.status = out->status;
-  a.ovf_cap = s.ovf_cap;
-  a.g_dump = g_dump;
-  a.g_ws = (use_ws && z.ws_gate > 0) ? static_cast<float*>(ws) : nullptr;
   return hip_status(twell::launch_gate_pack(a, (hipStream_t)stream), "twell_gate_pack_fp8");
 }
 
