@@ -75,6 +75,8 @@ def parse():
     p.add_argument("--cpu-sample", type=int, default=512, help="tokens per window of the CPU oracle sample")
     p.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of CPU oracle work")
     p.add_argument("--copy-calib", action="store_true", help="only run the copy kernel used to scale HBM counters")
+    p.add_argument("--traffic-pass", choices=("sparse", "dense"),
+                   help="only run warmup + steps of one path, untimed (for the HBM counter runs)")
     return p.parse_args()
 
 
@@ -131,6 +133,60 @@ def kernel_work(name, w, st, train):
         byt = N * D * e + nnz * 16 + 2 * F * D * 4
         return {"flops": 4.0 * D * nnz, "bytes": byt, "bound": "hbm"}
     return None
+
+
+def step_work(w, st, train, kernel_names):
+    """Algorithmic FLOPs and bytes of one step, for libtwell and for the dense
+    bf16 FFN of the same shape. libtwell: the sum of kernel_work over the
+    step's main kernels, plus the gate rows of the overflow rows, which are
+    recomputed (2 D F FLOP each). Dense: 6 N D F FLOP (18 N D F for a training
+    step); bytes are x, the three weights and the [N x F] hidden state written
+    and read once in bf16, plus y in bf16 (for a training step also dy, the
+    weights and the hidden state again, dx and the three weight gradients in
+    fp32)."""
+    N, D, F, e = w.N, w.D, w.F, 2
+    fl = 2.0 * st["n_ovf"] * D * F
+    by = 0.0
+    for k in kernel_names:
+        wk = kernel_work(k, w, st, train)
+        if wk:
+            fl += wk["flops"]
+            by += wk["bytes"]
+    dfl = 6.0 * N * D * F
+    dby = N * D * e + 3 * F * D * e + 2 * N * F * e + N * D * e
+    if train:
+        dfl = 18.0 * N * D * F
+        dby += N * D * e + 3 * F * D * e + 2 * N * F * e + N * D * 4 + 3 * F * D * 4
+    return {"flops": fl, "bytes": by, "dense_flops": dfl, "dense_bytes": dby}
+
+
+def measured_step_traffic(workload):
+    """HBM bytes per step of libtwell and of the dense baseline from the
+    committed counter summary (every kernel of one step, FETCH_SIZE +
+    WRITE_SIZE scaled by the copy-kernel calibration), or None if there is
+    none or a kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"step_traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#") and not line.startswith("|"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha256_16") != all_sources_hash():
+        return None
+    return {"sparse": float(kv["sparse_hbm_bytes_per_step"]), "dense": float(kv["dense_hbm_bytes_per_step"])}
+
+
+def all_sources_hash():
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "activation_sparse_ffn_03_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def cpu_baseline(w, train, sample, budget_s=10.0, fp8=False):
@@ -273,6 +329,37 @@ def main():
         if train:
             ffn.backward(x, dy, wg, wu, wd, w.lam)
 
+    lam = w.lam
+
+    # dense bf16 FFN on the same GPU and inputs (torch / hipBLASLt), same step definition
+    def dense_step():
+        g = torch.nn.functional.linear(x, wg)
+        a = torch.nn.functional.linear(x, wu)
+        m = g > t[:, None]
+        h = torch.where(m, g - t[:, None].to(g.dtype), torch.zeros((), dtype=g.dtype, device=dev))
+        z = h * a
+        y = torch.mm(z, wd)
+        if train:
+            dz = torch.nn.functional.linear(dy, wd)
+            dwd = torch.mm(z.t(), dy)
+            da = dz * h
+            dg = torch.where(m, dz * a + lam, torch.zeros((), dtype=g.dtype, device=dev))
+            dx = torch.mm(da, wu) + torch.mm(dg, wg)
+            dwu = torch.mm(da.t(), x)
+            dwg = torch.mm(dg.t(), x)
+            return y, dx, dwd, dwu, dwg
+        return y
+
+    if args.traffic_pass:
+        # counter runs: warmup + steps of one path only, nothing timed
+        fn = step if args.traffic_pass == "sparse" else dense_step
+        for _ in range(args.warmup + args.steps):
+            fn()
+        torch.cuda.synchronize()
+        print(json.dumps({"traffic_pass": args.traffic_pass, "workload": args.workload,
+                          "steps_run": args.warmup + args.steps}), flush=True)
+        return
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -347,29 +434,8 @@ def main():
         kernels[k]["GBps_algorithmic"] = wk_k["bytes"] / s_k / 1e9
         kernels[k]["TFLOPs"] = wk_k["flops"] / s_k / 1e12
 
-    # dense bf16 FFN on the same GPU and inputs (torch / hipBLASLt), same step definition
     dense = dense_graph_ms = None
     if not args.no_dense:
-        lam = w.lam
-
-        def dense_step():
-            g = torch.nn.functional.linear(x, wg)
-            a = torch.nn.functional.linear(x, wu)
-            m = g > t[:, None]
-            h = torch.where(m, g - t[:, None].to(g.dtype), torch.zeros((), dtype=g.dtype, device=dev))
-            z = h * a
-            y = torch.mm(z, wd)
-            if train:
-                dz = torch.nn.functional.linear(dy, wd)
-                dwd = torch.mm(z.t(), dy)
-                da = dz * h
-                dg = torch.where(m, dz * a + lam, torch.zeros((), dtype=g.dtype, device=dev))
-                dx = torch.mm(da, wu) + torch.mm(dg, wg)
-                dwu = torch.mm(da.t(), x)
-                dwg = torch.mm(dg.t(), x)
-                return y, dx, dwd, dwu, dwg
-            return y
-
         for _ in range(args.warmup):
             dense_step()
         torch.cuda.synchronize()
@@ -421,6 +487,18 @@ def main():
     del flush_buf
 
     flops_dense = 6.0 * w.N * w.D * w.F * (3 if train else 1)
+    # work and HBM bytes of one step against the dense FFN of the same shape
+    sw = step_work(w, stats, train, list(kernels))
+    meas = measured_step_traffic(args.workload)
+    vs_dense = {
+        "flops": {"twell": sw["flops"], "dense": sw["dense_flops"], "saved_frac": 1 - sw["flops"] / sw["dense_flops"]},
+        "bytes_algorithmic": {"twell": sw["bytes"], "dense": sw["dense_bytes"],
+                              "saved_frac": 1 - sw["bytes"] / sw["dense_bytes"]},
+        "hbm_bytes_measured": None if meas is None else
+        {"twell": meas["sparse"], "dense": meas["dense"], "saved_frac": 1 - meas["sparse"] / meas["dense"],
+         "twell_GBps": meas["sparse"] / (ms / 1e3) / 1e9,
+         "dense_GBps": (meas["dense"] / (dense / 1e3) / 1e9) if dense else None},
+    }
     out = {
         "metric": METRIC,
         "value": w.N / (ms / 1e3),
@@ -445,6 +523,7 @@ def main():
         "dense_step_ms": dense_step_ms,
         "dense_equivalent_tflops": flops_dense / (ms / 1e3) / 1e12,
         "roofline": roof,
+        "vs_dense": vs_dense,
         "kernels": kernels,
         "workload_stats": {**stats, "density": nnz / (w.N * w.F)},
         "wall_s_timed": wall,
