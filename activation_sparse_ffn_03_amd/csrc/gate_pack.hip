@@ -7,9 +7,9 @@
 // conversion pass, no extra round trip through global memory).
 //
 // Kernels
-//   gate_mfma_dma    TwELL pack path (bf16): 128x384 output tile per 4-wave
+//   gate_mfma_dma    TwELL pack path (bf16): 256x384 output tile per 8-wave
 //                    workgroup, v_mfma_f32_16x16x32_bf16, K-steps of 32 loaded
-//                    straight into a 2-stage LDS ring by global_load_lds;
+//                    straight into a 2- or 3-stage LDS ring by global_load_lds;
 //                    XCD-aware tile order; the epilogue stages the fp32 tile in
 //                    LDS one 128-column group at a time and packs it.
 //   gate_mfma_bf16   register-staged variant (128x128, K-steps of 64), used to
@@ -445,11 +445,11 @@ struct DmaCfg {
   static constexpr int RING = ST * STAGE;
   static constexpr int GROUPS = (BM + BN) / 16;      // 1 KB DMA groups per stage
   static constexpr int GPW = GROUPS / NW;            // DMA instructions per wave per stage
-  // The epilogue stages min(BM, 128) rows of fp32 g at a time in the same LDS
-  // (more rows per pass keep all waves of the pack busy; a 128-row pass needs
-  // a little more LDS than a 128x384 ring holds, which still leaves room for
-  // two workgroups per CU).
-  static constexpr int EPI_ROWS = BM >= 128 ? 128 : 64;
+  // The epilogue stages min(BM, 256) rows of fp32 g at a time in the same LDS
+  // (32 rows per wave, so every wave of an 8-wave 256-row tile packs in one
+  // pass per 128-column group; that staging, 132 KB, is larger than the
+  // operand ring, so the ring can take a third stage at no LDS cost).
+  static constexpr int EPI_ROWS = BM >= 256 ? 256 : (BM >= 128 ? 128 : 64);
   static constexpr int LDS = RING > EPI_ROWS * GS * 4 ? RING : EPI_ROWS * GS * 4;
   static_assert(WM % 16 == 0 && WN % 16 == 0 && BM % 16 == 0 && BN % 16 == 0, "whole fragments");
   static_assert(GROUPS % NW == 0, "DMA groups must split evenly over waves");
@@ -625,18 +625,25 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gate_mfma_dma(const void* __res
   }
 }
 
-// Tile configurations of the bf16 gate GEMM. Both accumulate each output
+// Tile configurations of the bf16 gate GEMM. All accumulate each output
 // element over K in the same order (32-wide MFMA steps, ascending K), so they
-// produce bit-identical g: the TwELL pack uses the LDS-DMA kernel with a
-// 128x384 tile (four waves of 128x96, two workgroups per CU; a 256x384 tile
-// of eight waves runs its main loop faster but its pack epilogue, with two of
-// eight waves busy per 128-row pass, costs more than that gains), the
-// overflow rows the register-staged kernel (a few rows, gathered): 64x128
+// produce bit-identical g. The TwELL pack uses the LDS-DMA kernel with a
+// 256x384 tile: eight waves of 128x96 (two per SIMD), one workgroup per CU,
+// the pack epilogue in 256-row passes with every wave busy. Its operand ring
+// has three stages (GatePack) when the grid is several waves of tiles deep,
+// two (GatePackOne) when every tile fits in one wave of workgroups (measured
+// on the 4096 x 5632 x 2048 gate: 92 us with two stages, 95 with three, 101
+// for the earlier 128x384 tile of four waves at two workgroups per CU; on the
+// 16384 x 11008 x 4096 gate 1.25 ms with three stages, 1.29 with two). The
+// overflow rows use the register-staged kernel (a few rows, gathered): 64x128
 // tiles for d_model <= 2048 (half the padding rows of a 128-row tile), 128x128
 // above (with a long K the better operand reuse of the larger wave tiles wins;
 // measured 46 -> 35 us at d_model 2048 and 80 -> 109 us at 4096 for 64-row
 // tiles).
-using GatePack = DmaCfg<128, 384, 1, 4, 2, 2>;
+using GatePack = DmaCfg<256, 384, 2, 4, 3, 1>;
+using GatePackOne = DmaCfg<256, 384, 2, 4, 2, 1>;
+static_assert(GatePack::BM == GatePackOne::BM && GatePack::BN == GatePackOne::BN, "same tile grid");
+constexpr int kCus = 256;  // compute units of an MI355X: workgroups of one wave of GatePack tiles
 using GateRowsS = MfmaCfg<64, 128, 1, 4>;
 using GateRowsL = MfmaCfg<128, 128, 2, 2>;
 
@@ -934,7 +941,11 @@ hipError_t launch_gate_pack(const GateArgs& a, hipStream_t s) {
   e.mode = MODE_PACK;
   if (a.fp8 && g_in == nullptr) {
     const int mbc = (int)((a.N + GatePack::BM - 1) / GatePack::BM), nbc = (a.F + GatePack::BN - 1) / GatePack::BN;
-    TWELL_LAUNCH("gate_mfma_fp8", (gate_mfma_dma<GatePack, MODE_PACK, true>), dim3(mbc * nbc), GatePack::NT, 0, s,
+    if ((int64_t)mbc * nbc <= kCus)
+      TWELL_LAUNCH("gate_mfma_fp8", (gate_mfma_dma<GatePackOne, MODE_PACK, true>), dim3(mbc * nbc), GatePackOne::NT,
+                   0, s, a.x, a.w, a.D, mbc, nbc, e);
+    else
+      TWELL_LAUNCH("gate_mfma_fp8", (gate_mfma_dma<GatePack, MODE_PACK, true>), dim3(mbc * nbc), GatePack::NT, 0, s,
                  a.x, a.w, a.D, mbc, nbc, e);
   } else if (g_in) {
     const int64_t mb = (a.N + SBM - 1) / SBM;
@@ -944,7 +955,11 @@ hipError_t launch_gate_pack(const GateArgs& a, hipStream_t s) {
       TWELL_LAUNCH("pack_from_g", (pack_from_g<float, MODE_PACK>), dim3(mb * ncb), 256, 0, s, g_in, ncb, e);
   } else if (a.is_bf16) {
     const int mbc = (int)((a.N + GatePack::BM - 1) / GatePack::BM), nbc = (a.F + GatePack::BN - 1) / GatePack::BN;
-    TWELL_LAUNCH("gate_mfma_bf16", (gate_mfma_dma<GatePack, MODE_PACK>), dim3(mbc * nbc), GatePack::NT, 0, s,
+    if ((int64_t)mbc * nbc <= kCus)
+      TWELL_LAUNCH("gate_mfma_bf16", (gate_mfma_dma<GatePackOne, MODE_PACK>), dim3(mbc * nbc), GatePackOne::NT, 0, s,
+                   (const uint16_t*)a.x, (const uint16_t*)a.w, a.D, mbc, nbc, e);
+    else
+      TWELL_LAUNCH("gate_mfma_bf16", (gate_mfma_dma<GatePack, MODE_PACK>), dim3(mbc * nbc), GatePack::NT, 0, s,
                  (const uint16_t*)a.x, (const uint16_t*)a.w, a.D, mbc, nbc, e);
   } else {
     const int64_t mb = (a.N + SBM - 1) / SBM;

@@ -381,7 +381,10 @@ def main():
     # the forward replayed from a HIP graph (the serving-loop form: no host
     # launch cost per kernel); same inputs, same K steps
     graph_ms = None
-    if not train and not args.no_graph:
+    # graph replays are timed for the uniform-density forwards; the
+    # skewed-density forward is timed eagerly only
+    replay = not train and not args.no_graph and w.density[0] == "uniform"
+    if replay:
         graph = ffn.capture(x, wgate, wu, wd, t)
         for _ in range(args.warmup):
             graph.replay()
@@ -446,7 +449,7 @@ def main():
         d1.record(stream)
         torch.cuda.synchronize()
         dense = d0.elapsed_time(d1) / args.steps
-        if not train and not args.no_graph:   # the dense forward replayed from a graph as well
+        if replay:   # the dense forward replayed from a graph as well
             dgraph = torch.cuda.CUDAGraph()
             with torch.cuda.graph(dgraph):
                 dense_step()
