@@ -336,6 +336,15 @@ __global__ __launch_bounds__(256) void dense_reduce(const float* __restrict__ pa
   out[(size_t)rows[o] * D + d] = s;
 }
 
+// Budget of an XCD's slice of W_down (see pick_l2_slices). It is larger than
+// the 4 MB L2: every slice pass re-reads all (column, z) lists and fewer,
+// wider slices halve that, which outweighs the slice's L2 misses (served by
+// the Infinity Cache) up to 256-column slices of 5.6-7.3 MB; 512-column
+// slices (11-15 MB) are slower again. Measured on the 16384 x 4096 x 11008
+// forward: 873 us with 128-column slices, 749 with 256, 1278 with 512; on the
+// 8192 x 4096 x 14336 one: 711, 660, 937.
+constexpr int64_t kDownSliceBudget = 8ll << 20;
+
 // Token rows per pair of up / down launches (0 = all rows in one pair).
 constexpr int64_t kTokenChunk = 0;
 // Up to this many rows the up / down launches use their small-batch forms.
@@ -353,7 +362,7 @@ hipError_t launch_sparse_rows(const FwdArgs& a, hipStream_t s, int64_t chunk) {
   // up: (column, z) list of the non-overflow rows, in up_nq d_model ranges;
   // down: their y rows, d_model cut into P slices (pick_l2_slices)
   const int parts = a.n_tiles < kParts ? a.n_tiles : kParts;
-  const SliceGeom geom = pick_l2_slices(a.D, (int)sizeof(TS), a.F);
+  const SliceGeom geom = pick_l2_slices(a.D, (int)sizeof(TS), a.F, kDownSliceBudget);
   const int P = geom.P, G8 = slice_group(P);
   if (chunk <= 0) chunk = a.N;
   for (int64_t i0 = 0; i0 < a.N; i0 += chunk) {

@@ -180,15 +180,14 @@ inline SliceGeom pick_slices(int D, int esz) {
 
 // Slicing for a pass that gathers slices of the rows of one [rows x D] matrix:
 // the slice is the widest power of two (down to 64 elements, and never wider
-// than pick_slices gives) whose column of the matrix, rows x slice, fits
-// 3.75 MB of an XCD's 4 MB L2 (measured on the 14336 x 4096 down projection:
-// 128-element slices of 3.67 MB take 0.71 ms, 64-element ones 0.81 ms). geom.P is then the total number of slices; they
+// than pick_slices gives) whose column of the matrix, rows x slice, fits the
+// budget: by default 3.75 MB of an XCD's 4 MB L2 (dx of the training step:
+// 4.2 MB slices measured slower there); the down projection passes its own. geom.P is then the total number of slices; they
 // are processed 8 at a time (one per XCD), in P/8 successive passes.
-inline SliceGeom pick_l2_slices(int D, int esz, int64_t rows) {
+inline SliceGeom pick_l2_slices(int D, int esz, int64_t rows, int64_t budget = 15ll << 18) {
   SliceGeom g = pick_slices(D, esz);
   const int e16 = 16 / esz;
   int slice = D / g.P;
-  const int64_t budget = 15ll << 18;
   while (slice > 64 && slice % 2 == 0 && (int64_t)slice / 2 >= e16 && rows * slice * esz > budget) slice /= 2;
   const int lpr = slice / e16 >= 64 ? 64 : slice / e16;
   return {D / slice, slice / lpr, 64 / lpr};
