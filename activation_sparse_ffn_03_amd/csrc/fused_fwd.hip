@@ -452,4 +452,20 @@ hipError_t launch_ffn_fwd(const FwdArgs& a, hipStream_t s) {
   return a.is_bf16 ? launch_t<uint16_t>(a, s, kTokenChunk) : launch_t<float>(a, s, kTokenChunk);
 }
 
+hipError_t launch_forward(const GateArgs& g, const FwdArgs& f, hipStream_t s) {
+  if (gate_ovf_rows_heavy(g)) {  // the two calls' order: overflow list and gate rows on `s` first
+    const hipError_t err = launch_gate_pack(g, s);
+    return err != hipSuccess ? err : launch_ffn_fwd(f, s);
+  }
+  hipStream_t side = s;
+  hipError_t err = launch_gate_pack_split(g, s, true, &side);
+  if (side == s) return err != hipSuccess ? err : launch_ffn_fwd(f, s);  // nothing was forked
+  if (err == hipSuccess && f.ovf_cap > 0)
+    err = f.is_bf16 ? launch_overflow_rows<uint16_t>(f, side) : launch_overflow_rows<float>(f, side);
+  if (err == hipSuccess)
+    err = f.is_bf16 ? launch_sparse_rows<uint16_t>(f, s, kTokenChunk) : launch_sparse_rows<float>(f, s, kTokenChunk);
+  const hipError_t ej = join_side(s, side);
+  return err != hipSuccess ? err : ej;
+}
+
 }  // namespace twell

@@ -899,7 +899,18 @@ __global__ __launch_bounds__(64) void ovf_flags(const uint16_t* __restrict__ cou
 
 }  // namespace
 
+bool gate_ovf_rows_heavy(const GateArgs& a) {
+  const bool small = a.g_in == nullptr && a.is_bf16 && a.N <= kSmallN && a.g_ws != nullptr;
+  return a.is_bf16 && !a.fp8 && a.g_in == nullptr && !small && a.D > 2048;
+}
+
 hipError_t launch_gate_pack(const GateArgs& a, hipStream_t s) {
+  hipStream_t so = s;
+  return launch_gate_pack_split(a, s, false, &so);
+}
+
+hipError_t launch_gate_pack_split(const GateArgs& a, hipStream_t s, bool fork, hipStream_t* ovf_stream) {
+  *ovf_stream = s;
   Epi e{};
   e.N = a.N;
   e.F = a.F;
@@ -974,9 +985,15 @@ hipError_t launch_gate_pack(const GateArgs& a, hipStream_t s) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || no_ovf) return err;
 
-  // 2. overflow rows from the true counts
+  // 2. overflow rows from the true counts: the flags on `s`, then the list
+  // and the dense rows on `so` (the side stream when asked to fork)
   TWELL_LAUNCH("ovf_flags", ovf_flags, dim3((a.N + 63) / 64), 64, 0, s, a.counts, a.N, a.n_tiles, a.slots, a.ovf_flag);
-  err = launch_compact(a.ovf_flag, a.N, a.ovf_rows, a.ovf_cap, a.n_ovf, a.status, 1u /*TWELL_DEV_OVF_CAPACITY*/, s);
+  hipStream_t so = s;
+  if (fork) {
+    if ((err = fork_side(s, &so)) != hipSuccess) return err;
+    *ovf_stream = so;
+  }
+  err = launch_compact(a.ovf_flag, a.N, a.ovf_rows, a.ovf_cap, a.n_ovf, a.status, 1u /*TWELL_DEV_OVF_CAPACITY*/, so);
   if (err != hipSuccess || a.ovf_cap == 0) return err;
 
   // 3. dense activation rows of the overflow rows, same arithmetic as step 1
@@ -986,18 +1003,18 @@ hipError_t launch_gate_pack(const GateArgs& a, hipStream_t s) {
               nbc = (a.F + GatePackFp8::BN - 1) / GatePackFp8::BN;
     TWELL_LAUNCH("gate_mfma_fp8_rows", (gate_mfma_dma<GatePackFp8, MODE_DENSE, true>), dim3(mbc * nbc),
                  GatePackFp8::NT, 0,
-                 s, a.x, a.w, a.D, mbc, nbc, e);
+                 so, a.x, a.w, a.D, mbc, nbc, e);
   } else if (g_in) {
     const int64_t mb = (a.ovf_cap + SBM - 1) / SBM;
     if (a.is_bf16)
-      TWELL_LAUNCH("pack_from_g_rows", (pack_from_g<uint16_t, MODE_DENSE>), dim3(mb * ncb), 256, 0, s, g_in, ncb, e);
+      TWELL_LAUNCH("pack_from_g_rows", (pack_from_g<uint16_t, MODE_DENSE>), dim3(mb * ncb), 256, 0, so, g_in, ncb, e);
     else
-      TWELL_LAUNCH("pack_from_g_rows", (pack_from_g<float, MODE_DENSE>), dim3(mb * ncb), 256, 0, s, g_in, ncb, e);
+      TWELL_LAUNCH("pack_from_g_rows", (pack_from_g<float, MODE_DENSE>), dim3(mb * ncb), 256, 0, so, g_in, ncb, e);
   } else if (a.is_bf16) {
     auto rows = [&](auto cfg) {
       using R = decltype(cfg);
       const int mbc = (a.ovf_cap + R::BM - 1) / R::BM, nbc = (a.F + R::BN - 1) / R::BN;
-      TWELL_LAUNCH("gate_mfma_bf16_rows", (gate_mfma_bf16<R, MODE_DENSE>), dim3(mbc * nbc), R::NT, 0, s,
+      TWELL_LAUNCH("gate_mfma_bf16_rows", (gate_mfma_bf16<R, MODE_DENSE>), dim3(mbc * nbc), R::NT, 0, so,
                    (const uint16_t*)a.x, (const uint16_t*)a.w, a.D, mbc, nbc, e);
     };
     if (a.D <= 2048)
@@ -1006,7 +1023,7 @@ hipError_t launch_gate_pack(const GateArgs& a, hipStream_t s) {
       rows(GateRowsL{});
   } else {
     const int64_t mb = (a.ovf_cap + SBM - 1) / SBM;
-    TWELL_LAUNCH("gate_simt_f32_rows", gate_simt_f32<MODE_DENSE>, dim3(mb * ncb), 256, 0, s, (const float*)a.x, (const float*)a.w, a.D, ncb, e);
+    TWELL_LAUNCH("gate_simt_f32_rows", gate_simt_f32<MODE_DENSE>, dim3(mb * ncb), 256, 0, so, (const float*)a.x, (const float*)a.w, a.D, ncb, e);
   }
   return hipGetLastError();
 }

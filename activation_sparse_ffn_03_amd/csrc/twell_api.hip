@@ -112,31 +112,42 @@ static twell::GateArgs gate_args(const twell::Shape& s, const twell_sizes& z, co
   return a;
 }
 
+// Validation and launch arguments of a bf16 / fp32 gate call (x and w_gate_t,
+// or a given pre-activation g).
+static twell_status gate_prepare(const twell_dims* dims, twell_dtype dtype, const void* x, const void* w_gate_t,
+                                 const float* g_in, const float* t, const twell_pack* out, float* g_dump,
+                                 void* ws, size_t ws_bytes, bool use_ws, twell::Shape* s, twell_sizes* z,
+                                 twell::GateArgs* a) {
+  twell_status st = prepare(dims, dtype, s, z);
+  if (st != TWELL_OK) return st;
+  if ((st = check_gate_ws(*z, ws, ws_bytes, use_ws)) != TWELL_OK) return st;
+  const size_t xd = (size_t)s->N * s->D * s->esz, wd = (size_t)s->F * s->D * s->esz;
+  if (g_in == nullptr) {
+    TWELL_CHECK_PTR(x, xd, "x");
+    TWELL_CHECK_PTR(w_gate_t, wd, "w_gate_t");
+  } else {
+    TWELL_CHECK_PTR(g_in, (size_t)s->N * s->F * 4, "g");
+  }
+  TWELL_CHECK_PTR(t, (size_t)s->N * 4, "t");
+  if ((st = check_pack(out, *z)) != TWELL_OK) return st;
+  if (g_dump != nullptr) TWELL_CHECK_PTR(g_dump, (size_t)s->N * s->F * 4, "g_dump");
+  *a = gate_args(*s, *z, t, out, g_dump, ws, use_ws);
+  a->is_bf16 = dtype == TWELL_BF16;
+  a->x = x;
+  a->w = w_gate_t;
+  a->g_in = g_in;
+  return TWELL_OK;
+}
+
 static twell_status gate_common(const twell_dims* dims, twell_dtype dtype, const void* x, const void* w_gate_t,
                                 const float* g_in, const float* t, const twell_pack* out, float* g_dump,
                                 void* ws, size_t ws_bytes, bool use_ws, void* stream) {
   twell::Shape s;
   twell_sizes z;
-  twell_status st = prepare(dims, dtype, &s, &z);
-  if (st != TWELL_OK) return st;
-  if ((st = check_gate_ws(z, ws, ws_bytes, use_ws)) != TWELL_OK) return st;
-  const size_t xd = (size_t)s.N * s.D * s.esz, wd = (size_t)s.F * s.D * s.esz;
-  if (g_in == nullptr) {
-    TWELL_CHECK_PTR(x, xd, "x");
-    TWELL_CHECK_PTR(w_gate_t, wd, "w_gate_t");
-  } else {
-    TWELL_CHECK_PTR(g_in, (size_t)s.N * s.F * 4, "g");
-  }
-  TWELL_CHECK_PTR(t, (size_t)s.N * 4, "t");
-  if ((st = check_pack(out, z)) != TWELL_OK) return st;
-  if (g_dump != nullptr) TWELL_CHECK_PTR(g_dump, (size_t)s.N * s.F * 4, "g_dump");
-  if (s.N == 0) return TWELL_OK;
-
-  twell::GateArgs a = gate_args(s, z, t, out, g_dump, ws, use_ws);
-  a.is_bf16 = dtype == TWELL_BF16;
-  a.x = x;
-  a.w = w_gate_t;
-  a.g_in = g_in;
+  twell::GateArgs a{};
+  const twell_status st =
+      gate_prepare(dims, dtype, x, w_gate_t, g_in, t, out, g_dump, ws, ws_bytes, use_ws, &s, &z, &a);
+  if (st != TWELL_OK || s.N == 0) return st;
   return hip_status(twell::launch_gate_pack(a, (hipStream_t)stream), "twell_gate_pack");
 }
 
@@ -210,13 +221,12 @@ twell_status twell_pack_preact(const twell_dims* dims, twell_dtype dtype, const 
   return gate_common(dims, dtype, nullptr, nullptr, g, t, out, nullptr, nullptr, 0, false, stream);
 }
 
-twell_status twell_ffn_fwd(const twell_dims* dims, twell_dtype dtype, const twell_pack* pack, const void* x,
-                           const void* w_up_t, const void* w_down, float* y, float* a_save, void* ws,
-                           size_t ws_bytes, void* stream) {
-  twell::Shape s;
-  twell_sizes z;
-  twell_status st = prepare(dims, dtype, &s, &z);
-  if (st != TWELL_OK) return st;
+// Validation and launch arguments of the up/down projection (shape already
+// checked by the caller).
+static twell_status fwd_prepare(const twell::Shape& s, const twell_sizes& z, twell_dtype dtype,
+                                const twell_pack* pack, const void* x, const void* w_up_t, const void* w_down,
+                                float* y, float* a_save, void* ws, size_t ws_bytes, twell::FwdArgs* out) {
+  twell_status st;
   if ((st = check_pack(pack, z)) != TWELL_OK) return st;
   const size_t xd = (size_t)s.N * s.D * s.esz, wd = (size_t)s.F * s.D * s.esz;
   TWELL_CHECK_PTR(x, xd, "x");
@@ -227,7 +237,6 @@ twell_status twell_ffn_fwd(const twell_dims* dims, twell_dtype dtype, const twel
   if (ws_bytes < z.ws_fwd) return fail(TWELL_ERR_WORKSPACE, "forward workspace smaller than twell_sizes.ws_fwd");
   if (twell::bad_ptr(ws, z.ws_fwd))
     return fail(TWELL_ERR_WORKSPACE, "forward workspace is NULL or not 16-byte aligned");
-  if (s.N == 0) return TWELL_OK;
 
   twell::FwdArgs a{};
   a.N = s.N;
@@ -250,15 +259,47 @@ twell_status twell_ffn_fwd(const twell_dims* dims, twell_dtype dtype, const twel
   a.w_down = w_down;
   a.y = y;
   a.a_save = a_save;
-  const twell::FwdLayout L = twell::fwd_layout(s);
-  char* base = reinterpret_cast<char*>(ws);
-  a.offs = reinterpret_cast<int32_t*>(base + L.offs);
-  a.zlist = reinterpret_cast<uint2*>(base + L.zlist);
-  a.upart = reinterpret_cast<float*>(base + L.upart);
-  a.uslot = reinterpret_cast<int32_t*>(base + L.uslot);
-  a.up_nq = twell::up_passes(s);
-  a.part = reinterpret_cast<float*>(base + L.part);
+  if (s.N > 0) {
+    const twell::FwdLayout L = twell::fwd_layout(s);
+    char* base = reinterpret_cast<char*>(ws);
+    a.offs = reinterpret_cast<int32_t*>(base + L.offs);
+    a.zlist = reinterpret_cast<uint2*>(base + L.zlist);
+    a.upart = reinterpret_cast<float*>(base + L.upart);
+    a.uslot = reinterpret_cast<int32_t*>(base + L.uslot);
+    a.up_nq = twell::up_passes(s);
+    a.part = reinterpret_cast<float*>(base + L.part);
+  }
+  *out = a;
+  return TWELL_OK;
+}
+
+twell_status twell_ffn_fwd(const twell_dims* dims, twell_dtype dtype, const twell_pack* pack, const void* x,
+                           const void* w_up_t, const void* w_down, float* y, float* a_save, void* ws,
+                           size_t ws_bytes, void* stream) {
+  twell::Shape s;
+  twell_sizes z;
+  twell_status st = prepare(dims, dtype, &s, &z);
+  if (st != TWELL_OK) return st;
+  twell::FwdArgs a{};
+  if ((st = fwd_prepare(s, z, dtype, pack, x, w_up_t, w_down, y, a_save, ws, ws_bytes, &a)) != TWELL_OK) return st;
+  if (s.N == 0) return TWELL_OK;
   return hip_status(twell::launch_ffn_fwd(a, (hipStream_t)stream), "twell_ffn_fwd");
+}
+
+twell_status twell_ffn_forward(const twell_dims* dims, twell_dtype dtype, const void* x, const void* w_gate_t,
+                               const float* t, const twell_pack* pack, const void* w_up_t, const void* w_down,
+                               float* y, float* a_save, void* ws, size_t ws_bytes, void* gate_ws,
+                               size_t gate_ws_bytes, void* stream) {
+  twell::Shape s;
+  twell_sizes z;
+  twell::GateArgs g{};
+  twell_status st = gate_prepare(dims, dtype, x, w_gate_t, nullptr, t, pack, nullptr, gate_ws, gate_ws_bytes,
+                                 gate_ws != nullptr, &s, &z, &g);
+  if (st != TWELL_OK) return st;
+  twell::FwdArgs f{};
+  if ((st = fwd_prepare(s, z, dtype, pack, x, w_up_t, w_down, y, a_save, ws, ws_bytes, &f)) != TWELL_OK) return st;
+  if (s.N == 0) return TWELL_OK;
+  return hip_status(twell::launch_forward(g, f, (hipStream_t)stream), "twell_ffn_forward");
 }
 
 static twell_status check_hybrid(const twell_hybrid* h, const twell_sizes& z) {

@@ -44,6 +44,16 @@ struct GateArgs {
 };
 
 hipError_t launch_gate_pack(const GateArgs& a, hipStream_t s);
+// The same launches, with the overflow list and the overflow rows' dense
+// activations enqueued on the side stream when `fork` is set (the pack and
+// the flags stay on `s`). *ovf_stream is the stream that ends the overflow
+// branch: `s` when nothing was forked (no overflow steps, or fork unset),
+// else the side stream, which the caller must join back into `s`.
+hipError_t launch_gate_pack_split(const GateArgs& a, hipStream_t s, bool fork, hipStream_t* ovf_stream);
+// True when the overflow rows' gate rows take the 128x128 register-staged
+// GEMM (bf16, d_model > 2048, large batch): a long launch that, run beside
+// the up projection, costs it more occupancy than it saves.
+bool gate_ovf_rows_heavy(const GateArgs& a);
 
 // Per-row E4M3 quantisation: q [rows][cols] codes, scale [rows] (quant.hip).
 hipError_t launch_quantize_e4m3(const void* in, int is_bf16, int64_t rows, int cols, uint8_t* q, float* scale,
@@ -75,6 +85,10 @@ struct FwdArgs {
 };
 
 hipError_t launch_ffn_fwd(const FwdArgs& a, hipStream_t s);
+// Gate + pack (g) followed by the up/down projection (f) in one call: the
+// overflow branch of both (list, dense rows, their up/down products) runs on
+// the side stream beside the up/down projection of the other rows.
+hipError_t launch_forward(const GateArgs& g, const FwdArgs& f, hipStream_t s);
 
 // Side stream of the current device for the independent branch of a call
 // (side_stream.hip): fork_side makes it wait for the work enqueued on `main`

@@ -29,7 +29,7 @@ _STATUS = {0: "TWELL_OK", 1: "TWELL_ERR_INVALID_ARG", 2: "TWELL_ERR_UNSUPPORTED"
 # Every symbol include/twell.h declares.
 EXPORTS = ("twell_status_str", "twell_last_error", "twell_n_tiles", "twell_query_sizes", "twell_gate_pack",
            "twell_gate_pack_ws", "twell_pack_preact", "twell_quantize_e4m3", "twell_gate_pack_fp8",
-           "twell_gate_pack_fp8_ws", "twell_ffn_fwd",
+           "twell_gate_pack_fp8_ws", "twell_ffn_fwd", "twell_ffn_forward",
            "twell_route_hybrid", "twell_ffn_bwd", "twell_trace_start", "twell_trace_stop", "twell_trace_count",
            "twell_trace_dropped", "twell_trace_get")
 
@@ -100,6 +100,8 @@ def lib() -> ctypes.CDLL:
         L.twell_gate_pack_fp8_ws.argtypes = [pd, vp, vp, vp, vp, vp, pp, vp, vp, sz, vp]
         L.twell_ffn_fwd.restype = ctypes.c_int
         L.twell_ffn_fwd.argtypes = [pd, ctypes.c_int, pp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.twell_ffn_forward.restype = ctypes.c_int
+        L.twell_ffn_forward.argtypes = [pd, ctypes.c_int, vp, vp, vp, pp, vp, vp, vp, vp, vp, sz, vp, sz, vp]
         L.twell_route_hybrid.restype = ctypes.c_int
         L.twell_route_hybrid.argtypes = [pd, ctypes.c_int, pp, vp, ph, vp]
         L.twell_ffn_bwd.restype = ctypes.c_int
@@ -284,6 +286,18 @@ def ffn_fwd(dims: Dims, dtype: int, pack: TwellPack, x, w_up_t, w_down, y, a_sav
            "twell_ffn_fwd")
 
 
+def ffn_forward(dims: Dims, dtype: int, x, w_gate_t, t, pack: TwellPack, w_up_t, w_down, y, a_save=None, ws=None,
+                gate_ws=None, stream=None) -> None:
+    """gate_pack (gate_pack with gate_ws when given) then ffn_fwd in one call
+    (twell_ffn_forward): the overflow branch runs beside the up/down projection."""
+    p = pack.struct()
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    gbytes = 0 if gate_ws is None else gate_ws.numel() * gate_ws.element_size()
+    _check(lib().twell_ffn_forward(ctypes.byref(dims), int(dtype), _ptr(x), _ptr(w_gate_t), _ptr(t), ctypes.byref(p),
+                                   _ptr(w_up_t), _ptr(w_down), _ptr(y), _ptr(a_save), _ptr(ws), nbytes,
+                                   _ptr(gate_ws), gbytes, _stream(stream)), "twell_ffn_forward")
+
+
 def route_hybrid(dims: Dims, dtype: int, pack: TwellPack, a_save, hyb: TwellHybrid, stream=None) -> None:
     p, h = pack.struct(), hyb.struct()
     _check(lib().twell_route_hybrid(ctypes.byref(dims), int(dtype), ctypes.byref(p), _ptr(a_save),
@@ -320,7 +334,8 @@ def trace_stop() -> list:
 class TwellFFN:
     """Buffers for one (dims, dtype) problem, and the whole hot path in order.
 
-    forward(): gate_pack -> ffn_fwd (with a_save when training)
+    forward(): gate_pack + ffn_fwd in one call, ffn_forward (with a_save when
+    training; the two separate calls when g_dump is asked for)
     backward(): route_hybrid -> ffn_bwd
     With fp8_gate (bf16 forward only), forward() takes the gate weight as
     (E4M3 codes, row scales) from quantize_e4m3 and runs
@@ -358,6 +373,10 @@ class TwellFFN:
             quantize_e4m3(x, stream=stream, out=(self.x_q, self.x_scale))
             gate_pack_fp8(self.dims, self.x_q, self.x_scale, w_q, w_scale, t, self.pack, g_dump=g_dump, stream=stream,
                           ws=self.ws_gate)
+        elif g_dump is None:
+            ffn_forward(self.dims, self.dtype, x, w_gate_t, t, self.pack, w_up_t, w_down, self.y, a_save=self.a_save,
+                        ws=self.ws_fwd, gate_ws=self.ws_gate, stream=stream)
+            return self.y
         else:
             gate_pack(self.dims, self.dtype, x, w_gate_t, t, self.pack, g_dump=g_dump, stream=stream, ws=self.ws_gate)
         ffn_fwd(self.dims, self.dtype, self.pack, x, w_up_t, w_down, self.y, a_save=self.a_save, ws=self.ws_fwd,

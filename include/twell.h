@@ -240,6 +240,27 @@ twell_status twell_ffn_fwd(const twell_dims* dims, twell_dtype dtype, const twel
                            const void* x, const void* w_up_t, const void* w_down, float* y,
                            float* a_save, void* ws, size_t ws_bytes, void* stream);
 
+/* Stages 1 and 2 in one call ("Sakana AI and NVIDIA present TwELL",
+ * edge.aivizor.me, second paragraph: the gate projection's epilogue forms
+ * TwELL and one inference kernel consumes it for the up and down
+ * projections). Same outputs as twell_gate_pack (or twell_gate_pack_ws when
+ * gate_ws is not NULL) followed by twell_ffn_fwd on the same stream: the
+ * TwELL pack, the overflow list and rows in *pack, y, and a_save when given.
+ * Within one call the overflow branch (the ascending overflow list, the
+ * overflow rows' dense activations and their up / down products) is
+ * enqueued on a second stream of the library beside the up / down
+ * projection of the other rows, which reads only the pack and the overflow
+ * flags, and is joined back before the call returns; the two separate calls
+ * must each finish their part before returning. No g_dump.
+ * x, w_gate_t, w_up_t, w_down: as in the two calls; ws: the forward
+ * workspace (twell_sizes.ws_fwd bytes); gate_ws: the small-batch gate
+ * workspace (twell_sizes.ws_gate bytes) or NULL. Validation covers every
+ * argument of both calls before anything is enqueued; errors as there. */
+twell_status twell_ffn_forward(const twell_dims* dims, twell_dtype dtype, const void* x, const void* w_gate_t,
+                               const float* t, const twell_pack* pack, const void* w_up_t, const void* w_down,
+                               float* y, float* a_save, void* ws, size_t ws_bytes, void* gate_ws,
+                               size_t gate_ws_bytes, void* stream);
+
 /* Stage 3a: route every row to the row-ELL (width K = dims->row_cap >= 1) or to
  * the dense backup (rule at twell_hybrid). a_save is the array filled by
  * twell_ffn_fwd. Writes every field of *out. */

@@ -95,6 +95,16 @@ def test_new_calls_validate_before_touching_the_device():
                                 None) == 3
     assert L.twell_gate_pack_ws(ctypes.byref(d), 0, fake, fake, fake, ctypes.byref(p), None, None, need, None) == 1
     assert b"ws" in L.twell_last_error()
+    # the combined forward validates the arguments of both calls first
+    ws_fwd = tw.query_sizes(d, tw.BF16)["ws_fwd"]
+    assert L.twell_ffn_forward(ctypes.byref(d), 0, None, None, None, ctypes.byref(p), None, None, None, None, None,
+                               0, None, 0, None) == 1
+    assert b"x" in L.twell_last_error()
+    assert L.twell_ffn_forward(ctypes.byref(d), 0, fake, fake, fake, ctypes.byref(p), fake, fake, fake, None, fake,
+                               ws_fwd, fake, need - 1, None) == 3  # gate workspace too small
+    assert L.twell_ffn_forward(ctypes.byref(d), 0, fake, fake, fake, ctypes.byref(p), fake, fake, fake, None, fake,
+                               ws_fwd, None, 0, None) == 1  # pack pointers NULL
+    assert b"pack" in L.twell_last_error()
     # quantiser: shapes, dtype, pointers
     assert L.twell_quantize_e4m3(-1, 8, 0, fake, fake, fake, None) == 1
     assert L.twell_quantize_e4m3(4, 0, 0, fake, fake, fake, None) == 1

@@ -1,0 +1,90 @@
+"""twell_ffn_forward (gate + pack and the up/down projection in one call, the
+overflow branch beside the up/down projection) against twell_gate_pack[_ws]
+followed by twell_ffn_fwd: the same kernels on the same inputs, so every output
+must match bit for bit; and against the oracle through TwellFFN.forward."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from activation_sparse_ffn_03_amd import twell as tw
+from synth import make_inputs
+
+from gpu_util import Pipeline, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _same(a, b, what):
+    if a.dtype == torch.bfloat16:
+        a, b = a.view(torch.int16), b.view(torch.int16)
+    elif a.dtype == torch.float32:
+        a, b = a.view(torch.int32), b.view(torch.int32)
+    assert torch.equal(a, b), what
+
+
+@pytest.mark.parametrize("name,kw,extra,small", [
+    ("c4", dict(N=600, D=512, F=2048), dict(slots=8), False),          # lognormal: overflow rows
+    ("c2", dict(N=700, D=256, F=1300), {}, False),                     # ragged, no overflow
+    ("c1", {}, dict(slots=2, ovf_cap=64), False),                      # fp32 with overflow rows
+    ("c2", dict(N=64, D=64, F=128), dict(slots=0, ovf_cap=64), True),   # every non-empty row overflows (64 rows: small-batch gate)
+    ("c2", dict(N=96, D=64, F=128), dict(slots=0, ovf_cap=96), False),  # the same above the small-batch limit
+    ("c2", dict(N=40, D=1024, F=1300), dict(slots=128), True),         # small batch: split-GEMV gate
+    ("c4", dict(N=300, D=512, F=2048), dict(slots=8, ovf_cap=16), False),  # overflow beyond capacity
+    ("c5", dict(N=500, D=256, F=1024), dict(slots=8), False),          # training: a_save as well
+])
+def test_combined_call_matches_separate_calls(name, kw, extra, small):
+    w = make_inputs(name, **kw)
+    print(f"[forward-call] {name} {kw} {extra} small={small}", flush=True)
+    pl = Pipeline(w, **extra)
+    ffn = pl.ffn
+    # the combined call (TwellFFN.forward without g_dump)
+    y1 = pl.forward().clone()
+    pk1 = {f: getattr(ffn.pack, f).clone() for f in ("vals", "cols", "counts", "ovf_flag", "ovf_rows", "ovf_h",
+                                                     "n_ovf", "status")}
+    a1 = ffn.a_save.clone() if ffn.a_save is not None else None
+    # the two separate calls into fresh outputs
+    ref = tw.TwellFFN(pl.dims, pl.code, train=ffn.train)
+    tw.gate_pack(pl.dims, pl.code, pl.x, pl.wg, pl.t, ref.pack, ws=ref.ws_gate)
+    tw.ffn_fwd(pl.dims, pl.code, ref.pack, pl.x, pl.wu, pl.wd, ref.y, a_save=ref.a_save, ws=ref.ws_fwd)
+    torch.cuda.synchronize()
+    assert (ref.ws_gate is not None) == small
+    n_ovf = int(ref.pack.n_ovf.item())
+    n = min(n_ovf, pl.ovf_cap)
+    for f in ("counts", "ovf_flag", "n_ovf", "status"):
+        _same(pk1[f], getattr(ref.pack, f), f)
+    _same(pk1["ovf_rows"][:n], ref.pack.ovf_rows[:n], "ovf_rows")
+    _same(pk1["ovf_h"][:n], ref.pack.ovf_h[:n], "ovf_h")
+    # slots in use only (the others are don't-care)
+    cnt = (ref.pack.counts.to(torch.int32) & 0xFFFF).clamp(max=pl.dims.slots)
+    S, N = pl.dims.slots, pl.dims.n_tokens
+    if S > 0:
+        used = torch.arange(S, device=cnt.device)[None, :, None] < cnt[:, None, :]
+        _same(pk1["vals"].view(-1, S, N)[used], ref.pack.vals.view(-1, S, N)[used], "vals")
+        _same(pk1["cols"].view(-1, S, N)[used], ref.pack.cols.view(-1, S, N)[used], "cols")
+    status = int(ref.pack.status.item())
+    if status == 0:
+        _same(y1, ref.y, "y")
+    else:  # rows beyond the overflow capacity are left unwritten: compare the others
+        keep = torch.ones(N, dtype=torch.bool, device=y1.device)
+        flagged = torch.nonzero(ref.pack.ovf_flag.bool()).flatten()
+        keep[flagged[n:]] = False
+        _same(y1[keep], ref.y[keep], "y")
+    if a1 is not None:
+        flag = ref.pack.ovf_flag.bool()
+        used = (torch.arange(S, device=cnt.device)[None, :, None] < cnt[:, None, :]) & ~flag[None, None, :]
+        _same(a1.view(-1, S, N)[used], ref.a_save.view(-1, S, N)[used], "a_save")
+
+
+def test_combined_call_twice_in_a_row_is_stable():
+    """The side stream is shared by every call on a device: two combined calls
+    back to back on the same stream give the same outputs as one."""
+    require_gpu()
+    w = make_inputs("c4", N=500, D=512, F=2048)
+    pl = Pipeline(w, slots=8, ovf_cap=w.N)
+    y1 = pl.forward().clone()
+    assert int(pl.ffn.pack.n_ovf.item()) > 0
+    pl.ffn.forward(pl.x, pl.wg, pl.wu, pl.wd, pl.t)
+    y2 = pl.forward().clone()
+    _same(y1, y2, "y")
