@@ -39,6 +39,13 @@ namespace {
 
 constexpr int kParts = 8;  // one part per XCD
 
+// Maximum of v over the 64 lanes of a wave (every lane gets it).
+__device__ __forceinline__ int wave_max_int(int v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = max(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
 // Walk TwELL tiles [j0, j1) of token i (not an overflow row) and hand its
 // packed entries to `flush` in lists of at most 64: lane k of the list holds
 // entry k as (global column c, stored activation h, slot id j*S+s). The slot
@@ -136,14 +143,24 @@ __global__ __launch_bounds__(256) void ffn_up_kernel(FwdArgs a, int parts, int64
   const int j0 = (int)((int64_t)part * a.n_tiles / parts), j1 = (int)((int64_t)(part + 1) * a.n_tiles / parts);
   const int D = a.D, Dq = D / a.up_nq, nch = Dq / E;
   const int64_t N = a.N;
-  // Independent loads first, in one memory round trip: the overflow flag, the
-  // counts of the tiles before this part and of its own tiles, the x slice.
-  const bool ovf = a.ovf_flag[i] != 0;
-  const int cb = lane < j0 ? (int)a.counts[(size_t)lane * N + i] : 0;
+  // Independent loads first, in one memory round trip: the counts of the
+  // first 64 tiles and of this part's tiles, the x slice.
+  const int ca = lane < a.n_tiles ? (int)a.counts[(size_t)lane * N + i] : 0;
   const int cf = j0 + lane < j1 ? (int)a.counts[(size_t)(j0 + lane) * N + i] : 0;
   u32x4_t xr[M];
   load_row<TS, M>(xr, reinterpret_cast<const TS*>(a.x) + (size_t)i * D + (size_t)q * Dq, nch, lane);
-  if (ovf) return;
+  // An overflow row (some tile count above S; the pack's flag, taken here
+  // from the counts so that this kernel need not wait for the flag kernel) is
+  // left to the dense-row path; its entry total is marked -1 for the down
+  // projection and the finish pass.
+  int cmax = ca;
+  for (int jb = 64; jb < a.n_tiles; jb += 64)
+    cmax = max(cmax, jb + lane < a.n_tiles ? (int)a.counts[(size_t)(jb + lane) * N + i] : 0);
+  if (wave_max_int(cmax) > a.slots) {
+    if (j1 == a.n_tiles && q == 0 && lane == 0) a.offs[i] = -1;
+    return;
+  }
+  const int cb = lane < j0 ? ca : 0;
   const size_t L = (size_t)a.n_tiles * a.slots;
   const TS* __restrict__ w_up = reinterpret_cast<const TS*>(a.w_up) + (size_t)q * Dq;
   uint2* __restrict__ zl = a.zlist + (size_t)i * L;
@@ -195,12 +212,13 @@ __global__ __launch_bounds__(256) void ffn_up_kernel(FwdArgs a, int parts, int64
 __global__ __launch_bounds__(256) void ffn_up_finish(FwdArgs a, int64_t i0, int64_t i1) {
   const int lane = threadIdx.x & 63;
   const int64_t i = i0 + (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (i >= i1 || a.ovf_flag[i]) return;
+  if (i >= i1) return;
+  const int total = a.offs[i];
+  if (total < 0) return;  // an overflow row
   const size_t L = (size_t)a.n_tiles * a.slots;
   const size_t qstride = (size_t)a.N * L;
   uint2* __restrict__ zl = a.zlist + (size_t)i * L;
   const float* __restrict__ up = a.upart + (size_t)i * L;
-  const int total = a.offs[i];
   for (int k = lane; k < total; k += 64) {
     float sum = 0.f;
     for (int q = 0; q < a.up_nq; ++q) sum += up[q * qstride + k];
@@ -232,13 +250,12 @@ __global__ __launch_bounds__(256) void ffn_down_kernel(FwdArgs a, int G8, int64_
   const TS* __restrict__ w_down = reinterpret_cast<const TS*>(a.w_down) + d0;
   const int L = a.n_tiles * a.slots;
   const uint2* __restrict__ zl = a.zlist + (size_t)i * L;
-  // Independent loads first, in one memory round trip: the overflow flag, the
-  // row's entry total and (speculatively, inside the row's list) its first 64
-  // entries.
-  const bool ovf = a.ovf_flag[i] != 0;
+  // Independent loads first, in one memory round trip: the row's entry total
+  // (-1 for an overflow row) and (speculatively, inside the row's list) its
+  // first 64 entries.
   const int total = a.offs[i];
   const uint2 ent0 = lane < L ? zl[lane] : make_uint2(0u, 0u);
-  if (ovf) return;
+  if (total < 0) return;
   float acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;

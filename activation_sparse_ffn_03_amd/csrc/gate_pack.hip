@@ -985,14 +985,16 @@ hipError_t launch_gate_pack_split(const GateArgs& a, hipStream_t s, bool fork, h
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || no_ovf) return err;
 
-  // 2. overflow rows from the true counts: the flags on `s`, then the list
-  // and the dense rows on `so` (the side stream when asked to fork)
-  TWELL_LAUNCH("ovf_flags", ovf_flags, dim3((a.N + 63) / 64), 64, 0, s, a.counts, a.N, a.n_tiles, a.slots, a.ovf_flag);
+  // 2. overflow rows from the true counts: the flags, the list and the dense
+  // rows on `so` (the side stream when asked to fork: the up / down
+  // projection takes the overflow test from the counts itself)
   hipStream_t so = s;
   if (fork) {
     if ((err = fork_side(s, &so)) != hipSuccess) return err;
     *ovf_stream = so;
   }
+  TWELL_LAUNCH("ovf_flags", ovf_flags, dim3((a.N + 63) / 64), 64, 0, so, a.counts, a.N, a.n_tiles, a.slots,
+               a.ovf_flag);
   err = launch_compact(a.ovf_flag, a.N, a.ovf_rows, a.ovf_cap, a.n_ovf, a.status, 1u /*TWELL_DEV_OVF_CAPACITY*/, so);
   if (err != hipSuccess || a.ovf_cap == 0) return err;
 
