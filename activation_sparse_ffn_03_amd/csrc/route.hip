@@ -11,7 +11,8 @@
 // ascending order.
 //
 // Kernels
-//   route_rows     wave per row: row_nnz, is_dense, and the ELL entries of
+//   route_rows     wave per row, 16 rows per workgroup (their TwELL slot
+//                  loads share cache lines): row_nnz, is_dense, and the ELL entries of
 //                  ELL rows (vals, global cols, saved a).
 //   launch_compact ascending dense-row list + capacity status.
 //   route_dense_h  thread per (dense row, column): dense activation rows,
@@ -47,9 +48,9 @@ __device__ __forceinline__ int wave_excl_scan(int v) {
 // position (start of the tile + s), so all loads of one iteration are in
 // flight together.
 template <typename TS>
-__global__ __launch_bounds__(256) void route_rows(RouteArgs a) {
+__global__ __launch_bounds__(1024) void route_rows(RouteArgs a) {
   const int lane = threadIdx.x & 63;
-  const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t i = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 6);
   if (i >= a.N) return;
   const int64_t N = a.N;
   int nnz = 0;
@@ -120,7 +121,7 @@ __global__ __launch_bounds__(256) void route_dense_h(RouteArgs a) {
 
 template <typename TS>
 hipError_t launch_t(const RouteArgs& a, hipStream_t s) {
-  TWELL_LAUNCH("route_rows", route_rows<TS>, dim3((unsigned)((a.N + 3) / 4)), 256, 0, s, a);
+  TWELL_LAUNCH("route_rows", route_rows<TS>, dim3((unsigned)((a.N + 15) / 16)), 1024, 0, s, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   err = launch_compact(a.is_dense, a.N, a.dense_rows, a.dense_cap, a.n_dense, a.status, 2u /*TWELL_DEV_DENSE_CAPACITY*/, s);
