@@ -113,25 +113,25 @@ def kernel_work(name, w, st, train):
         return {"flops": 0.0, "bytes": N * F * 4 + twell, "bound": "hbm"}
     if name == "ffn_up_kernel":   # x, W_up once; TwELL read; z (and a when training) written
         byt = N * D * e + F * D * e + nnz * (e + 2) + n_t * N * 2 + nnz * 4 + (nnz * 4 if train else 0)
-        return {"flops": 2.0 * D * nnz, "bytes": byt, "bound": "hbm"}
+        return {"flops": 2.0 * D * nnz, "bytes": byt, "bound": "hbm", "gathered": nnz * D * e}
     if name == "ffn_down_kernel":  # W_down once; cols + z read; y written (fp32)
         byt = F * D * e + nnz * (2 + 4) + n_t * N * 2 + N * D * 4
-        return {"flops": 2.0 * D * nnz, "bytes": byt, "bound": "hbm"}
+        return {"flops": 2.0 * D * nnz, "bytes": byt, "bound": "hbm", "gathered": nnz * D * e}
     if name == "bwd_dz_ell":   # dy, W_down once; row-ELL read; (col, z, da, dg) records written
         byt = N * D * e + F * D * e + nnz_ell * (e + 8) + nnz_ell * 20
-        return {"flops": 2.0 * D * nnz_ell, "bytes": byt, "bound": "hbm"}
+        return {"flops": 2.0 * D * nnz_ell, "bytes": byt, "bound": "hbm", "gathered": nnz_ell * D * e}
     if name == "bwd_dx":       # W_up once; records read; dx written (fp32)
         byt = F * D * e + nnz * 8 + N * D * 4
-        return {"flops": 2.0 * D * nnz, "bytes": byt, "bound": "hbm"}
+        return {"flops": 2.0 * D * nnz, "bytes": byt, "bound": "hbm", "gathered": nnz * D * e}
     if name == "bwd_dx_gate":  # W_gate once; records read; dx read and written (fp32)
         byt = F * D * e + nnz * 8 + 2 * N * D * 4
-        return {"flops": 2.0 * D * nnz, "bytes": byt, "bound": "hbm"}
+        return {"flops": 2.0 * D * nnz, "bytes": byt, "bound": "hbm", "gathered": nnz * D * e}
     if name == "bwd_dw_down":  # dy once; records via the column transpose; dW_down written (fp32)
         byt = N * D * e + nnz * 12 + F * D * 4
-        return {"flops": 2.0 * D * nnz, "bytes": byt, "bound": "hbm"}
+        return {"flops": 2.0 * D * nnz, "bytes": byt, "bound": "hbm", "gathered": nnz * D * e}
     if name == "bwd_dw":       # x once; records via the column transpose; dW_up, dW_gate written (fp32)
         byt = N * D * e + nnz * 16 + 2 * F * D * 4
-        return {"flops": 4.0 * D * nnz, "bytes": byt, "bound": "hbm"}
+        return {"flops": 4.0 * D * nnz, "bytes": byt, "bound": "hbm", "gathered": nnz * D * e}
     return None
 
 
@@ -436,6 +436,8 @@ def main():
         s_k = kernels[k]["avg_ms"] / 1e3
         kernels[k]["GBps_algorithmic"] = wk_k["bytes"] / s_k / 1e9
         kernels[k]["TFLOPs"] = wk_k["flops"] / s_k / 1e12
+        if "gathered" in wk_k:   # weight (or token) rows delivered per active entry, mostly from L2
+            kernels[k]["gather_TBps"] = wk_k["gathered"] / s_k / 1e12
 
     dense = dense_graph_ms = None
     if not args.no_dense:
