@@ -30,7 +30,9 @@ def _same(a, b, what):
     ("c1", {}, dict(slots=2, ovf_cap=64), False),                      # fp32 with overflow rows
     ("c2", dict(N=64, D=64, F=128), dict(slots=0, ovf_cap=64), True),   # every non-empty row overflows (64 rows: small-batch gate)
     ("c2", dict(N=96, D=64, F=128), dict(slots=0, ovf_cap=96), False),  # the same above the small-batch limit
-    ("c2", dict(N=40, D=1024, F=1300), dict(slots=128), True),         # small batch: split-GEMV gate
+    ("c2", dict(N=40, D=1024, F=1300), dict(slots=128), True),         # small batch: split-GEMV gate, entries from g
+    ("c3", dict(N=9, D=4096, F=11008), dict(slots=128), True),         # the same with four d_model passes
+    ("c2", dict(N=33, D=512, F=700), dict(tile_n=64, slots=64), True),  # narrower tiles, F ragged
     ("c4", dict(N=300, D=512, F=2048), dict(slots=8, ovf_cap=16), False),  # overflow beyond capacity
     ("c5", dict(N=500, D=256, F=1024), dict(slots=8), False),          # training: a_save as well
 ])
