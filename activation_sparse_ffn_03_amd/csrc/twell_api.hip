@@ -176,30 +176,40 @@ twell_status twell_quantize_e4m3(int64_t rows, int32_t cols, twell_dtype dtype, 
                     "twell_quantize_e4m3");
 }
 
+// Validation and launch arguments of an FP8 gate call.
+static twell_status fp8_prepare(const twell_dims* dims, const uint8_t* x_q, const float* x_scale, const uint8_t* w_q,
+                                const float* w_scale, const float* t, const twell_pack* out, float* g_dump, void* ws,
+                                size_t ws_bytes, bool use_ws, twell::Shape* s, twell_sizes* z, twell::GateArgs* a) {
+  twell_status st = prepare(dims, TWELL_BF16, s, z);
+  if (st != TWELL_OK) return st;
+  if ((st = check_gate_ws(*z, ws, ws_bytes, use_ws)) != TWELL_OK) return st;
+  if (s->D % 64 != 0) return fail(TWELL_ERR_UNSUPPORTED, "the FP8 gate needs d_model to be a multiple of 64");
+  TWELL_CHECK_PTR(x_q, (size_t)s->N * s->D, "x_q");
+  TWELL_CHECK_PTR(x_scale, (size_t)s->N * 4, "x_scale");
+  TWELL_CHECK_PTR(w_q, (size_t)s->F * s->D, "w_q");
+  TWELL_CHECK_PTR(w_scale, (size_t)s->F * 4, "w_scale");
+  TWELL_CHECK_PTR(t, (size_t)s->N * 4, "t");
+  if ((st = check_pack(out, *z)) != TWELL_OK) return st;
+  if (g_dump != nullptr) TWELL_CHECK_PTR(g_dump, (size_t)s->N * s->F * 4, "g_dump");
+  *a = gate_args(*s, *z, t, out, g_dump, ws, use_ws);
+  a->is_bf16 = 1;  // TwELL values and overflow rows are stored in bf16
+  a->fp8 = 1;
+  a->x = x_q;
+  a->w = w_q;
+  a->x_scale = x_scale;
+  a->w_scale = w_scale;
+  return TWELL_OK;
+}
+
 static twell_status fp8_common(const twell_dims* dims, const uint8_t* x_q, const float* x_scale, const uint8_t* w_q,
                                const float* w_scale, const float* t, const twell_pack* out, float* g_dump, void* ws,
                                size_t ws_bytes, bool use_ws, void* stream) {
   twell::Shape s;
   twell_sizes z;
-  twell_status st = prepare(dims, TWELL_BF16, &s, &z);
-  if (st != TWELL_OK) return st;
-  if ((st = check_gate_ws(z, ws, ws_bytes, use_ws)) != TWELL_OK) return st;
-  if (s.D % 64 != 0) return fail(TWELL_ERR_UNSUPPORTED, "the FP8 gate needs d_model to be a multiple of 64");
-  TWELL_CHECK_PTR(x_q, (size_t)s.N * s.D, "x_q");
-  TWELL_CHECK_PTR(x_scale, (size_t)s.N * 4, "x_scale");
-  TWELL_CHECK_PTR(w_q, (size_t)s.F * s.D, "w_q");
-  TWELL_CHECK_PTR(w_scale, (size_t)s.F * 4, "w_scale");
-  TWELL_CHECK_PTR(t, (size_t)s.N * 4, "t");
-  if ((st = check_pack(out, z)) != TWELL_OK) return st;
-  if (g_dump != nullptr) TWELL_CHECK_PTR(g_dump, (size_t)s.N * s.F * 4, "g_dump");
-  if (s.N == 0) return TWELL_OK;
-  twell::GateArgs a = gate_args(s, z, t, out, g_dump, ws, use_ws);
-  a.is_bf16 = 1;  // TwELL values and overflow rows are stored in bf16
-  a.fp8 = 1;
-  a.x = x_q;
-  a.w = w_q;
-  a.x_scale = x_scale;
-  a.w_scale = w_scale;
+  twell::GateArgs a{};
+  const twell_status st =
+      fp8_prepare(dims, x_q, x_scale, w_q, w_scale, t, out, g_dump, ws, ws_bytes, use_ws, &s, &z, &a);
+  if (st != TWELL_OK || s.N == 0) return st;
   return hip_status(twell::launch_gate_pack(a, (hipStream_t)stream), "twell_gate_pack_fp8");
 }
 
@@ -284,6 +294,23 @@ twell_status twell_ffn_fwd(const twell_dims* dims, twell_dtype dtype, const twel
   if ((st = fwd_prepare(s, z, dtype, pack, x, w_up_t, w_down, y, a_save, ws, ws_bytes, &a)) != TWELL_OK) return st;
   if (s.N == 0) return TWELL_OK;
   return hip_status(twell::launch_ffn_fwd(a, (hipStream_t)stream), "twell_ffn_fwd");
+}
+
+twell_status twell_ffn_forward_fp8(const twell_dims* dims, const uint8_t* x_q, const float* x_scale,
+                                   const uint8_t* w_q, const float* w_scale, const float* t, const twell_pack* pack,
+                                   const void* x, const void* w_up_t, const void* w_down, float* y, float* a_save,
+                                   void* ws, size_t ws_bytes, void* gate_ws, size_t gate_ws_bytes, void* stream) {
+  twell::Shape s;
+  twell_sizes z;
+  twell::GateArgs g{};
+  twell_status st = fp8_prepare(dims, x_q, x_scale, w_q, w_scale, t, pack, nullptr, gate_ws, gate_ws_bytes,
+                                gate_ws != nullptr, &s, &z, &g);
+  if (st != TWELL_OK) return st;
+  twell::FwdArgs f{};
+  if ((st = fwd_prepare(s, z, TWELL_BF16, pack, x, w_up_t, w_down, y, a_save, ws, ws_bytes, &f)) != TWELL_OK)
+    return st;
+  if (s.N == 0) return TWELL_OK;
+  return hip_status(twell::launch_forward(g, f, (hipStream_t)stream), "twell_ffn_forward_fp8");
 }
 
 twell_status twell_ffn_forward(const twell_dims* dims, twell_dtype dtype, const void* x, const void* w_gate_t,

@@ -29,7 +29,7 @@ _STATUS = {0: "TWELL_OK", 1: "TWELL_ERR_INVALID_ARG", 2: "TWELL_ERR_UNSUPPORTED"
 # Every symbol include/twell.h declares.
 EXPORTS = ("twell_status_str", "twell_last_error", "twell_n_tiles", "twell_query_sizes", "twell_gate_pack",
            "twell_gate_pack_ws", "twell_pack_preact", "twell_quantize_e4m3", "twell_gate_pack_fp8",
-           "twell_gate_pack_fp8_ws", "twell_ffn_fwd", "twell_ffn_forward",
+           "twell_gate_pack_fp8_ws", "twell_ffn_fwd", "twell_ffn_forward", "twell_ffn_forward_fp8",
            "twell_route_hybrid", "twell_ffn_bwd", "twell_trace_start", "twell_trace_stop", "twell_trace_count",
            "twell_trace_dropped", "twell_trace_get")
 
@@ -102,6 +102,8 @@ def lib() -> ctypes.CDLL:
         L.twell_ffn_fwd.argtypes = [pd, ctypes.c_int, pp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.twell_ffn_forward.restype = ctypes.c_int
         L.twell_ffn_forward.argtypes = [pd, ctypes.c_int, vp, vp, vp, pp, vp, vp, vp, vp, vp, sz, vp, sz, vp]
+        L.twell_ffn_forward_fp8.restype = ctypes.c_int
+        L.twell_ffn_forward_fp8.argtypes = [pd, vp, vp, vp, vp, vp, pp, vp, vp, vp, vp, vp, vp, sz, vp, sz, vp]
         L.twell_route_hybrid.restype = ctypes.c_int
         L.twell_route_hybrid.argtypes = [pd, ctypes.c_int, pp, vp, ph, vp]
         L.twell_ffn_bwd.restype = ctypes.c_int
@@ -298,6 +300,18 @@ def ffn_forward(dims: Dims, dtype: int, x, w_gate_t, t, pack: TwellPack, w_up_t,
                                    _ptr(gate_ws), gbytes, _stream(stream)), "twell_ffn_forward")
 
 
+def ffn_forward_fp8(dims: Dims, x_q, x_scale, w_q, w_scale, t, pack: TwellPack, x, w_up_t, w_down, y, a_save=None,
+                    ws=None, gate_ws=None, stream=None) -> None:
+    """gate_pack_fp8 (with gate_ws when given) then ffn_fwd in one call (twell_ffn_forward_fp8)."""
+    p = pack.struct()
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    gbytes = 0 if gate_ws is None else gate_ws.numel() * gate_ws.element_size()
+    _check(lib().twell_ffn_forward_fp8(ctypes.byref(dims), _ptr(x_q), _ptr(x_scale), _ptr(w_q), _ptr(w_scale), _ptr(t),
+                                       ctypes.byref(p), _ptr(x), _ptr(w_up_t), _ptr(w_down), _ptr(y), _ptr(a_save),
+                                       _ptr(ws), nbytes, _ptr(gate_ws), gbytes, _stream(stream)),
+           "twell_ffn_forward_fp8")
+
+
 def route_hybrid(dims: Dims, dtype: int, pack: TwellPack, a_save, hyb: TwellHybrid, stream=None) -> None:
     p, h = pack.struct(), hyb.struct()
     _check(lib().twell_route_hybrid(ctypes.byref(dims), int(dtype), ctypes.byref(p), _ptr(a_save),
@@ -339,7 +353,7 @@ class TwellFFN:
     backward(): route_hybrid -> ffn_bwd
     With fp8_gate (bf16 forward only), forward() takes the gate weight as
     (E4M3 codes, row scales) from quantize_e4m3 and runs
-    quantize_e4m3(x) -> gate_pack_fp8 -> ffn_fwd.
+    quantize_e4m3(x) -> gate_pack_fp8 + ffn_fwd in one call (ffn_forward_fp8).
     All buffers are allocated once here, with torch, on `device`.
     """
 
@@ -371,6 +385,10 @@ class TwellFFN:
         if self.fp8_gate:
             w_q, w_scale = w_gate_t
             quantize_e4m3(x, stream=stream, out=(self.x_q, self.x_scale))
+            if g_dump is None:
+                ffn_forward_fp8(self.dims, self.x_q, self.x_scale, w_q, w_scale, t, self.pack, x, w_up_t, w_down, self.y,
+                                a_save=self.a_save, ws=self.ws_fwd, gate_ws=self.ws_gate, stream=stream)
+                return self.y
             gate_pack_fp8(self.dims, self.x_q, self.x_scale, w_q, w_scale, t, self.pack, g_dump=g_dump, stream=stream,
                           ws=self.ws_gate)
         elif g_dump is None:

@@ -261,6 +261,16 @@ twell_status twell_ffn_forward(const twell_dims* dims, twell_dtype dtype, const 
                                float* y, float* a_save, void* ws, size_t ws_bytes, void* gate_ws,
                                size_t gate_ws_bytes, void* stream);
 
+/* twell_ffn_forward with the FP8 gate: twell_gate_pack_fp8 (or
+ * twell_gate_pack_fp8_ws when gate_ws is not NULL) followed by twell_ffn_fwd
+ * (bf16 x and weights) on the same stream, in one call, with the same
+ * outputs and the same overlap of the overflow branch. Arguments as in those
+ * calls; the pack buffers are those of TWELL_BF16. */
+twell_status twell_ffn_forward_fp8(const twell_dims* dims, const uint8_t* x_q, const float* x_scale,
+                                   const uint8_t* w_q, const float* w_scale, const float* t, const twell_pack* pack,
+                                   const void* x, const void* w_up_t, const void* w_down, float* y, float* a_save,
+                                   void* ws, size_t ws_bytes, void* gate_ws, size_t gate_ws_bytes, void* stream);
+
 /* Stage 3a: route every row to the row-ELL (width K = dims->row_cap >= 1) or to
  * the dense backup (rule at twell_hybrid). a_save is the array filled by
  * twell_ffn_fwd. Writes every field of *out. */

@@ -105,6 +105,9 @@ def test_new_calls_validate_before_touching_the_device():
     assert L.twell_ffn_forward(ctypes.byref(d), 0, fake, fake, fake, ctypes.byref(p), fake, fake, fake, None, fake,
                                ws_fwd, None, 0, None) == 1  # pack pointers NULL
     assert b"pack" in L.twell_last_error()
+    assert L.twell_ffn_forward_fp8(ctypes.byref(d), None, None, None, None, None, ctypes.byref(p), None, None, None,
+                                   None, None, None, 0, None, 0, None) == 1
+    assert b"x_q" in L.twell_last_error()
     # quantiser: shapes, dtype, pointers
     assert L.twell_quantize_e4m3(-1, 8, 0, fake, fake, fake, None) == 1
     assert L.twell_quantize_e4m3(4, 0, 0, fake, fake, fake, None) == 1

@@ -90,3 +90,35 @@ def test_combined_call_twice_in_a_row_is_stable():
     pl.ffn.forward(pl.x, pl.wg, pl.wu, pl.wd, pl.t)
     y2 = pl.forward().clone()
     _same(y1, y2, "y")
+
+
+@pytest.mark.parametrize("name,kw,slots", [
+    ("c4", dict(N=600, D=512, F=2048), 8),     # overflow rows
+    ("c2", dict(N=40, D=1024, F=1300), 4),     # small batch (split GEMV), overflow possible
+    ("c2", dict(N=48, D=512, F=1000), 128),    # small batch, no overflow possible
+])
+def test_combined_fp8_call_matches_separate_calls(name, kw, slots):
+    w = make_inputs(name, **kw)
+    print(f"[forward-call fp8] {name} {kw} S={slots}", flush=True)
+    pl = Pipeline(w, slots=slots)
+    dims = pl.dims
+    xq, xs = tw.quantize_e4m3(pl.x)
+    wq, wsc = tw.quantize_e4m3(pl.wg)
+    a = tw.TwellFFN(dims, tw.BF16)
+    b = tw.TwellFFN(dims, tw.BF16)
+    tw.ffn_forward_fp8(dims, xq, xs, wq, wsc, pl.t, a.pack, pl.x, pl.wu, pl.wd, a.y, ws=a.ws_fwd, gate_ws=a.ws_gate)
+    tw.gate_pack_fp8(dims, xq, xs, wq, wsc, pl.t, b.pack, ws=b.ws_gate)
+    tw.ffn_fwd(dims, tw.BF16, b.pack, pl.x, pl.wu, pl.wd, b.y, ws=b.ws_fwd)
+    torch.cuda.synchronize()
+    assert int(b.pack.status.item()) == 0
+    n = min(int(b.pack.n_ovf.item()), pl.ovf_cap)
+    for f in ("counts", "ovf_flag", "n_ovf", "status"):
+        _same(getattr(a.pack, f), getattr(b.pack, f), f)
+    _same(a.pack.ovf_rows[:n], b.pack.ovf_rows[:n], "ovf_rows")
+    _same(a.pack.ovf_h[:n], b.pack.ovf_h[:n], "ovf_h")
+    S, N = dims.slots, dims.n_tokens
+    cnt = (b.pack.counts.to(torch.int32) & 0xFFFF).clamp(max=S)
+    used = torch.arange(S, device=cnt.device)[None, :, None] < cnt[:, None, :]
+    _same(a.pack.vals.view(-1, S, N)[used], b.pack.vals.view(-1, S, N)[used], "vals")
+    _same(a.pack.cols.view(-1, S, N)[used], b.pack.cols.view(-1, S, N)[used], "cols")
+    _same(a.y, b.y, "y")
