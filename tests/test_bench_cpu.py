@@ -60,3 +60,34 @@ def test_committed_step_traffic_summaries_parse(wl):
                      "dense": float(kv["dense_hbm_bytes_per_step"])}
     else:
         assert m is None
+
+
+def test_more_than_one_gpu_is_refused():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(bench.ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in r.stderr
+
+
+def _traffic_files():
+    d = os.path.join(bench.ROOT, "profiles")
+    return sorted(f for f in os.listdir(d) if f.endswith("_traffic.txt") and not f.startswith("step_traffic_"))
+
+
+@pytest.mark.parametrize("fname", _traffic_files())
+def test_committed_kernel_traffic_summaries_parse(fname):
+    kv = {}
+    for line in open(os.path.join(bench.ROOT, "profiles", fname)):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    kernel, workload = kv["kernel"], kv["workload"]
+    assert fname == f"{kernel}_{workload}_traffic.txt"
+    assert kernel in bench.KERNEL_SOURCES
+    b = float(kv["hbm_bytes_per_launch"])
+    f, w = float(kv["fetch_kib_per_dispatch"]), float(kv["write_kib_per_dispatch"])
+    assert abs(b - (f * float(kv["fetch_scale"]) + w * float(kv["write_scale"])) * 1024) <= 1e-6 * b + 1024
+    m = bench.measured_traffic(kernel, workload)
+    assert m == (b if kv["source_sha256_16"] == bench.kernel_source_hash(kernel) else None)
