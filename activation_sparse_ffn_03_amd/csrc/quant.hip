@@ -9,9 +9,10 @@
 // One wavefront per row (four rows per workgroup): the row is read once with
 // 16-byte loads and kept in registers (rows longer than 64 * 16 * kRegChunks
 // bytes re-read the rest from L2), its largest magnitude is reduced across
-// the wave, scale = max / 448 in fp32 (1 for an all-zero row, and for a row
-// holding NaN: the maximum is taken on the magnitudes' bit patterns, so NaN
-// wins it and fails the > 0 test), then every element x / scale (IEEE fp32
+// the wave, scale = max / 448 in fp32 (1 when that is not > 0: an all-zero
+// row, a row whose maximum underflows, and a row holding NaN, since the
+// maximum is taken on the magnitudes' bit patterns and NaN wins it), then
+// every element x / scale (IEEE fp32
 // division) is encoded: sign bit, 4 exponent bits with bias 7, 3 mantissa
 // bits, subnormals m * 2^-9, magnitudes of 448 and above saturated to 448,
 // NaN to 0x7F (rows with a finite maximum use the hardware conversion, which
@@ -77,18 +78,26 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t m) {
   return m;
 }
 
-// scale of a row from the bit pattern of its largest magnitude
+// scale of a row from the bit pattern of its largest magnitude: m / 448 in
+// fp32, or 1 when that is not > 0 (an all-zero row, a row holding NaN, or a
+// maximum so small that the quotient underflows to 0)
 __device__ __forceinline__ float row_scale(uint32_t mbits) {
-  const float m = __uint_as_float(mbits);
-  return m > 0.f ? m / 448.0f : 1.0f;  // NaN fails the test
+  const float s = __uint_as_float(mbits) / 448.0f;
+  return s > 0.f ? s : 1.0f;  // NaN fails the test
 }
+
+// Bit pattern of 448 * 2^-126: rows whose largest magnitude is at least this
+// have a normal scale, so every quotient stays below 448.001.
+constexpr uint32_t kHwMinMaxBits = 0x04E00000u;
 
 // Codes of four quotients with the hardware conversion (v_cvt_pk_fp8_f32,
 // round to nearest even). A sweep of all 2^32 fp32 bit patterns on gfx950
 // found it equal to e4m3_code for every |v| <= 448, subnormals and -0
 // included; it differs only above 464 and on NaN and infinities. A row whose
-// largest magnitude m is finite has every quotient |x / scale| <= m / fl(m /
-// 448) < 448.001, so such rows may take it.
+// largest magnitude m is finite and at least 448 * 2^-126 has a normal scale
+// fl(m / 448) and every quotient |x / scale| <= m / fl(m / 448) < 448.001, so
+// such rows may take it. (A smaller m gives a subnormal scale, rounded by up
+// to half of 2^-149, and quotients up to 512 and beyond.)
 __device__ __forceinline__ uint32_t e4m3_codes_hw(float a, float b, float c, float d) {
   const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
@@ -163,9 +172,10 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void quantize_rows_vec(const TS
     }
     for (int i = lane + 64 * kRegChunks; i < nch; i += 64) encode_chunk<TS, HW>(row[i], sc, qrow + (size_t)i * EPC);
   };
-  // finite largest magnitude (wave-uniform): every quotient is within the
-  // hardware conversion's exact range; NaN or infinity in the row: software
-  if (mbits < 0x7F800000u)
+  // finite largest magnitude with a normal scale (wave-uniform): every
+  // quotient is within the hardware conversion's exact range; NaN or infinity
+  // in the row, or a subnormal scale: software
+  if (mbits < 0x7F800000u && mbits >= kHwMinMaxBits)
     encode(std::true_type{});
   else
     encode(std::false_type{});

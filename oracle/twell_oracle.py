@@ -40,7 +40,8 @@ rounded value is what the up/down products and the backward use.
 
 Parity status: every function here is pinned by the CPU test suite against
 closed forms, torch float64 autograd, finite differences, brute-force
-enumeration or hand-worked fixtures; none is "parity unpinned".
+enumeration or hand-worked fixtures (the FP8 quantiser and FP8 gate by the
+hand-worked tests/golden/fp8_handworked.json); none is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -196,13 +197,17 @@ def e4m3_encode(v) -> np.ndarray:
 
 
 def quantize_rows_e4m3(a):
-    """Per-row FP8 quantisation: scale = float32(max|row|) / 448 in float32
-    (1 for an all-zero row), q = e4m3(float32(a / scale)). Returns (q uint8,
-    scale float32)."""
+    """Per-row FP8 quantisation: scale = float32(max|row|) / 448 in float32,
+    replaced by 1 when it is not > 0 (an all-zero row, a row holding NaN, or a
+    maximum so small that the quotient underflows to 0: a zero scale would
+    turn the row's zeros into NaN codes); q = e4m3(float32(a / scale)).
+    Returns (q uint8, scale float32)."""
     a32 = np.asarray(a, dtype=np.float32)
     amax = np.max(np.abs(a32), axis=1) if a32.shape[1] else np.zeros(a32.shape[0], np.float32)
-    scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
-    scaled = (a32 / scale[:, None]).astype(np.float32)
+    with np.errstate(invalid="ignore"):
+        scale = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+        scale = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+        scaled = (a32 / scale[:, None]).astype(np.float32)
     return e4m3_encode(scaled), scale
 
 

@@ -60,6 +60,17 @@ def test_quantize_e4m3_bit_exact(dtype, cols):
     a[11, 2] = np.inf      # scale inf: finite elements -> +-0, inf -> 0x7F
     a[13] = -0.0           # sign of zero kept
     a[13, 1] = 0.0
+    if dtype == "f32":
+        # largest magnitude below 448 * 2^-126: the scale is subnormal (2^-149
+        # here) and the largest quotient 512 saturates
+        a[15] = 0.0
+        a[15, :4] = np.array([2.0 ** -140, -(2.0 ** -141), 2.0 ** -149, 3 * 2.0 ** -145])
+        # the quotient max / 448 underflows to 0: scale 1, every code +-0
+        a[17] = 0.0
+        a[17, :3] = np.array([2.0 ** -146, -(2.0 ** -147), 2.0 ** -149])
+        # maximum just above and just below 448 * 2^-126 (normal scale or not)
+        a[19] *= np.float32(448.0 * 2.0 ** -126) / np.float32(np.abs(a[19]).max())
+        a[21] *= np.float32(447.0 * 2.0 ** -126) / np.float32(np.abs(a[21]).max())
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
     dev = torch.from_numpy(a).cuda().to(tdt)
     q, s = tw.quantize_e4m3(dev)

@@ -498,3 +498,102 @@ def test_gate_preact_fp8_closed_form():
     sx = np.float32(2.0) ** rng.integers(-3, 3, 9).astype(np.float32)
     sw = np.float32(2.0) ** rng.integers(-3, 3, 13).astype(np.float32)
     np.testing.assert_allclose(orc.gate_preact_fp8(xq, sx, wq, sw), ref * np.outer(sx, sw), rtol=0, atol=0)
+
+
+# ---------------------------------------------------------------- FP8: hand-worked fixture
+
+def _fp8_fixture():
+    with open(os.path.join(GOLD, "fp8_handworked.json")) as fh:
+        return json.load(fh)
+
+
+def _f32_from_bits(hexes):
+    return np.array([int(h, 16) for h in hexes], dtype=np.uint32).view(np.float32)
+
+
+def _fp8_gate_operands(fx):
+    from fractions import Fraction
+    g = fx["gate"]
+    D = g["d_model"]
+
+    def codes(rows):
+        out = np.zeros((len(rows), D), dtype=np.uint8)
+        for r, nz in enumerate(rows):
+            for k, c in nz.items():
+                out[r, int(k)] = int(c, 16)
+        return out
+
+    xq, wq = codes(g["x_codes_nonzero"]), codes(g["w_codes_nonzero"])
+    sx = np.array([float(Fraction(v)) for v in g["x_scale"]], dtype=np.float32)
+    sw = np.array([float(Fraction(v)) for v in g["w_scale"]], dtype=np.float32)
+    expect = np.array([[float(Fraction(v)) for v in row] for row in g["expect_g"]])
+    return xq, sx, wq, sw, expect
+
+
+def _check_quantize_fixture(quantize, fx):
+    q = fx["quantize"]
+    for bits, scale_bits, codes in zip(q["rows_f32_bits"], q["expect_scale_f32_bits"], q["expect_codes"]):
+        row = _f32_from_bits(bits)[None, :]
+        got_q, got_s = quantize(row)
+        assert got_s.dtype == np.float32
+        if got_s.view(np.uint32)[0] != int(scale_bits, 16):
+            return False
+        if not np.array_equal(got_q[0], np.array([int(c, 16) for c in codes], dtype=np.uint8)):
+            return False
+    return True
+
+
+def test_quantize_rows_e4m3_handworked():
+    """Rows quantised by hand (tests/golden/fp8_handworked.json): a
+    non-power-of-two scale, ties to the even code in the normal and the
+    subnormal range, a scale rounded up in fp32, a deep-subnormal maximum whose
+    quotient saturates, and a maximum whose quotient underflows (scale 1)."""
+    assert _check_quantize_fixture(orc.quantize_rows_e4m3, _fp8_fixture())
+
+
+def test_gate_preact_fp8_handworked():
+    """FP8 gate on hand-decoded codes (subnormal, negative, 0x7E) with
+    non-power-of-two scales; g written out exactly by hand."""
+    xq, sx, wq, sw, expect = _fp8_gate_operands(_fp8_fixture())
+    np.testing.assert_array_equal(orc.gate_preact_fp8(xq, sx, wq, sw), expect)
+
+
+def test_fp8_fixture_catches_planted_mistakes():
+    """The fixture is sharp enough to fail plausible mistakes planted in copies
+    of the oracle functions (on the CPU): the scale computed as
+    max * fl32(1/448), the scale rule without the underflow case, the row and
+    column scales swapped, a dropped subnormal decode and a lost sign."""
+    fx = _fp8_fixture()
+
+    def q_recip(a):
+        a32 = np.asarray(a, dtype=np.float32)
+        amax = np.max(np.abs(a32), axis=1)
+        s = (amax * (np.float32(1.0) / np.float32(448.0))).astype(np.float32)
+        s = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+        return orc.e4m3_encode((a32 / s[:, None]).astype(np.float32)), s
+
+    def q_no_underflow_rule(a):
+        a32 = np.asarray(a, dtype=np.float32)
+        amax = np.max(np.abs(a32), axis=1)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            s = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+            return orc.e4m3_encode((a32 / s[:, None]).astype(np.float32)), s
+
+    assert not _check_quantize_fixture(q_recip, fx)
+    assert not _check_quantize_fixture(q_no_underflow_rule, fx)
+
+    xq, sx, wq, sw, expect = _fp8_gate_operands(fx)
+    dec = orc.e4m3_decode
+    swapped = np.outer(sw[:3], sx[:3]).astype(np.float64) * (dec(xq) @ dec(wq).T)
+    assert not np.array_equal(swapped, expect)
+
+    def dec_no_sub(q):
+        v = dec(q)
+        return np.where((np.asarray(q) & 0x78) == 0, 0.0, v)
+
+    assert not np.array_equal(np.outer(sx, sw) * (dec_no_sub(xq) @ dec_no_sub(wq).T), expect)
+
+    def dec_abs(q):
+        return np.abs(dec(q))
+
+    assert not np.array_equal(np.outer(sx, sw) * (dec_abs(xq) @ dec_abs(wq).T), expect)
