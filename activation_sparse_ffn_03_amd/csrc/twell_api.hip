@@ -115,14 +115,14 @@ static twell::GateArgs gate_args(const twell::Shape& s, const twell_sizes& z, co
 // Validation and launch arguments of a bf16 / fp32 gate call (x and w_gate_t,
 // or a given pre-activation g).
 static twell_status gate_prepare(const twell_dims* dims, twell_dtype dtype, const void* x, const void* w_gate_t,
-                                 const float* g_in, const float* t, const twell_pack* out, float* g_dump,
-                                 void* ws, size_t ws_bytes, bool use_ws, twell::Shape* s, twell_sizes* z,
-                                 twell::GateArgs* a) {
+                                 const float* g_in, bool from_g, const float* t, const twell_pack* out,
+                                 float* g_dump, void* ws, size_t ws_bytes, bool use_ws, twell::Shape* s,
+                                 twell_sizes* z, twell::GateArgs* a) {
   twell_status st = prepare(dims, dtype, s, z);
   if (st != TWELL_OK) return st;
   if ((st = check_gate_ws(*z, ws, ws_bytes, use_ws)) != TWELL_OK) return st;
   const size_t xd = (size_t)s->N * s->D * s->esz, wd = (size_t)s->F * s->D * s->esz;
-  if (g_in == nullptr) {
+  if (!from_g) {
     TWELL_CHECK_PTR(x, xd, "x");
     TWELL_CHECK_PTR(w_gate_t, wd, "w_gate_t");
   } else {
@@ -140,26 +140,26 @@ static twell_status gate_prepare(const twell_dims* dims, twell_dtype dtype, cons
 }
 
 static twell_status gate_common(const twell_dims* dims, twell_dtype dtype, const void* x, const void* w_gate_t,
-                                const float* g_in, const float* t, const twell_pack* out, float* g_dump,
-                                void* ws, size_t ws_bytes, bool use_ws, void* stream) {
+                                const float* g_in, bool from_g, const float* t, const twell_pack* out,
+                                float* g_dump, void* ws, size_t ws_bytes, bool use_ws, void* stream) {
   twell::Shape s;
   twell_sizes z;
   twell::GateArgs a{};
   const twell_status st =
-      gate_prepare(dims, dtype, x, w_gate_t, g_in, t, out, g_dump, ws, ws_bytes, use_ws, &s, &z, &a);
+      gate_prepare(dims, dtype, x, w_gate_t, g_in, from_g, t, out, g_dump, ws, ws_bytes, use_ws, &s, &z, &a);
   if (st != TWELL_OK || s.N == 0) return st;
   return hip_status(twell::launch_gate_pack(a, (hipStream_t)stream), "twell_gate_pack");
 }
 
 twell_status twell_gate_pack(const twell_dims* dims, twell_dtype dtype, const void* x, const void* w_gate_t,
                              const float* t, const twell_pack* out, float* g_dump, void* stream) {
-  return gate_common(dims, dtype, x, w_gate_t, nullptr, t, out, g_dump, nullptr, 0, false, stream);
+  return gate_common(dims, dtype, x, w_gate_t, nullptr, false, t, out, g_dump, nullptr, 0, false, stream);
 }
 
 twell_status twell_gate_pack_ws(const twell_dims* dims, twell_dtype dtype, const void* x, const void* w_gate_t,
                                 const float* t, const twell_pack* out, float* g_dump, void* ws, size_t ws_bytes,
                                 void* stream) {
-  return gate_common(dims, dtype, x, w_gate_t, nullptr, t, out, g_dump, ws, ws_bytes, true, stream);
+  return gate_common(dims, dtype, x, w_gate_t, nullptr, false, t, out, g_dump, ws, ws_bytes, true, stream);
 }
 
 twell_status twell_quantize_e4m3(int64_t rows, int32_t cols, twell_dtype dtype, const void* in, uint8_t* q,
@@ -227,8 +227,7 @@ twell_status twell_gate_pack_fp8_ws(const twell_dims* dims, const uint8_t* x_q, 
 
 twell_status twell_pack_preact(const twell_dims* dims, twell_dtype dtype, const float* g, const float* t,
                                const twell_pack* out, void* stream) {
-  if (g == nullptr) return fail(TWELL_ERR_INVALID_ARG, "g is NULL");
-  return gate_common(dims, dtype, nullptr, nullptr, g, t, out, nullptr, nullptr, 0, false, stream);
+  return gate_common(dims, dtype, nullptr, nullptr, g, true, t, out, nullptr, nullptr, 0, false, stream);
 }
 
 // Validation and launch arguments of the up/down projection (shape already
@@ -320,8 +319,8 @@ twell_status twell_ffn_forward(const twell_dims* dims, twell_dtype dtype, const 
   twell::Shape s;
   twell_sizes z;
   twell::GateArgs g{};
-  twell_status st = gate_prepare(dims, dtype, x, w_gate_t, nullptr, t, pack, nullptr, gate_ws, gate_ws_bytes,
-                                 gate_ws != nullptr, &s, &z, &g);
+  twell_status st = gate_prepare(dims, dtype, x, w_gate_t, nullptr, false, t, pack, nullptr, gate_ws,
+                                 gate_ws_bytes, gate_ws != nullptr, &s, &z, &g);
   if (st != TWELL_OK) return st;
   twell::FwdArgs f{};
   if ((st = fwd_prepare(s, z, dtype, pack, x, w_up_t, w_down, y, a_save, ws, ws_bytes, &f)) != TWELL_OK) return st;

@@ -117,3 +117,72 @@ def test_new_calls_validate_before_touching_the_device():
     # FP8 gate: missing operands
     assert L.twell_gate_pack_fp8(ctypes.byref(d), None, fake, fake, fake, fake, ctypes.byref(p), None, None) == 1
     assert L.twell_gate_pack_fp8(ctypes.byref(d), fake, fake, fake, None, fake, ctypes.byref(p), None, None) == 1
+
+
+# ---------------------------------------------------------------- header <-> binding marshalling
+
+_C_SCALARS = {"int64_t": ctypes.c_int64, "int32_t": ctypes.c_int32, "int": ctypes.c_int, "twell_dtype": ctypes.c_int,
+              "size_t": ctypes.c_size_t, "float": ctypes.c_float, "uint32_t": ctypes.c_uint32}
+
+
+def _header_text():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", " ", txt, flags=re.S)
+    return re.sub(r"//[^\n]*", " ", txt)
+
+
+def _c_kind(decl: str):
+    """'pointer' for any pointer parameter or field, else the ctypes scalar."""
+    decl = decl.strip()
+    if "*" in decl:
+        return "pointer"
+    typ = " ".join(decl.split()[:-1]).replace("const ", "").strip()
+    return _C_SCALARS[typ]
+
+
+def _py_kind(t):
+    if t in (ctypes.c_void_p, ctypes.c_char_p) or (isinstance(t, type) and issubclass(t, ctypes._Pointer)):
+        return "pointer"
+    return t
+
+
+def test_binding_signatures_match_the_header():
+    """Every prototype in twell.h against the binding's argtypes / restype:
+    the same number of parameters, pointers where the header has pointers and
+    the same scalar type otherwise (a mismatch would corrupt the call)."""
+    txt = _header_text()
+    protos = re.findall(r"([A-Za-z_][A-Za-z0-9_ ]*?[\s\*]+)(twell_[a-z0-9_]+)\s*\(([^)]*)\)\s*;", txt)
+    assert {p[1] for p in protos} == set(tw.EXPORTS)
+    L = tw.lib()
+    for ret, name, params in protos:
+        fn = getattr(L, name)
+        params = params.strip()
+        want = [] if params in ("", "void") else [_c_kind(p) for p in params.split(",")]
+        got = [_py_kind(t) for t in fn.argtypes]
+        assert got == want, f"{name}: binding {got} vs header {want}"
+        ret = ret.strip()
+        rk = "pointer" if "*" in ret else {"twell_status": ctypes.c_int, "int32_t": ctypes.c_int32}[ret]
+        assert _py_kind(fn.restype) == rk, f"{name}: return type"
+
+
+@pytest.mark.parametrize("cname,pycls", [("twell_dims", tw.Dims), ("twell_pack", tw.Pack),
+                                         ("twell_hybrid", tw.Hybrid), ("twell_sizes", tw.Sizes)])
+def test_binding_structs_match_the_header(cname, pycls):
+    """Field order and types of each struct in twell.h against the ctypes
+    Structure the binding passes by reference."""
+    txt = _header_text()
+    body = re.search(r"typedef struct " + cname + r"\s*\{(.*?)\}\s*" + cname + r"\s*;", txt, re.S).group(1)
+    fields = []
+    for decl in body.split(";"):
+        decl = decl.strip()
+        if not decl:
+            continue
+        m = re.match(r"(.*?)([A-Za-z_][A-Za-z0-9_\s,\*]*)$", decl)
+        base = decl.split()[0] if not decl.startswith("const") else " ".join(decl.split()[:2])
+        names = decl[len(base):]
+        for n in names.split(","):
+            n = n.strip()
+            fields.append((n.lstrip("*").strip(), "pointer" if n.startswith("*") or base.endswith("*")
+                           else _C_SCALARS[base]))
+    got = [(n, _py_kind(t)) for n, t in pycls._fields_]
+    assert got == fields, f"{cname}: binding {got} vs header {fields}"
