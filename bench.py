@@ -2,13 +2,14 @@
 """Benchmark of the libtwell hot path on one MI355X.
 
 A step is one pass of the whole hot path over one batch of synthetic input.
-The default workload is the 1B-class forward (4096 tokens, d_model 2048, d_ff
-5632, uniform gate density 1%): gate GEMM with the TwELL pack epilogue,
-overflow rows, and the fused up/down projection. The other workloads are
-picked with --workload: the 7B-class forward at three densities, the
-skewed-density forward, the training step (forward saving a, hybrid
-routing and the sparse backward), and the 1B / 7B forwards with the gate
-projection on FP8 E4M3 operands (x quantised per step, W_gate once).
+The default workload is the 7B-class forward (16384 tokens, d_model 4096, d_ff
+11008, uniform gate density 1%), the largest single-GPU configuration: gate
+GEMM with the TwELL pack epilogue, overflow rows, and the fused up/down
+projection. The other workloads are picked with --workload: the 1B-class
+forward, the 7B-class forward at 5% and 0.5%, the skewed-density forward, the
+training step (forward saving a, hybrid routing and the sparse backward), and
+the 1B / 7B forwards with the gate projection on FP8 E4M3 operands (x
+quantised per step, W_gate once).
 
 Prints ONE JSON line: throughput in tokens/s, the dense bf16 FFN on the same
 GPU and inputs as reference, the roofline of the dominant kernel (device time
@@ -68,7 +69,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="c2", choices=sorted(WORKLOADS))
+    p.add_argument("--workload", default="c3_1", choices=sorted(WORKLOADS))
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-dense", action="store_true")
     p.add_argument("--no-graph", action="store_true", help="skip the graph-replay timings")
@@ -381,9 +382,9 @@ def main():
     # the forward replayed from a HIP graph (the serving-loop form: no host
     # launch cost per kernel); same inputs, same K steps
     graph_ms = None
-    # graph replays are timed for the uniform-density forwards; the
-    # skewed-density forward is timed eagerly only
-    replay = not train and not args.no_graph and w.density[0] == "uniform"
+    # graph replays are timed for the forwards whose capture is supported
+    # (TwellFFN.capture_supported); the others are timed eagerly only
+    replay = not train and not args.no_graph and ffn.capture_supported()
     if replay:
         graph = ffn.capture(x, wgate, wu, wd, t)
         for _ in range(args.warmup):

@@ -138,3 +138,46 @@ def test_forward_graph_replay(name, N):
         torch.cuda.synchronize()
         assert torch.equal(y_graph.view(torch.int32), y_eager.view(torch.int32)), rep
         assert torch.equal(ffn.pack.counts, eager.pack.counts), rep
+
+
+def test_capture_refused_where_not_cleared():
+    """capture() raises on the bf16 forward with d_model > 2048 and possible
+    overflow rows (the path with the unexplained abort at process exit), and
+    allows the small-batch and no-overflow forms of the same layer."""
+    require_gpu()
+    w = make_inputs("c4", seed=11, N=128, D=4096, F=1024)
+    dims = tw.make_dims(128, 4096, 1024, 128, 16, 0, 32, 0)
+    ffn = tw.TwellFFN(dims, tw.BF16)
+    assert not ffn.capture_supported()
+    x, wg, wu, wd = (dev(a, "bf16") for a in (w.x, w.w_gate_t, w.w_up_t, w.w_down))
+    with pytest.raises(tw.TwellError):
+        ffn.capture(x, wg, wu, wd, torch.from_numpy(w.t).cuda())
+    assert tw.TwellFFN(tw.make_dims(128, 4096, 1024, 128, 128, 0, 32, 0), tw.BF16).capture_supported()
+    assert tw.TwellFFN(tw.make_dims(48, 4096, 1024, 128, 16, 0, 48, 0), tw.BF16).capture_supported()
+    assert tw.TwellFFN(tw.make_dims(128, 2048, 1024, 128, 16, 0, 32, 0), tw.BF16).capture_supported()
+
+
+@pytest.mark.skip(reason="graph capture of the bf16 forward with d_model > 2048 and overflow rows is disabled: one "
+                         "process that captured and replayed it (8192 x 4096 x 14336, skewed density) aborted at exit "
+                         "in glibc (free(): invalid pointer) with no GPU fault; cause not found, so the case stays "
+                         "off the GPU")
+def test_forward_graph_replay_skewed_density_full_size():
+    """The 8192 x 4096 x 14336 skewed-density forward (overflow rows present)
+    recorded into a HIP graph and replayed: each replay equals the eager
+    forward bit for bit, and the process exits cleanly."""
+    require_gpu()
+    w = make_inputs("c4")
+    dims = tw.make_dims(w.N, w.D, w.F, w.tile_n, w.slots, 0, max(64, w.N // 8), 0)
+    ffn = tw.TwellFFN(dims, tw.BF16)
+    x, wg, wu, wd = (dev(a, "bf16") for a in (w.x, w.w_gate_t, w.w_up_t, w.w_down))
+    t = torch.from_numpy(w.t).cuda()
+    graph = ffn.capture(x, wg, wu, wd, t)
+    eager = tw.TwellFFN(dims, tw.BF16)
+    for rep in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        y_graph = ffn.y.clone()
+        y_eager = eager.forward(x, wg, wu, wd, t).clone()
+        torch.cuda.synchronize()
+        assert int(eager.pack.n_ovf.item()) > 0
+        assert torch.equal(y_graph.view(torch.int32), y_eager.view(torch.int32)), rep

@@ -188,3 +188,139 @@ def test_fullsize_training_step():
                (dhc * np.abs(bc["dz"])).T @ np.abs(w.x.astype(np.float64)))
     rowwise_ok(f64(dwd[ci]), bc["dw_down"], Y_TOL, "c5 dW_down",
                (dhc * np.abs(fc["a"])).T @ np.abs(w.dy.astype(np.float64)))
+
+
+def _hybrid_mask_h(ffn, w, rows=None, cols=None):
+    """The GPU's own mask and stored activation, read back from the hybrid
+    format the backward consumes: the row-ELL (positions < row_nnz) for ELL
+    rows and the dense-backup rows (active iff the stored h > 0, the rule the
+    backward applies to them). Returns (mask, hq) restricted to `rows` (all
+    columns) or to `cols` (all rows)."""
+    N, F = w.N, w.F
+    K = w.row_cap
+    row_nnz = ffn.hyb.row_nnz.cpu().numpy().astype(np.int64)
+    is_dense = ffn.hyb.is_dense.cpu().numpy().astype(bool)
+    nd = int(ffn.hyb.n_dense.item())
+    dense_rows = ffn.hyb.dense_rows[:nd].cpu().numpy().astype(np.int64)
+    pos = np.full(N, -1, dtype=np.int64)
+    pos[dense_rows] = np.arange(nd)
+    ell_cols = ffn.hyb.ell_cols.cpu().numpy().astype(np.int64)        # [K][N]
+    ell_vals = f64(ffn.hyb.ell_vals)                                  # [K][N]
+    valid = (np.arange(K)[:, None] < row_nnz[None, :]) & ~is_dense[None, :]
+    if rows is not None:
+        sel_rows, sel_cols = rows, np.arange(F)
+    else:
+        sel_rows, sel_cols = np.arange(N), cols
+    colmap = np.full(F, -1, dtype=np.int64)
+    colmap[sel_cols] = np.arange(sel_cols.size)
+    rowmap = np.full(N, -1, dtype=np.int64)
+    rowmap[sel_rows] = np.arange(sel_rows.size)
+    hq = np.zeros((sel_rows.size, sel_cols.size))
+    k_idx, i_idx = np.nonzero(valid)
+    c_idx = ell_cols[k_idx, i_idx]
+    assert ((c_idx >= 0) & (c_idx < F)).all()
+    keep = (rowmap[i_idx] >= 0) & (colmap[c_idx] >= 0)
+    hq[rowmap[i_idx[keep]], colmap[c_idx[keep]]] = ell_vals[k_idx[keep], i_idx[keep]]
+    mask = np.zeros(hq.shape, dtype=bool)
+    mask[rowmap[i_idx[keep]], colmap[c_idx[keep]]] = True
+    dsel = [(r, pos[r]) for r in sel_rows if is_dense[r]]
+    if dsel:
+        dr = np.array([r for r, _ in dsel])
+        dh = f64(ffn.hyb.dense_h[torch.from_numpy(np.array([p for _, p in dsel])).cuda()])[:, sel_cols]
+        hq[rowmap[dr]] = dh
+        mask[rowmap[dr]] = dh > 0
+    # ascending global columns in every ELL row, and positive stored values
+    assert (hq[mask] > 0).all()
+    return mask, hq
+
+
+def test_fullsize_training_step_benchmark_thresholds():
+    """The training step exactly as bench.py times it: the generator's own
+    per-token thresholds (units may sit arbitrarily close to them), the
+    bench's capacities. The mask and the stored activation the backward uses
+    are read back from the GPU's hybrid format and fed to the oracle's
+    backward (ReLU' jumps at the threshold, so a near-threshold unit may fall
+    on either side; its h there is tiny). Checked: routing of every row; the
+    GPU mask against the oracle's fp64 g (disagreements only within the fp32
+    evaluation error of the threshold); the hybrid against the TwELL pack on
+    sampled rows; y and dx on sampled rows (dense-backup and overflow rows
+    included) and dW_gate, dW_up, dW_down on sampled columns, each within
+    1e-2 * rms of the oracle per row."""
+    w, train = _setup("c5")
+    assert train
+    print(f"[fullsize] c5 train, benchmark thresholds: N={w.N} D={w.D} F={w.F}", flush=True)
+    ovf_cap, dense_cap = capacities(w, True)
+    dims = tw.make_dims(w.N, w.D, w.F, w.tile_n, w.slots, w.row_cap, ovf_cap, dense_cap)
+    ffn = tw.TwellFFN(dims, tw.BF16, train=True)
+    x, wg, wu, wd, dy = (dev(a, "bf16") for a in (w.x, w.w_gate_t, w.w_up_t, w.w_down, w.dy))
+    y = ffn.forward(x, wg, wu, wd, torch.from_numpy(w.t).cuda())
+    dx, dwg, dwu, dwd = ffn.backward(x, dy, wg, wu, wd, w.lam)
+    torch.cuda.synchronize()
+    assert int(ffn.pack.status.item()) == 0 and int(ffn.hyb.status.item()) == 0
+
+    # routing of every row from the GPU's own counts
+    counts = u16(ffn.pack.counts)                                     # [n_t][N]
+    nnz = counts.sum(0)
+    np.testing.assert_array_equal(ffn.hyb.row_nnz.cpu().numpy(), nnz)
+    dense = (nnz > w.row_cap) | (counts > w.slots).any(0)
+    np.testing.assert_array_equal(ffn.hyb.is_dense.cpu().numpy().astype(bool), dense)
+    nd = int(ffn.hyb.n_dense.item())
+    np.testing.assert_array_equal(ffn.hyb.dense_rows[:nd].cpu().numpy(), np.nonzero(dense)[0])
+    assert nd > 0
+    n_ovf = int(ffn.pack.n_ovf.item())
+    ovf_rows = ffn.pack.ovf_rows[:n_ovf].cpu().numpy()
+    assert n_ovf > 0
+
+    rows = _sample_rows(w.N, np.concatenate([np.nonzero(dense)[0], ovf_rows]), k=40)
+    mask_r, hq_r = _hybrid_mask_h(ffn, w, rows=rows)
+
+    # the hybrid holds what the pack holds (ELL rows: slots in tile order, columns ascending)
+    vals, cols = f64(ffn.pack.vals), u16(ffn.pack.cols)
+    T, S = w.tile_n, w.slots
+    for r_i, r in enumerate(rows):
+        if dense[r]:
+            continue
+        want = np.zeros(w.F)
+        for j in range(counts.shape[0]):
+            c = int(counts[j, r])
+            want[j * T + cols[j, :c, r]] = vals[j, :c, r]
+        np.testing.assert_array_equal(hq_r[r_i], want, err_msg=f"hybrid vs pack, row {r}")
+
+    # the GPU mask against the oracle's g: disagreements only within the fp32 error of the threshold
+    g64 = orc.gate_preact(w.x[rows], w.w_gate_t)
+    t64 = w.t[rows].astype(np.float64)
+    ref_mask = g64 > t64[:, None]
+    rms_g = np.sqrt(np.mean(g64 * g64, axis=1))
+    near = np.abs(g64 - t64[:, None]) <= DELTA_REL * rms_g[:, None]
+    flips = mask_r != ref_mask
+    assert not (flips & ~near).any(), "mask differs from the oracle away from the threshold"
+    print(f"[fullsize] c5 benchmark thresholds: {int(flips.sum())} near-threshold mask flips in "
+          f"{rows.size} sampled rows, {int(near.sum())} units within the fp32 band", flush=True)
+    # the stored activation where both agree: Q(fl32(g) - t), up to the fp32
+    # evaluation error of g (relatively large where g - t is small) plus one
+    # rounding to bf16
+    fw = orc.ffn_forward(w.x[rows], w.w_gate_t, w.w_up_t, w.w_down, w.t[rows], store="bf16", arith="f32")
+    both = mask_r & ref_mask
+    dh = np.abs(hq_r - fw["hq"])
+    allowed = DELTA_REL * rms_g[:, None] + orc.store_ulp(np.maximum(np.abs(hq_r), np.abs(fw["hq"])), "bf16")
+    assert (dh[both] <= allowed[both]).all(), "stored activation beyond the fp32 error of g plus one bf16 ulp"
+    print(f"[fullsize] c5 benchmark thresholds: stored h differs from the oracle's in {int((dh[both] > 0).sum())} "
+          f"of {int(both.sum())} active units (largest {float((dh / allowed)[both].max()):.3f} of the bound)",
+          flush=True)
+
+    # y and dx of the sampled rows from the GPU's mask and h
+    a_r = fw["a"]
+    y_ref = (hq_r * a_r) @ w.w_down.astype(np.float64)
+    rowwise_ok(f64(y[torch.from_numpy(rows).cuda()]), y_ref, Y_TOL, "c5 (benchmark thresholds) y")
+    br = orc.ffn_backward(w.x[rows], w.dy[rows], w.w_gate_t, w.w_up_t, w.w_down, mask_r, hq_r, w.lam)
+    rowwise_ok(f64(dx[torch.from_numpy(rows).cuda()]), br["dx"], Y_TOL, "c5 (benchmark thresholds) dx")
+
+    # weight gradients on sampled columns, over every token, from the GPU's mask and h
+    rng = np.random.default_rng(13)
+    ccols = np.sort(rng.choice(w.F, size=24, replace=False))
+    mask_c, hq_c = _hybrid_mask_h(ffn, w, cols=ccols)
+    bc = orc.ffn_backward(w.x, w.dy, w.w_gate_t[ccols], w.w_up_t[ccols], w.w_down[ccols], mask_c, hq_c, w.lam)
+    ci = torch.from_numpy(ccols).cuda()
+    rowwise_ok(f64(dwg[ci]), bc["dw_gate_t"], Y_TOL, "c5 (benchmark thresholds) dW_gate")
+    rowwise_ok(f64(dwu[ci]), bc["dw_up_t"], Y_TOL, "c5 (benchmark thresholds) dW_up")
+    rowwise_ok(f64(dwd[ci]), bc["dw_down"], Y_TOL, "c5 (benchmark thresholds) dW_down")
