@@ -444,11 +444,11 @@ hipError_t launch_overflow_rows(const FwdArgs& a, hipStream_t s) {
 // overflow partials; disjoint rows of y), so the overflow rows run on the side
 // stream beside the up / down launches.
 template <typename TS>
-hipError_t launch_t(const FwdArgs& a, hipStream_t s, int64_t chunk) {
+hipError_t launch_t(const FwdArgs& a, hipStream_t s, int64_t chunk, bool use_side = true) {
   hipStream_t side = s;
   hipError_t err = hipSuccess, err2 = hipSuccess;
   if (a.ovf_cap > 0) {
-    if ((err = fork_side(s, &side)) != hipSuccess) return err;
+    if (use_side && (err = fork_side(s, &side)) != hipSuccess) return err;
     err = launch_overflow_rows<TS>(a, side);
   }
   if (err == hipSuccess) err = launch_sparse_rows<TS>(a, s, chunk);
@@ -469,7 +469,12 @@ hipError_t launch_ffn_fwd(const FwdArgs& a, hipStream_t s) {
   return a.is_bf16 ? launch_t<uint16_t>(a, s, kTokenChunk) : launch_t<float>(a, s, kTokenChunk);
 }
 
-hipError_t launch_forward(const GateArgs& g, const FwdArgs& f, hipStream_t s) {
+hipError_t launch_forward(const GateArgs& g, const FwdArgs& f, hipStream_t s, bool use_side) {
+  if (!use_side) {  // everything in order on `s`
+    const hipError_t err = launch_gate_pack(g, s);
+    if (err != hipSuccess) return err;
+    return f.is_bf16 ? launch_t<uint16_t>(f, s, kTokenChunk, false) : launch_t<float>(f, s, kTokenChunk, false);
+  }
   if (gate_ovf_rows_heavy(g)) {  // the two calls' order: overflow list and gate rows on `s` first
     const hipError_t err = launch_gate_pack(g, s);
     return err != hipSuccess ? err : launch_ffn_fwd(f, s);

@@ -3,6 +3,7 @@
 #include <string>
 
 #include "twell_host.h"
+#include "twell_internal.h"
 #include "twell_kernels.h"
 
 namespace {
@@ -49,6 +50,12 @@ twell_status prepare(const twell_dims* dims, twell_dtype dtype, twell::Shape* s,
 }
 
 }  // namespace
+
+namespace twell {
+
+twell_status set_error(twell_status st, const char* why) { return fail(st, why); }
+
+}  // namespace twell
 
 extern "C" {
 
@@ -316,16 +323,8 @@ twell_status twell_ffn_forward(const twell_dims* dims, twell_dtype dtype, const 
                                const float* t, const twell_pack* pack, const void* w_up_t, const void* w_down,
                                float* y, float* a_save, void* ws, size_t ws_bytes, void* gate_ws,
                                size_t gate_ws_bytes, void* stream) {
-  twell::Shape s;
-  twell_sizes z;
-  twell::GateArgs g{};
-  twell_status st = gate_prepare(dims, dtype, x, w_gate_t, nullptr, false, t, pack, nullptr, gate_ws,
-                                 gate_ws_bytes, gate_ws != nullptr, &s, &z, &g);
-  if (st != TWELL_OK) return st;
-  twell::FwdArgs f{};
-  if ((st = fwd_prepare(s, z, dtype, pack, x, w_up_t, w_down, y, a_save, ws, ws_bytes, &f)) != TWELL_OK) return st;
-  if (s.N == 0) return TWELL_OK;
-  return hip_status(twell::launch_forward(g, f, (hipStream_t)stream), "twell_ffn_forward");
+  return twell::ffn_forward_call(dims, dtype, x, w_gate_t, t, pack, w_up_t, w_down, y, a_save, ws, ws_bytes, gate_ws,
+                                 gate_ws_bytes, true, false, stream);
 }
 
 static twell_status check_hybrid(const twell_hybrid* h, const twell_sizes& z) {
@@ -449,3 +448,23 @@ twell_status twell_ffn_bwd(const twell_dims* dims, twell_dtype dtype, const twel
 }
 
 }  // extern "C"
+
+namespace twell {
+
+twell_status ffn_forward_call(const twell_dims* dims, twell_dtype dtype, const void* x, const void* w_gate_t,
+                              const float* t, const twell_pack* pack, const void* w_up_t, const void* w_down,
+                              float* y, float* a_save, void* ws, size_t ws_bytes, void* gate_ws, size_t gate_ws_bytes,
+                              bool use_side, bool validate_only, void* stream) {
+  twell::Shape s;
+  twell_sizes z;
+  twell::GateArgs g{};
+  twell_status st = gate_prepare(dims, dtype, x, w_gate_t, nullptr, false, t, pack, nullptr, gate_ws,
+                                 gate_ws_bytes, gate_ws != nullptr, &s, &z, &g);
+  if (st != TWELL_OK) return st;
+  twell::FwdArgs f{};
+  if ((st = fwd_prepare(s, z, dtype, pack, x, w_up_t, w_down, y, a_save, ws, ws_bytes, &f)) != TWELL_OK) return st;
+  if (s.N == 0 || validate_only) return TWELL_OK;
+  return hip_status(twell::launch_forward(g, f, (hipStream_t)stream, use_side), "twell_ffn_forward");
+}
+
+}  // namespace twell

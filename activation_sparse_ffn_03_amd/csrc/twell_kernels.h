@@ -87,8 +87,10 @@ struct FwdArgs {
 hipError_t launch_ffn_fwd(const FwdArgs& a, hipStream_t s);
 // Gate + pack (g) followed by the up/down projection (f) in one call: the
 // overflow branch of both (list, dense rows, their up/down products) runs on
-// the side stream beside the up/down projection of the other rows.
-hipError_t launch_forward(const GateArgs& g, const FwdArgs& f, hipStream_t s);
+// the side stream beside the up/down projection of the other rows. With
+// `side` false everything is enqueued on `s` in order (no side stream is
+// created or used); the results are the same.
+hipError_t launch_forward(const GateArgs& g, const FwdArgs& f, hipStream_t s, bool side = true);
 
 // Side stream of the current device for the independent branch of a call
 // (side_stream.hip): fork_side makes it wait for the work enqueued on `main`

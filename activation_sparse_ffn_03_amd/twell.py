@@ -30,8 +30,11 @@ _STATUS = {0: "TWELL_OK", 1: "TWELL_ERR_INVALID_ARG", 2: "TWELL_ERR_UNSUPPORTED"
 EXPORTS = ("twell_status_str", "twell_last_error", "twell_n_tiles", "twell_query_sizes", "twell_gate_pack",
            "twell_gate_pack_ws", "twell_pack_preact", "twell_quantize_e4m3", "twell_gate_pack_fp8",
            "twell_gate_pack_fp8_ws", "twell_ffn_fwd", "twell_ffn_forward", "twell_ffn_forward_fp8",
-           "twell_route_hybrid", "twell_ffn_bwd", "twell_trace_start", "twell_trace_stop", "twell_trace_count",
-           "twell_trace_dropped", "twell_trace_get")
+           "twell_ffn_forward_noalloc", "twell_route_hybrid", "twell_ffn_bwd", "twell_trace_start",
+           "twell_trace_stop", "twell_trace_count", "twell_trace_dropped", "twell_trace_get")
+
+# Bytes of the library's static scratch used by twell_ffn_forward_noalloc.
+NOALLOC_SCRATCH_BYTES = 128 << 20
 
 
 class TwellError(RuntimeError):
@@ -104,6 +107,8 @@ def lib() -> ctypes.CDLL:
         L.twell_ffn_forward.argtypes = [pd, ctypes.c_int, vp, vp, vp, pp, vp, vp, vp, vp, vp, sz, vp, sz, vp]
         L.twell_ffn_forward_fp8.restype = ctypes.c_int
         L.twell_ffn_forward_fp8.argtypes = [pd, vp, vp, vp, vp, vp, pp, vp, vp, vp, vp, vp, vp, sz, vp, sz, vp]
+        L.twell_ffn_forward_noalloc.restype = ctypes.c_int
+        L.twell_ffn_forward_noalloc.argtypes = [pd, ctypes.c_int, vp, vp, vp, pp, vp, vp, vp, vp, vp]
         L.twell_route_hybrid.restype = ctypes.c_int
         L.twell_route_hybrid.argtypes = [pd, ctypes.c_int, pp, vp, ph, vp]
         L.twell_ffn_bwd.restype = ctypes.c_int
@@ -310,6 +315,17 @@ def ffn_forward_fp8(dims: Dims, x_q, x_scale, w_q, w_scale, t, pack: TwellPack, 
                                        ctypes.byref(p), _ptr(x), _ptr(w_up_t), _ptr(w_down), _ptr(y), _ptr(a_save),
                                        _ptr(ws), nbytes, _ptr(gate_ws), gbytes, _stream(stream)),
            "twell_ffn_forward_fp8")
+
+
+def ffn_forward_noalloc(dims: Dims, dtype: int, x, w_gate_t, t, pack: TwellPack, w_up_t, w_down, y, a_save=None,
+                        stream=None) -> None:
+    """ffn_forward with the library's static scratch as its workspaces
+    (twell_ffn_forward_noalloc): allocates nothing, everything in order on
+    the stream."""
+    p = pack.struct()
+    _check(lib().twell_ffn_forward_noalloc(ctypes.byref(dims), int(dtype), _ptr(x), _ptr(w_gate_t), _ptr(t),
+                                           ctypes.byref(p), _ptr(w_up_t), _ptr(w_down), _ptr(y), _ptr(a_save),
+                                           _stream(stream)), "twell_ffn_forward_noalloc")
 
 
 def route_hybrid(dims: Dims, dtype: int, pack: TwellPack, a_save, hyb: TwellHybrid, stream=None) -> None:

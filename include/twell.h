@@ -271,6 +271,33 @@ twell_status twell_ffn_forward_fp8(const twell_dims* dims, const uint8_t* x_q, c
                                    const void* x, const void* w_up_t, const void* w_down, float* y, float* a_save,
                                    void* ws, size_t ws_bytes, void* gate_ws, size_t gate_ws_bytes, void* stream);
 
+/* Size of the library's static device scratch used by
+ * twell_ffn_forward_noalloc (one copy per GPU, held until the process ends). */
+#define TWELL_NOALLOC_SCRATCH_BYTES (128u << 20)
+
+/* twell_ffn_forward for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments (minus the two workspaces), outputs and results as
+ * twell_ffn_forward (with gate_ws given whenever twell_sizes.ws_gate > 0);
+ * the workspaces are carved out of a static device array of
+ * TWELL_NOALLOC_SCRATCH_BYTES that the library owns, one per GPU. The call
+ * allocates nothing, frees nothing and creates no stream: every kernel is
+ * enqueued on `stream` in order (the overflow branch does not run beside the
+ * up / down projection). On a device's first call the array's device address
+ * is looked up (hipGetSymbolAddress) and kept.
+ * The scratch keeps the last call's contents; every call writes what it reads.
+ * Calls that overlap on one GPU (different streams, or different host
+ * threads, without ordering between them) share that GPU's scratch and race:
+ * the caller must order them.
+ * Errors as twell_ffn_forward, plus TWELL_ERR_WORKSPACE when the shape needs
+ * more than TWELL_NOALLOC_SCRATCH_BYTES of workspace
+ * (align256(twell_sizes.ws_fwd) + twell_sizes.ws_gate), checked on the host
+ * before anything is enqueued. */
+twell_status twell_ffn_forward_noalloc(const twell_dims* dims, twell_dtype dtype, const void* x,
+                                       const void* w_gate_t, const float* t, const twell_pack* pack,
+                                       const void* w_up_t, const void* w_down, float* y, float* a_save,
+                                       void* stream);
+
 /* Stage 3a: route every row to the row-ELL (width K = dims->row_cap >= 1) or to
  * the dense backup (rule at twell_hybrid). a_save is the array filled by
  * twell_ffn_fwd. Writes every field of *out. */

@@ -163,7 +163,7 @@ hipError_t launch_ffn_fwd(const FwdArgs& a, hipStream_t) {
   ++g_launches;
   return hipSuccess;
 }
-hipError_t launch_forward(const GateArgs& g, const FwdArgs& f, hipStream_t) {
+hipError_t launch_forward(const GateArgs& g, const FwdArgs& f, hipStream_t, bool) {
   gate_extents(g);
   fwd_extents(f);
   ++g_launches;
