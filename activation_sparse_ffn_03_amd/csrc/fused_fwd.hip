@@ -39,13 +39,6 @@ namespace {
 
 constexpr int kParts = 8;  // one part per XCD
 
-// Maximum of v over the 64 lanes of a wave (every lane gets it).
-__device__ __forceinline__ int wave_max_int(int v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = max(v, __shfl_xor(v, off, 64));
-  return v;
-}
-
 // Walk TwELL tiles [j0, j1) of token i (not an overflow row) and hand its
 // packed entries to `flush` in lists of at most 64: lane k of the list holds
 // entry k as (global column c, stored activation h, slot id j*S+s). The slot
@@ -277,15 +270,15 @@ __global__ __launch_bounds__(256) void ffn_down_kernel(FwdArgs a, int G8, int64_
 // Work item (o, g): overflow row o, columns [g*kDenseChunk, ...) of its dense
 // activation row; writes the partial y row part[o][g]. The active columns of
 // each 64-column block are handled in two batched passes: a for U columns at a
-// time (U W_up rows in flight), then y += z * W_down[c] likewise.
+// time (U W_up rows in flight), then y += z * W_down[c] likewise. The grid is
+// capped (kRowsGrid workgroups) and each wave strides over the work items of
+// the rows that really overflowed, so a step without overflow rows costs one
+// small launch whatever the capacity.
 template <typename TS, int M>
-__global__ __launch_bounds__(256) void ffn_dense_rows(FwdArgs a, int G) {
+__device__ __forceinline__ void dense_row_item(const FwdArgs& a, int G, int o, int g) {
   constexpr int E = ChunkElems<TS>::E;
   constexpr int U = M <= 4 ? 4 : (M == 8 ? 2 : 1);
   const int lane = threadIdx.x & 63;
-  const int64_t k = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int o = (int)(k / G), g = (int)(k % G);
-  if (o >= a.ovf_cap || o >= *a.n_ovf) return;
   const int D = a.D, nch = D / E;
   const TS* __restrict__ w_up = reinterpret_cast<const TS*>(a.w_up);
   const TS* __restrict__ w_down = reinterpret_cast<const TS*>(a.w_down);
@@ -338,19 +331,32 @@ __global__ __launch_bounds__(256) void ffn_dense_rows(FwdArgs a, int G) {
   store_row<TS, M>(a.part + ((size_t)o * G + g) * D, acc, nch, lane);
 }
 
-// y[ovf_rows[o]] = sum_g part[o][g]  (fixed chunk order)
+constexpr int kRowsGrid = 1024;
+
+template <typename TS, int M>
+__global__ __launch_bounds__(256) void ffn_dense_rows(FwdArgs a, int G) {
+  const int n_rows = min(a.ovf_cap, *a.n_ovf);
+  const int64_t items = (int64_t)n_rows * G;
+  for (int64_t k = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); k < items; k += (int64_t)gridDim.x * 4)
+    dense_row_item<TS, M>(a, G, (int)(k / G), (int)(k % G));
+}
+
+// y[ovf_rows[o]] = sum_g part[o][g]  (fixed chunk order); a capped grid
+// strides over the rows that really overflowed
 __global__ __launch_bounds__(256) void dense_reduce(const float* __restrict__ part, const int32_t* __restrict__ rows,
                                                     const int32_t* __restrict__ n_rows, int cap, int G, int D,
                                                     float* __restrict__ out) {
   const int db = (D + 255) / 256;
-  const int o = blockIdx.x / db;
-  if (o >= cap || o >= *n_rows) return;
-  const int d = (blockIdx.x % db) * 256 + threadIdx.x;
-  if (d >= D) return;
-  const float* p = part + (size_t)o * G * D + d;
-  float s = 0.f;
-  for (int g = 0; g < G; ++g) s += p[(size_t)g * D];
-  out[(size_t)rows[o] * D + d] = s;
+  const int64_t nb = (int64_t)min(cap, *n_rows) * db;
+  for (int64_t b = blockIdx.x; b < nb; b += gridDim.x) {
+    const int o = (int)(b / db);
+    const int d = (int)(b % db) * 256 + threadIdx.x;
+    if (d >= D) continue;
+    const float* p = part + (size_t)o * G * D + d;
+    float s = 0.f;
+    for (int g = 0; g < G; ++g) s += p[(size_t)g * D];
+    out[(size_t)rows[o] * D + d] = s;
+  }
 }
 
 // Budget of an XCD's slice of W_down (see pick_l2_slices). It is larger than
@@ -387,6 +393,10 @@ hipError_t launch_sparse_rows(const FwdArgs& a, hipStream_t s, int64_t chunk) {
     const int64_t tblocks = (i1 - i0 + 3) / 4;
     const dim3 gup((unsigned)(tblocks * parts * a.up_nq));
     const bool small = i1 - i0 <= kSmallRows;
+    if (sizeof(TS) == 2 && chunk == a.N && up_blocked_applies(a)) {
+      // large batches: token blocks x tile groups through LDS (up_blocked.hip)
+      if ((err = launch_up_blocked(a, s)) != hipSuccess) return err;
+    } else {
 #define TWELL_UP(MM)                                                                                          \
   case MM:                                                                                                    \
     if (small)                                                                                                \
@@ -403,6 +413,7 @@ hipError_t launch_sparse_rows(const FwdArgs& a, hipStream_t s, int64_t chunk) {
     if (a.up_nq > 1) {
       TWELL_LAUNCH("ffn_up_finish", ffn_up_finish, dim3((unsigned)tblocks), blk, 0, s, a, i0, i1);
       if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
     }
     const dim3 gdn((unsigned)(tblocks * P));
 #define TWELL_DOWN(E, R)                                                                                    \
@@ -426,7 +437,8 @@ template <typename TS>
 hipError_t launch_overflow_rows(const FwdArgs& a, hipStream_t s) {
   const int M = pick_m(a.D / ChunkElems<TS>::E);
   const int G = (a.F + kDenseChunk - 1) / kDenseChunk;
-  const dim3 gov((unsigned)(((int64_t)a.ovf_cap * G + 3) / 4)), blk(256);
+  const int64_t want = ((int64_t)a.ovf_cap * G + 3) / 4;
+  const dim3 gov((unsigned)(want < kRowsGrid ? want : kRowsGrid)), blk(256);
   switch (M) {
     case 1: TWELL_LAUNCH("ffn_dense_rows", (ffn_dense_rows<TS, 1>), gov, blk, 0, s, a, G); break;
     case 2: TWELL_LAUNCH("ffn_dense_rows", (ffn_dense_rows<TS, 2>), gov, blk, 0, s, a, G); break;
@@ -461,7 +473,9 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t s, int64_t chunk, bool use_sid
 hipError_t launch_dense_reduce(const float* part, const int32_t* rows, const int32_t* n_rows, int cap, int G,
                                int D, float* out, hipStream_t s) {
   if (cap == 0) return hipSuccess;
-  TWELL_LAUNCH("dense_reduce", dense_reduce, dim3((unsigned)(((D + 255) / 256) * (int64_t)cap)), 256, 0, s, part, rows, n_rows, cap, G, D, out);
+  const int64_t want = ((D + 255) / 256) * (int64_t)cap;
+  TWELL_LAUNCH("dense_reduce", dense_reduce, dim3((unsigned)(want < kRowsGrid ? want : kRowsGrid)), 256, 0, s, part,
+               rows, n_rows, cap, G, D, out);
   return hipGetLastError();
 }
 

@@ -72,9 +72,6 @@ struct Epi {
 
 __device__ __forceinline__ uint64_t mask_below(int n) { return n >= 64 ? ~0ull : ((1ull << n) - 1ull); }
 
-// Workgroup barrier that orders LDS accesses only (waits for this wave's
-// outstanding LDS operations, not for its global loads or stores).
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 __device__ __forceinline__ int dense_valid(const Epi& e) { return min(*e.n_ovf, e.cap); }
 
@@ -466,14 +463,6 @@ struct DmaCfg {
 // chosen by timing all 256 linear 2-bit keys of the row index).
 __device__ __forceinline__ int dma_swz(int r) { return ((r >> 3) & 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 1); }
 
-__device__ __forceinline__ void dma_16B(const void* g, uint32_t lds_byte) {
-  const uint32_t m = __builtin_amdgcn_readfirstlane(lds_byte);  // wave-uniform by construction
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m) : "memory");
-}
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
 
 // FP8: x and w hold E4M3 codes (one byte per element). A 64-byte stage row is
 // then 64 k, exactly the depth of gfx950's v_mfma_f32_32x32x64_f8f6f4, so each

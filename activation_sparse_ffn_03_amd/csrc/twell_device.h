@@ -62,10 +62,34 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
 
 __device__ __forceinline__ int wave_lane() { return threadIdx.x & (kWave - 1); }
 
+// Maximum of v over the 64 lanes of a wave (every lane gets it).
+__device__ __forceinline__ int wave_max_int(int v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = max(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 
 __device__ __forceinline__ uint32_t lanemask_lt_popc(uint64_t m, int lane) {
   return __popcll(m & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
+}
+
+// Workgroup barrier that orders LDS accesses only (waits for this wave's
+// outstanding LDS operations, not for its global loads or stores).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// 16 bytes per lane from global memory straight into LDS
+// (global_load_lds_dwordx4): lane l's bytes land at lds_byte + 16 * l, where
+// lds_byte is the wave's base address (wave-uniform by construction).
+__device__ __forceinline__ void dma_16B(const void* g, uint32_t lds_byte) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane(lds_byte);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m) : "memory");
+}
+// Wait until at most N of this wave's vector memory operations are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 // Storage types: raw bf16 bits or fp32.

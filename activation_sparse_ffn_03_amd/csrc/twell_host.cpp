@@ -103,7 +103,9 @@ FwdLayout fwd_layout(const Shape& s) {
   L.upart = L.zlist + align_up(entries * 8);
   L.uslot = L.upart + (nq > 1 ? align_up((size_t)nq * entries * 4) : 0);
   L.part = L.uslot + (nq > 1 ? align_up(entries * 4) : 0);
-  L.total = L.part + (size_t)s.ovf_cap * s.G * s.D * 4;
+  L.gbase = L.part + align_up((size_t)s.ovf_cap * s.G * s.D * 4);
+  const size_t groups = (size_t)(s.n_tiles + kUpGroupTiles - 1) / kUpGroupTiles;
+  L.total = L.gbase + groups * (size_t)s.N * 4;
   return L;
 }
 

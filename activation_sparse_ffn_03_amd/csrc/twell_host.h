@@ -13,6 +13,8 @@
 namespace twell {
 
 constexpr size_t kWsAlign = 256;
+// TwELL tiles per column group of the blocked up projection (up_blocked.hip).
+constexpr int kUpGroupTiles = 4;
 
 struct Shape {
   int64_t N;
@@ -43,9 +45,10 @@ int up_passes(const Shape& s);
 // row-major (column, z) list ([N][n_t*S] x 8 bytes), and only when
 // up_passes > 1 the passes' partial dot products ([up_passes][N][n_t*S] fp32)
 // and the slot of every list entry ([N][n_t*S] int32); then the dense-row
-// partials.
+// partials; then the list position of each kUpGroupTiles-tile group's first
+// entry ([ceil(n_t / kUpGroupTiles)][N] int32).
 struct FwdLayout {
-  size_t offs, zlist, upart, uslot, part, total;
+  size_t offs, zlist, upart, uslot, part, gbase, total;
 };
 FwdLayout fwd_layout(const Shape& s);
 size_t fwd_ws_bytes(const Shape& s);

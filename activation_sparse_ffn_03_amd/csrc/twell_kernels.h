@@ -82,9 +82,14 @@ struct FwdArgs {
   int32_t* uslot; // [N][n_t*S]: slot of each list entry, for a_save (workspace, up_nq > 1)
   int up_nq;      // passes of the up projection over d_model (up_passes)
   float* part;    // [ovf_cap][G][D] fp32 partial outputs of dense-row chunks (workspace)
+  int32_t* gbase; // [ceil(n_t / kUpGroupTiles)][N]: list position of each tile group's first entry (workspace)
 };
 
 hipError_t launch_ffn_fwd(const FwdArgs& a, hipStream_t s);
+// Up projection of large bf16 batches with weight-row reuse through LDS
+// (up_blocked.hip): list lengths and group positions, then z and a_save.
+bool up_blocked_applies(const FwdArgs& a);
+hipError_t launch_up_blocked(const FwdArgs& a, hipStream_t s);
 // Gate + pack (g) followed by the up/down projection (f) in one call: the
 // overflow branch of both (list, dense rows, their up/down products) runs on
 // the side stream beside the up/down projection of the other rows. With

@@ -18,6 +18,7 @@
 #include <vector>
 
 #include "twell.h"
+#include "twell_host.h"
 #include "twell_kernels.h"
 
 namespace {
@@ -125,6 +126,7 @@ static void fwd_extents(const FwdArgs& a) {
   extent(a.y, N * D * 4, "y");
   if (a.a_save) extent(a.a_save, nt * S * N * 4, "a_save");
   extent(a.offs, N * 4, "ws.offs");
+  extent(a.gbase, (nt + kUpGroupTiles - 1) / kUpGroupTiles * N * 4, "ws.gbase");
   extent(a.zlist, N * L * 8, "ws.zlist");
   CHECK(a.up_nq >= 1 && D % (size_t)a.up_nq == 0, "up_nq %d does not divide d_model", a.up_nq);
   if (a.up_nq > 1) {
