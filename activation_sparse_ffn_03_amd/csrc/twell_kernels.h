@@ -97,10 +97,11 @@ hipError_t launch_up_blocked(const FwdArgs& a, hipStream_t s);
 // created or used); the results are the same.
 hipError_t launch_forward(const GateArgs& g, const FwdArgs& f, hipStream_t s, bool side = true);
 
-// Side stream of the current device for the independent branch of a call
-// (side_stream.hip): fork_side makes it wait for the work enqueued on `main`
-// and returns it (or `main` itself when no side stream could be created);
-// join_side makes `main` wait for the work enqueued on it.
+// Side stream of the caller's stream (one per caller stream and device,
+// side_stream.hip) for the independent branch of a call: fork_side makes it
+// wait for the work enqueued on `main` and returns it (or `main` itself when
+// there is none: a capture in progress, too many caller streams, or a
+// creation failure); join_side makes `main` wait for the work enqueued on it.
 hipError_t fork_side(hipStream_t main, hipStream_t* side);
 hipError_t join_side(hipStream_t main, hipStream_t side);
 

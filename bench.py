@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, published
 MFMA_FP8_PEAK_TFS = 5000.0   # MI355X dense fp8 MFMA, published
+VALU_FP32_PEAK_TFS = 157.3   # MI355X fp32 vector, published
 METRIC = "sparse FFN tokens/s and speedup vs dense bf16 FFN; HBM GB/s / MFMA % of peak"
 
 WORKLOADS = {
@@ -112,7 +113,7 @@ def kernel_work(name, w, st, train):
     if name == "pack_from_g":      # g read, TwELL written
         twell = n_t * w.slots * N * (e + 2) + n_t * N * 2
         return {"flops": 0.0, "bytes": N * F * 4 + twell, "bound": "hbm"}
-    if name == "ffn_up_kernel":   # x, W_up once; TwELL read; z (and a when training) written
+    if name in ("ffn_up_kernel", "ffn_up_blocked"):  # x, W_up once; TwELL read; z (and a when training) written
         byt = N * D * e + F * D * e + nnz * (e + 2) + n_t * N * 2 + nnz * 4 + (nnz * 4 if train else 0)
         return {"flops": 2.0 * D * nnz, "bytes": byt, "bound": "hbm", "gathered": nnz * D * e}
     if name == "ffn_down_kernel":  # W_down once; cols + z read; y written (fp32)
@@ -244,6 +245,7 @@ KERNEL_SOURCES = {
     "pack_from_g": ["gate_pack.hip", "twell_device.h"],
     "quantize_e4m3": ["quant.hip", "twell_device.h"],
     "ffn_up_kernel": ["fused_fwd.hip", "row_ops.h", "twell_device.h"],
+    "ffn_up_blocked": ["up_blocked.hip", "row_ops.h", "twell_device.h"],
     "ffn_down_kernel": ["fused_fwd.hip", "row_ops.h", "twell_device.h"],
     "bwd_dz_ell": ["bwd.hip", "row_ops.h", "twell_device.h"],
     "bwd_dx": ["bwd.hip", "row_ops.h", "twell_device.h"],
@@ -351,6 +353,22 @@ def main():
             return y, dx, dwd, dwu, dwg
         return y
 
+    # the dense baseline's matrix products alone (hipBLASLt through torch),
+    # without its elementwise work: the bar a fused dense kernel would face
+    h_dense = torch.randn((w.N, w.F), device=dev, dtype=torch.bfloat16) if not args.no_dense else None
+
+    def dense_gemms():
+        torch.nn.functional.linear(x, wg)
+        torch.nn.functional.linear(x, wu)
+        torch.mm(h_dense, wd)
+        if train:
+            torch.nn.functional.linear(dy, wd)
+            torch.mm(h_dense.t(), dy)
+            torch.mm(h_dense, wu)
+            torch.mm(h_dense, wg)
+            torch.mm(h_dense.t(), x)
+            torch.mm(h_dense.t(), x)
+
     if args.traffic_pass:
         # counter runs: warmup + steps of one path only, nothing timed
         fn = step if args.traffic_pass == "sparse" else dense_step
@@ -437,6 +455,16 @@ def main():
         s_k = kernels[k]["avg_ms"] / 1e3
         kernels[k]["GBps_algorithmic"] = wk_k["bytes"] / s_k / 1e9
         kernels[k]["TFLOPs"] = wk_k["flops"] / s_k / 1e12
+        # the kernel's floor at spec peaks: MFMA (its dtype), or the larger of
+        # HBM (algorithmic bytes at 8 TB/s) and VALU (flops at 157.3 TFLOP/s);
+        # frac_of_floor = floor / measured time
+        if wk_k["bound"] == "mfma":
+            peak = MFMA_FP8_PEAK_TFS if wk_k.get("peak") == "fp8" else MFMA_BF16_PEAK_TFS
+            floor_s = wk_k["flops"] / (peak * 1e12)
+        else:
+            floor_s = max(wk_k["bytes"] / (HBM_PEAK_GBS * 1e9), wk_k["flops"] / (VALU_FP32_PEAK_TFS * 1e12))
+        kernels[k]["floor_ms"] = floor_s * 1e3
+        kernels[k]["frac_of_floor"] = floor_s / s_k
         if "gathered" in wk_k:   # weight (or token) rows delivered per active entry, mostly from L2
             kernels[k]["gather_TBps"] = wk_k["gathered"] / s_k / 1e12
 
@@ -466,6 +494,19 @@ def main():
             torch.cuda.synchronize()
             dense_graph_ms = d0.elapsed_time(d1) / args.steps
             del dgraph
+
+    dense_gemm_ms = None
+    if not args.no_dense:
+        for _ in range(args.warmup):
+            dense_gemms()
+        torch.cuda.synchronize()
+        m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        m0.record(stream)
+        for _ in range(args.steps):
+            dense_gemms()
+        m1.record(stream)
+        torch.cuda.synchronize()
+        dense_gemm_ms = m0.elapsed_time(m1) / args.steps
 
     # per-step times (each step bracketed by its own events): warm caches, and
     # cold ones (a 512 MB write between steps evicts the 4 MB L2s and the 256 MB
@@ -524,6 +565,8 @@ def main():
         "graph_ms_per_step": graph_ms,
         "dense_graph_ms_per_step": dense_graph_ms,
         "speedup_vs_dense": (dense / ms) if dense else None,
+        "dense_gemm_only_ms_per_step": dense_gemm_ms,
+        "speedup_vs_dense_gemm_only": (dense_gemm_ms / ms) if dense_gemm_ms else None,
         "dense_bf16_ms_per_step": dense,
         "step_ms": step_ms,
         "dense_step_ms": dense_step_ms,

@@ -248,10 +248,15 @@ twell_status twell_ffn_fwd(const twell_dims* dims, twell_dtype dtype, const twel
  * TwELL pack, the overflow list and rows in *pack, y, and a_save when given.
  * Within one call the overflow branch (the ascending overflow list, the
  * overflow rows' dense activations and their up / down products) is
- * enqueued on a second stream of the library beside the up / down
- * projection of the other rows, which reads only the pack and the overflow
- * flags, and is joined back before the call returns; the two separate calls
- * must each finish their part before returning. No g_dump.
+ * enqueued on a side stream beside the up / down projection of the other
+ * rows, which reads only the pack and the overflow flags, and is joined back
+ * into `stream` before the call returns; the two separate calls must each
+ * finish their part before returning. The library keeps one side stream (and
+ * one pair of events) per caller stream and device, created on that caller
+ * stream's first call and kept until the process ends (at most 16 per
+ * device); a caller stream that is being captured into a graph before it has
+ * one, or one beyond that limit, gets the branch in order on `stream`
+ * instead, with the same results. No g_dump.
  * x, w_gate_t, w_up_t, w_down: as in the two calls; ws: the forward
  * workspace (twell_sizes.ws_fwd bytes); gate_ws: the small-batch gate
  * workspace (twell_sizes.ws_gate bytes) or NULL. Validation covers every

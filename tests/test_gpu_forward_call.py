@@ -122,3 +122,36 @@ def test_combined_fp8_call_matches_separate_calls(name, kw, slots):
     _same(a.pack.vals.view(-1, S, N)[used], b.pack.vals.view(-1, S, N)[used], "vals")
     _same(a.pack.cols.view(-1, S, N)[used], b.pack.cols.view(-1, S, N)[used], "cols")
     _same(a.y, b.y, "y")
+
+
+def test_forward_on_two_caller_streams():
+    """Two forwards with overflow rows enqueued back to back on two caller
+    streams (each with its own side stream), no host synchronisation between
+    them: both equal the same forward run alone, bit for bit."""
+    require_gpu()
+    from gpu_util import dev
+    w1 = make_inputs("c4", seed=31, N=300, D=1024, F=2000, slots=4)
+    w2 = make_inputs("c4", seed=32, N=300, D=1024, F=2000, slots=4)
+    dims = tw.make_dims(300, 1024, 2000, 128, 4, 0, 300, 0)
+
+    def up(w):
+        return tuple(dev(a, "bf16") for a in (w.x, w.w_gate_t, w.w_up_t, w.w_down)) + (torch.from_numpy(w.t).cuda(),)
+
+    a1, a2 = up(w1), up(w2)
+    ref = []
+    for args in (a1, a2):
+        f = tw.TwellFFN(dims, tw.BF16)
+        ref.append(f.forward(*args[:4], args[4]).clone())
+        torch.cuda.synchronize()
+        assert int(f.pack.n_ovf.item()) > 0
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    f1, f2 = tw.TwellFFN(dims, tw.BF16), tw.TwellFFN(dims, tw.BF16)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            f1.forward(*a1[:4], a1[4])
+        with torch.cuda.stream(s2):
+            f2.forward(*a2[:4], a2[4])
+    torch.cuda.synchronize()
+    assert torch.equal(f1.y.view(torch.int32), ref[0].view(torch.int32))
+    assert torch.equal(f2.y.view(torch.int32), ref[1].view(torch.int32))
