@@ -26,10 +26,12 @@
 //                    [p*D/P, (p+1)*D/P). One wave per token: its (c, z) list,
 //                    the slice of each W_down row, y slice in registers.
 //
-// Overflow rows (a tile count above S) are skipped by both: their dense
-// activation row is split into column chunks of kDenseChunk, each chunk a
-// work item of its own wave writing a partial y row (ffn_dense_rows), and
-// dense_reduce adds the partials in chunk order (deterministic, no atomics).
+// Overflow rows (a tile count above S) are skipped by both. In bf16 layers
+// (d_model a multiple of 128) all of them go through two skinny MFMA products
+// (dense_rows.hip). Otherwise each dense activation row is split into column
+// chunks of kDenseChunk, each chunk a work item of its own wave writing a
+// partial y row (ffn_dense_rows). Either way dense_reduce adds the chunk
+// partials in chunk order (deterministic, no atomics).
 #include "row_ops.h"
 #include "twell_kernels.h"
 #include "twell_trace.h"
@@ -435,6 +437,7 @@ hipError_t launch_sparse_rows(const FwdArgs& a, hipStream_t s, int64_t chunk) {
 // Overflow rows: dense chunks + fixed-order reduction into y.
 template <typename TS>
 hipError_t launch_overflow_rows(const FwdArgs& a, hipStream_t s) {
+  if (sizeof(TS) == 2 && dense_mfma_applies(a)) return launch_dense_mfma(a, s);
   const int M = pick_m(a.D / ChunkElems<TS>::E);
   const int G = (a.F + kDenseChunk - 1) / kDenseChunk;
   const int64_t want = ((int64_t)a.ovf_cap * G + 3) / 4;

@@ -284,6 +284,7 @@ static twell_status fwd_prepare(const twell::Shape& s, const twell_sizes& z, twe
     a.uslot = reinterpret_cast<int32_t*>(base + L.uslot);
     a.up_nq = twell::up_passes(s);
     a.part = reinterpret_cast<float*>(base + L.part);
+    a.zov = reinterpret_cast<uint16_t*>(base + L.zov);
     a.gbase = reinterpret_cast<int32_t*>(base + L.gbase);
   }
   *out = a;

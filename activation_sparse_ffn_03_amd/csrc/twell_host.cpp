@@ -103,7 +103,8 @@ FwdLayout fwd_layout(const Shape& s) {
   L.upart = L.zlist + align_up(entries * 8);
   L.uslot = L.upart + (nq > 1 ? align_up((size_t)nq * entries * 4) : 0);
   L.part = L.uslot + (nq > 1 ? align_up(entries * 4) : 0);
-  L.gbase = L.part + align_up((size_t)s.ovf_cap * s.G * s.D * 4);
+  L.zov = L.part + align_up((size_t)s.ovf_cap * s.G * s.D * 4);
+  L.gbase = L.zov + (s.esz == 2 ? align_up((size_t)2 * s.ovf_cap * dense_z_stride(s.F) * 2) : 0);
   const size_t groups = (size_t)(s.n_tiles + kUpGroupTiles - 1) / kUpGroupTiles;
   L.total = L.gbase + groups * (size_t)s.N * 4;
   return L;

@@ -45,11 +45,16 @@ int up_passes(const Shape& s);
 // row-major (column, z) list ([N][n_t*S] x 8 bytes), and only when
 // up_passes > 1 the passes' partial dot products ([up_passes][N][n_t*S] fp32)
 // and the slot of every list entry ([N][n_t*S] int32); then the dense-row
-// partials; then the list position of each kUpGroupTiles-tile group's first
-// entry ([ceil(n_t / kUpGroupTiles)][N] int32).
+// partials; then, for bf16 storage, the overflow rows' z = h*a as bf16 high
+// and low parts ([2][ovf_cap][dense_z_stride(F)] uint16); then the list
+// position of each kUpGroupTiles-tile group's first entry
+// ([ceil(n_t / kUpGroupTiles)][N] int32).
 struct FwdLayout {
-  size_t offs, zlist, upart, uslot, part, gbase, total;
+  size_t offs, zlist, upart, uslot, part, zov, gbase, total;
 };
+// Row stride (elements) of the overflow rows' z: d_ff rounded up to 32, so
+// every 32-column block of a row lies inside it and rows stay 64-byte aligned.
+inline int dense_z_stride(int F) { return (F + 31) / 32 * 32; }
 FwdLayout fwd_layout(const Shape& s);
 size_t fwd_ws_bytes(const Shape& s);
 

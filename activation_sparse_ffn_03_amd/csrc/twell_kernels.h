@@ -82,6 +82,7 @@ struct FwdArgs {
   int32_t* uslot; // [N][n_t*S]: slot of each list entry, for a_save (workspace, up_nq > 1)
   int up_nq;      // passes of the up projection over d_model (up_passes)
   float* part;    // [ovf_cap][G][D] fp32 partial outputs of dense-row chunks (workspace)
+  uint16_t* zov;  // bf16: [2][ovf_cap][dense_z_stride(F)] high / low bf16 parts of the overflow rows' z (workspace)
   int32_t* gbase; // [ceil(n_t / kUpGroupTiles)][N]: list position of each tile group's first entry (workspace)
 };
 
@@ -90,6 +91,10 @@ hipError_t launch_ffn_fwd(const FwdArgs& a, hipStream_t s);
 // (up_blocked.hip): list lengths and group positions, then z and a_save.
 bool up_blocked_applies(const FwdArgs& a);
 hipError_t launch_up_blocked(const FwdArgs& a, hipStream_t s);
+// Overflow rows of bf16 layers as two skinny MFMA products (dense_rows.hip):
+// z = h * (X_o . W_up^T), then z . W_down in d_ff chunks and dense_reduce.
+bool dense_mfma_applies(const FwdArgs& a);
+hipError_t launch_dense_mfma(const FwdArgs& a, hipStream_t s);
 // Gate + pack (g) followed by the up/down projection (f) in one call: the
 // overflow branch of both (list, dense rows, their up/down products) runs on
 // the side stream beside the up/down projection of the other rows. With

@@ -234,8 +234,9 @@ twell_status twell_gate_pack_fp8_ws(const twell_dims* dims, const uint8_t* x_q, 
  * the (column, z = h·a) pair of every packed entry in row-major order (the
  * sparse intermediate between the up and the down projection, never a dense
  * hidden state), for large d_model x d_ff the partial a of every entry over
- * each of a few d_model ranges, and the partial rows of the overflow-row
- * chunks. */
+ * each of a few d_model ranges, the partial rows of the overflow-row
+ * chunks, for bf16 the overflow rows' z = h·a (as bf16 high and low parts),
+ * and the list position of each group of tiles' first entry per row. */
 twell_status twell_ffn_fwd(const twell_dims* dims, twell_dtype dtype, const twell_pack* pack,
                            const void* x, const void* w_up_t, const void* w_down, float* y,
                            float* a_save, void* ws, size_t ws_bytes, void* stream);

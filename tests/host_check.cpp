@@ -139,6 +139,7 @@ static void fwd_extents(const FwdArgs& a) {
     extent(a.ovf_h, (size_t)a.ovf_cap * F * esz, "ovf_h");
     extent(a.n_ovf, 4, "n_ovf");
     extent(a.part, (size_t)a.ovf_cap * G * D * 4, "ws.part");
+    if (a.is_bf16) extent(a.zov, (size_t)2 * a.ovf_cap * dense_z_stride(a.F) * 2, "ws.zov");
   }
 }
 

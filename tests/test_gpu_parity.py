@@ -171,6 +171,8 @@ def test_ovf_rows_match_epilogue_values():
     ("c2", dict(N=130, D=128, F=200), dict(tile_n=16, slots=3)),
     ("c2", dict(N=64, D=64, F=128), dict(slots=0, ovf_cap=64)),  # every non-empty row is dense
     ("c2", dict(N=96, D=128, F=300, density=0.75), dict(slots=128)),  # more than 64 slots in use per tile
+    ("c4", dict(N=520, D=384, F=1100), dict(slots=2, ovf_cap=520)),  # hundreds of overflow rows: MFMA
+                                                          # passes of 64 rows, ragged last d_ff chunk
     ("c2", dict(N=300, D=2048, F=8448), {}),             # W_up block per XCD > 4 MB: two d_model passes
     ("c1", dict(N=200, D=1024, F=8448), {}),             # the same in fp32
 ])
