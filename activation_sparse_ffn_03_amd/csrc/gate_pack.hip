@@ -29,7 +29,10 @@
 //   ovf_flags        overflow flag of every row from its true tile counts
 //                    (the ascending list is built by launch_compact).
 // The same kernels, with MODE_DENSE, recompute the dense activation rows of
-// the overflow rows with identical arithmetic (gathered A rows).
+// the overflow rows with identical arithmetic (gathered A rows); for bf16
+// operands with d_model a multiple of 32 that is gate_rows_skinny
+// (dense_rows.hip) instead, a wave per 16 columns over all of d_model with the
+// same chain of MFMAs per output.
 #include "../../include/twell.h"
 #include "twell_device.h"
 #include "twell_kernels.h"
@@ -933,7 +936,7 @@ __global__ __launch_bounds__(64) void ovf_flags(const uint16_t* __restrict__ cou
 
 bool gate_ovf_rows_heavy(const GateArgs& a) {
   const bool small = a.g_in == nullptr && a.is_bf16 && a.N <= kSmallN && a.g_ws != nullptr;
-  return a.is_bf16 && !a.fp8 && a.g_in == nullptr && !small && a.D > 2048;
+  return a.is_bf16 && !a.fp8 && a.g_in == nullptr && !small && a.D > 2048 && !gate_rows_skinny_applies(a.D);
 }
 
 hipError_t launch_gate_pack(const GateArgs& a, hipStream_t s) {
@@ -1017,18 +1020,19 @@ hipError_t launch_gate_pack_split(const GateArgs& a, hipStream_t s, bool fork, h
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || no_ovf) return err;
 
-  // 2. overflow rows from the true counts: the flags, the list and the dense
-  // rows on `so` (the side stream when asked to fork: the up / down
-  // projection takes the overflow test from the counts itself)
+  // 2. overflow rows from the true counts: the flags and the list on `s`
+  // (two short launches; on a side stream they would wait for CUs behind the
+  // up projection, which holds all of a CU's LDS), then the dense rows on `so`
+  // (the side stream when asked to fork)
+  TWELL_LAUNCH("ovf_flags", ovf_flags, dim3((a.N + 63) / 64), 64, 0, s, a.counts, a.N, a.n_tiles, a.slots,
+               a.ovf_flag);
+  err = launch_compact(a.ovf_flag, a.N, a.ovf_rows, a.ovf_cap, a.n_ovf, a.status, 1u /*TWELL_DEV_OVF_CAPACITY*/, s);
+  if (err != hipSuccess || a.ovf_cap == 0) return err;
   hipStream_t so = s;
   if (fork) {
     if ((err = fork_side(s, &so)) != hipSuccess) return err;
     *ovf_stream = so;
   }
-  TWELL_LAUNCH("ovf_flags", ovf_flags, dim3((a.N + 63) / 64), 64, 0, so, a.counts, a.N, a.n_tiles, a.slots,
-               a.ovf_flag);
-  err = launch_compact(a.ovf_flag, a.N, a.ovf_rows, a.ovf_cap, a.n_ovf, a.status, 1u /*TWELL_DEV_OVF_CAPACITY*/, so);
-  if (err != hipSuccess || a.ovf_cap == 0) return err;
 
   // 3. dense activation rows of the overflow rows, same arithmetic as step 1
   e.mode = MODE_DENSE;
@@ -1044,6 +1048,9 @@ hipError_t launch_gate_pack_split(const GateArgs& a, hipStream_t s, bool fork, h
       TWELL_LAUNCH("pack_from_g_rows", (pack_from_g<uint16_t, MODE_DENSE>), dim3(mb * ncb), 256, 0, so, g_in, ncb, e);
     else
       TWELL_LAUNCH("pack_from_g_rows", (pack_from_g<float, MODE_DENSE>), dim3(mb * ncb), 256, 0, so, g_in, ncb, e);
+  } else if (a.is_bf16 && gate_rows_skinny_applies(a.D)) {
+    return launch_gate_rows_skinny((const uint16_t*)a.x, (const uint16_t*)a.w, a.D, a.F, a.ovf_rows, a.n_ovf,
+                                   a.ovf_cap, a.t, (uint16_t*)a.ovf_h, so);
   } else if (a.is_bf16) {
     auto rows = [&](auto cfg) {
       using R = decltype(cfg);

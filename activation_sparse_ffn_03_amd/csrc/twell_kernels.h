@@ -44,15 +44,16 @@ struct GateArgs {
 };
 
 hipError_t launch_gate_pack(const GateArgs& a, hipStream_t s);
-// The same launches, with the overflow list and the overflow rows' dense
-// activations enqueued on the side stream when `fork` is set (the pack and
-// the flags stay on `s`). *ovf_stream is the stream that ends the overflow
-// branch: `s` when nothing was forked (no overflow steps, or fork unset),
-// else the side stream, which the caller must join back into `s`.
+// The same launches, with the overflow rows' dense activations enqueued on
+// the side stream when `fork` is set (the pack, the flags and the overflow
+// list stay on `s`). *ovf_stream is the stream that ends the overflow branch:
+// `s` when nothing was forked (no overflow steps, or fork unset), else the
+// side stream, which the caller must join back into `s`.
 hipError_t launch_gate_pack_split(const GateArgs& a, hipStream_t s, bool fork, hipStream_t* ovf_stream);
 // True when the overflow rows' gate rows take the 128x128 register-staged
-// GEMM (bf16, d_model > 2048, large batch): a long launch that, run beside
-// the up projection, costs it more occupancy than it saves.
+// GEMM (bf16, d_model > 2048 and not a multiple of 32, large batch): a long
+// launch that, run beside the up projection, costs it more occupancy than it
+// saves.
 bool gate_ovf_rows_heavy(const GateArgs& a);
 
 // Per-row E4M3 quantisation: q [rows][cols] codes, scale [rows] (quant.hip).
@@ -95,6 +96,11 @@ hipError_t launch_up_blocked(const FwdArgs& a, hipStream_t s);
 // z = h * (X_o . W_up^T), then z . W_down in d_ff chunks and dense_reduce.
 bool dense_mfma_applies(const FwdArgs& a);
 hipError_t launch_dense_mfma(const FwdArgs& a, hipStream_t s);
+// The overflow rows' dense activations h = Q(ReLU(g - t)) (bf16 gate), one
+// wave per 16 columns over all of d_model, g bit-identical to the gate GEMM's.
+bool gate_rows_skinny_applies(int D);
+hipError_t launch_gate_rows_skinny(const uint16_t* x, const uint16_t* w, int D, int F, const int32_t* rows,
+                                   const int32_t* n_ovf, int cap, const float* t, uint16_t* ovf_h, hipStream_t s);
 // Gate + pack (g) followed by the up/down projection (f) in one call: the
 // overflow branch of both (list, dense rows, their up/down products) runs on
 // the side stream beside the up/down projection of the other rows. With
