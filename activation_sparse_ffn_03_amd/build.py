@@ -27,7 +27,7 @@ HIP_FLAGS = [
     "-I", INCLUDE, "-I", CSRC,
 ]
 SOURCES = ["twell_host.cpp", "twell_api.hip", "trace.hip", "side_stream.hip", "scan.hip", "gate_pack.hip",
-           "quant.hip", "fused_fwd.hip", "up_blocked.hip", "route.hip", "bwd.hip", "noalloc.hip", "dense_rows.hip"]
+           "quant.hip", "fused_fwd.hip", "up_blocked.hip", "route.hip", "bwd.hip", "noalloc.hip", "dense_rows.hip", "bwd_blocked.hip", "bwd_dense.hip"]
 
 
 def _hipcc() -> str:

@@ -14,10 +14,14 @@
 // Pipeline (all deterministic, no floating-point atomics):
 //   dense_groups  per dense row: active count per column chunk -> offsets
 //   row_scan      CSR offsets of every row's entries (one workgroup)
-//   bwd_rows      wave per ELL row / per dense-row chunk: dz, da, dg, z and the
-//                 dx row (dense rows recompute a = x_i . W_up^T[c]); writes
-//                 each entry's column and (z, da, dg) in CSR order
-//   dense_reduce  dx of dense rows = sum of the chunk partials
+//   bwd_dz_ell    wave per ELL row and column part: dz, da, dg, z; writes
+//                 each entry's column and (z, da, dg) in CSR order (bf16
+//                 batches take the blocked form of bwd_blocked.hip instead)
+//   bwd_dz_dense  wave per dense-row chunk: the same, recomputing
+//                 a = x_i . W_up^T[c] for dense rows (bf16 layers with d_model
+//                 a multiple of 128 take the skinny MFMA products of
+//                 bwd_dense.hip instead, which also give those rows' dx)
+//   bwd_dx        wave per row: dx from the records
 //   csc_*         stable counting sort of the entries by column (row blocks
 //                 processed row by row, so each column lists rows ascending)
 //   bwd_dw        wave per (column, D-part): the three weight-gradient rows
@@ -255,8 +259,8 @@ __device__ __forceinline__ float entry_f(float v, int k) {
   else return __shfl(v, k, 64);
 }
 
-// Every row (ELL and dense-backup alike): its records are contiguous in CSR
-// order. Part p owns a d_model slice of dx (pick_l2_slices; slices go G8 at a
+// Every row (ELL and dense-backup alike, except dense rows whose dx the MFMA
+// path of bwd_dense.hip computes): its records are contiguous in CSR order. Part p owns a d_model slice of dx (pick_l2_slices; slices go G8 at a
 // time, slice_block), so each XCD gathers only a slice of the weight that
 // fits its L2, 16 bytes per lane. Two launches, one weight each:
 //   GATE = false:  dx_i[slice]  = sum over records da * W_up^T[c][slice]
@@ -272,6 +276,10 @@ __global__ __launch_bounds__(256) void bwd_dx(BwdArgs a, int G8, int64_t rblocks
   slice_block(blockIdx.x, G8, rblocks, p, rb);
   const int64_t i = rb * 4 + (threadIdx.x >> 6);
   if (i >= a.N) return;
+  if (a.ws.dxpart != nullptr) {  // dense rows inside the capacity: dx from the MFMA path
+    const int dp = a.ws.dense_pos[i];
+    if (dp >= 0 && dp < min(*a.n_dense, a.dense_cap)) return;
+  }
   const int D = a.D;
   const int d0 = p * (LPR * EPL) + (lane % LPR) * EPL;
   const TS* __restrict__ wt = reinterpret_cast<const TS*>(GATE ? a.w_gate : a.w_up) + d0;
@@ -493,6 +501,30 @@ hipError_t launch_dx(const BwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Weight gradients: column-owned, d_model in 1/8 slices (slicing x / dy
+// further to fit L2 measured slower here: a column's tokens ascend, so its
+// gathers already fall close together).
+template <typename TS>
+hipError_t launch_dw(const BwdArgs& a, hipStream_t s) {
+  const dim3 blk(256);
+  const SliceGeom geom = pick_slices(a.D, (int)sizeof(TS));
+  const int P = geom.P, G8 = slice_group(P);
+  const int64_t cblocks = (a.F + 3) / 4;
+  const dim3 gdw((unsigned)(cblocks * P));
+#define TWELL_DWD(E, R) TWELL_LAUNCH("bwd_dw_down", (bwd_dw<TS, E, R, false>), gdw, blk, 0, s, a, G8, cblocks)
+#define TWELL_DW(E, R) TWELL_LAUNCH("bwd_dw", (bwd_dw<TS, E, R, true>), gdw, blk, 0, s, a, G8, cblocks)
+  if constexpr (sizeof(TS) == 2) {
+    TWELL_SLICED_CASES(8, TWELL_DWD)
+    TWELL_SLICED_CASES(8, TWELL_DW)
+  } else {
+    TWELL_SLICED_CASES(4, TWELL_DWD)
+    TWELL_SLICED_CASES(4, TWELL_DW)
+  }
+#undef TWELL_DWD
+#undef TWELL_DW
+  return hipGetLastError();
+}
+
 template <typename TS>
 hipError_t launch_t(const BwdArgs& a, hipStream_t s) {
   constexpr int E = ChunkElems<TS>::E;
@@ -512,9 +544,17 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t s) {
   // dz records: ELL rows by column part (main stream), dense rows by column
   // chunk (side stream: disjoint record ranges)
   hipStream_t side = s;
+  const bool dense_mfma = sizeof(TS) == 2 && bwd_dense_mfma_applies(a);
   if (a.dense_cap > 0) {
     if ((err = fork_side(s, &side)) != hipSuccess) return err;
     const dim3 gdd((unsigned)(((int64_t)a.dense_cap * G + 3) / 4));
+    if (dense_mfma) {
+      err = launch_bwd_dense_dz(a, side);
+      if (err != hipSuccess) {
+        (void)join_side(s, side);
+        return err;
+      }
+    } else {
     switch (M) {
       case 1: TWELL_LAUNCH("bwd_dz_dense", (bwd_dz_dense<TS, 1>), gdd, blk, 0, side, a, G); break;
       case 2: TWELL_LAUNCH("bwd_dz_dense", (bwd_dz_dense<TS, 2>), gdd, blk, 0, side, a, G); break;
@@ -527,9 +567,13 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t s) {
       (void)join_side(s, side);
       return err;
     }
+    }
   }
   const int parts = 8;
   const dim3 gdz((unsigned)(((a.N + 3) / 4) * parts));
+  if (sizeof(TS) == 2 && dz_blocked_applies(a)) {
+    err = launch_dz_blocked(a, s);
+  } else {
   switch (M) {
     case 1: TWELL_LAUNCH("bwd_dz_ell", (bwd_dz_ell<TS, 1>), gdz, blk, 0, s, a, parts); break;
     case 2: TWELL_LAUNCH("bwd_dz_ell", (bwd_dz_ell<TS, 2>), gdz, blk, 0, s, a, parts); break;
@@ -539,6 +583,7 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t s) {
     default: (void)join_side(s, side); return hipErrorInvalidValue;
   }
   err = hipGetLastError();
+  }
   const hipError_t ej = join_side(s, side);
   if (err != hipSuccess) return err;
   if (ej != hipSuccess) return ej;
@@ -550,31 +595,23 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t s) {
     (void)join_side(s, side);
     return err;
   }
+  // then, past a mark the weight gradients wait for, dx of the dense rows
+  // (bwd_dx leaves those rows alone); it runs on beside the weight gradients
+  if ((err = mark_side(s, side)) != hipSuccess || (dense_mfma && (err = launch_bwd_dense_dx(a, side)) != hipSuccess)) {
+    (void)join_side(s, side);
+    return err;
+  }
 
   err = launch_dx<TS>(a, s);
-  const hipError_t ej2 = join_side(s, side);
-  if (err != hipSuccess) return err;
-  if (ej2 != hipSuccess) return ej2;
-
-  // weight gradients: column-owned, d_model in 1/8 slices (slicing x / dy
-  // further to fit L2 measured slower here: a column's tokens ascend, so its
-  // gathers already fall close together)
-  const SliceGeom geom = pick_slices(a.D, (int)sizeof(TS));
-  const int P = geom.P, G8 = slice_group(P);
-  const int64_t cblocks = (a.F + 3) / 4;
-  const dim3 gdw((unsigned)(cblocks * P));
-#define TWELL_DWD(E, R) TWELL_LAUNCH("bwd_dw_down", (bwd_dw<TS, E, R, false>), gdw, blk, 0, s, a, G8, cblocks)
-#define TWELL_DW(E, R) TWELL_LAUNCH("bwd_dw", (bwd_dw<TS, E, R, true>), gdw, blk, 0, s, a, G8, cblocks)
-  if constexpr (sizeof(TS) == 2) {
-    TWELL_SLICED_CASES(8, TWELL_DWD)
-    TWELL_SLICED_CASES(8, TWELL_DW)
-  } else {
-    TWELL_SLICED_CASES(4, TWELL_DWD)
-    TWELL_SLICED_CASES(4, TWELL_DW)
+  const hipError_t ej2 = wait_mark(s, side);
+  if (err != hipSuccess || ej2 != hipSuccess) {
+    (void)join_side(s, side);
+    return err != hipSuccess ? err : ej2;
   }
-#undef TWELL_DWD
-#undef TWELL_DW
-  return hipGetLastError();
+
+  err = launch_dw<TS>(a, s);
+  const hipError_t ej3 = join_side(s, side);
+  return err != hipSuccess ? err : ej3;
 }
 
 }  // namespace

@@ -1,0 +1,110 @@
+// dz of the ELL rows of the backward with weight-row reuse through LDS.
+//
+// "Sakana AI and NVIDIA present TwELL" (edge.aivizor.me), second paragraph:
+// training runs on the hybrid format, whose compact ELL part holds the rows
+// that fit it. For the loss of the backward's header (bwd.hip), every active
+// entry (i, c) of an ELL row needs dz = dy_i . W_down[c], a sampled product of
+// the same shape as the forward's up projection (x -> dy, W_up -> W_down), so
+// it runs on the same blocked kernel (blocked_sddmm.h): 512 tokens x 512
+// columns per workgroup, dy and W_down staged through LDS.
+//
+// ell_groups, a small pass before, finds for every ELL row the ELL position
+// of its first entry in each 512-column group (its columns ascend). The
+// blocked kernel then writes each entry's record at row_ptr[i] + its ELL
+// position, as bwd_dz_ell does: column and (z, da, dg) = (h*a, dz*h,
+// dz*a + lambda).
+#include "blocked_sddmm.h"
+#include "twell_host.h"
+#include "twell_kernels.h"
+#include "twell_trace.h"
+
+namespace twell {
+namespace {
+
+constexpr int kGroupCols = blk::kGroupCols;
+constexpr int kMaxGroups = 64;  // d_ff up to 32768
+
+// Wave per row (lane = ELL position): egrp[g][i] = ELL position of the first
+// entry of row i with column >= g * 512, for g = 0 .. n_groups (0 everywhere
+// for dense rows). Entry k writes the groups after its predecessor's up to
+// its own; the first position past the row's end writes the rest, so every
+// egrp value is written exactly once.
+__global__ __launch_bounds__(256) void ell_groups(BwdArgs a, int n_groups) {
+  const int lane = threadIdx.x & 63;
+  const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t N = a.N;
+  if (i >= N) return;
+  const int n = a.is_dense[i] ? 0 : min(a.row_nnz[i], a.row_cap);
+  int32_t* eg = a.ws.egrp + i;  // row g at eg[g * N]
+  int prev_last = -1;           // group of position kb - 1
+  for (int kb = 0; kb <= n; kb += 64) {
+    const int k = kb + lane;
+    // group of position k; positions at or past the end count as group n_groups
+    const int cur = k < n ? (int)min((unsigned)a.ell_cols[(size_t)k * N + i] / kGroupCols, (unsigned)n_groups - 1)
+                          : n_groups;
+    int prev = __shfl_up(cur, 1, 64);
+    if (lane == 0) prev = prev_last;
+    if (k <= n)
+      for (int g = prev + 1; g <= cur; ++g) eg[(size_t)g * N] = k;
+    prev_last = __shfl(cur, 63, 64);
+  }
+}
+
+// The backward's pattern: the ELL entries of the ELL rows; records at
+// row_ptr[i] + ELL position.
+struct DzPolicy {
+  BwdArgs a;
+  static constexpr int kSub = 1;
+  __device__ const uint16_t* rows_a() const { return reinterpret_cast<const uint16_t*>(a.dy); }
+  __device__ const uint16_t* rows_b() const { return reinterpret_cast<const uint16_t*>(a.w_down); }
+  __device__ int64_t n() const { return a.N; }
+  __device__ int d() const { return a.D; }
+  __device__ int f() const { return a.F; }
+  __device__ int c0(int g) const { return g * kGroupCols; }
+  __device__ bool own(int64_t i) const { return !a.is_dense[i]; }
+  __device__ int count(int64_t i, int g, int) const {
+    return a.ws.egrp[(size_t)(g + 1) * a.N + i] - a.ws.egrp[(size_t)g * a.N + i];
+  }
+  __device__ void entry(int64_t i, int g, int, int k, uint32_t& cg, uint32_t& key, uint32_t& hb) const {
+    const int kk = a.ws.egrp[(size_t)g * a.N + i] + k;
+    const size_t off = (size_t)kk * a.N + i;
+    cg = (uint32_t)(a.ell_cols[off] - c0(g));
+    key = (uint32_t)kk;
+    hb = (uint32_t)reinterpret_cast<const uint16_t*>(a.ell_vals)[off] << 16;
+  }
+  __device__ int base(int64_t i, int g) const { return a.ws.row_ptr[i] + a.ws.egrp[(size_t)g * a.N + i]; }
+  __device__ void store(int64_t i, int g, uint32_t cg, uint32_t key, float h, int pos, float dz) const {
+    const float av = a.ell_a[(size_t)key * a.N + i];
+    a.ws.pair_col[pos] = c0(g) + (int)cg;
+    a.ws.coef[pos] = make_float4(h * av, dz * h, fmaf(dz, av, a.lam), 0.f);
+  }
+};
+
+using DzBlk = blk::Default;
+
+__global__ __launch_bounds__(DzBlk::NT, 1) void bwd_dz_blocked(BwdArgs a, int n_groups, int64_t n_tblocks) {
+  blk::sddmm_block<DzBlk>(DzPolicy{a}, n_groups, n_tblocks);
+}
+
+}  // namespace
+
+int dz_groups(int F) { return (F + kGroupCols - 1) / kGroupCols; }
+
+bool dz_blocked_applies(const BwdArgs& a) {
+  return a.is_bf16 && a.N > 64 && a.D % 32 == 0 && a.row_cap < 1024 && dz_groups(a.F) <= kMaxGroups &&
+         a.ws.egrp != nullptr;
+}
+
+hipError_t launch_dz_blocked(const BwdArgs& a, hipStream_t s) {
+  if (!dz_blocked_applies(a)) return hipErrorInvalidValue;
+  const int n_groups = dz_groups(a.F);
+  TWELL_LAUNCH("ell_groups", ell_groups, dim3((unsigned)((a.N + 3) / 4)), 256, 0, s, a, n_groups);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int64_t ntb = (a.N + DzBlk::T - 1) / DzBlk::T;
+  TWELL_LAUNCH("bwd_dz_blocked", bwd_dz_blocked, dim3((unsigned)blk::grid_blocks(ntb, n_groups)), DzBlk::NT, 0, s, a,
+               n_groups, ntb);
+  return hipGetLastError();
+}
+
+}  // namespace twell

@@ -13,8 +13,11 @@
 //
 // fork_side: the side stream waits for everything enqueued on the caller's
 // stream so far. join_side: the caller's stream waits for everything enqueued
-// on the side stream so far. Both only enqueue; neither blocks the host. All
-// streams have the default priority and are non-blocking.
+// on the side stream so far. mark_side / wait_mark split a join in two: the
+// mark is taken on the side stream (everything enqueued there so far), and the
+// caller's stream waits for it later, so work enqueued on the side stream in
+// between runs on past that point. All only enqueue; none blocks the host.
+// All streams have the default priority and are non-blocking.
 #include <mutex>
 
 #include "twell_kernels.h"
@@ -28,7 +31,7 @@ constexpr int kMaxPerDevice = 16;
 struct Side {
   hipStream_t caller = nullptr;
   hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr, mark = nullptr;
 };
 
 struct DeviceSides {
@@ -76,10 +79,12 @@ hipError_t fork_side(hipStream_t main, hipStream_t* side) {
       return hipSuccess;
     }
     if (hipEventCreateWithFlags(&n.fork, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&n.join, hipEventDisableTiming) != hipSuccess) {
+        hipEventCreateWithFlags(&n.join, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&n.mark, hipEventDisableTiming) != hipSuccess) {
       (void)hipGetLastError();
       (void)hipStreamDestroy(n.s);
       if (n.fork) (void)hipEventDestroy(n.fork);
+      if (n.join) (void)hipEventDestroy(n.join);
       return hipSuccess;
     }
     d.e[d.n] = n;
@@ -102,6 +107,30 @@ hipError_t join_side(hipStream_t main, hipStream_t side) {
   if (S == nullptr) return hipErrorInvalidValue;  // not a side stream this library forked
   if ((err = hipEventRecord(S->join, side)) != hipSuccess) return err;
   return hipStreamWaitEvent(main, S->join, 0);
+}
+
+hipError_t mark_side(hipStream_t main, hipStream_t side) {
+  if (side == main) return hipSuccess;
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidValue;
+  std::lock_guard<std::mutex> g(g_mu);
+  Side* S = find_side(g_dev[dev], side);
+  if (S == nullptr) return hipErrorInvalidValue;
+  return hipEventRecord(S->mark, side);
+}
+
+hipError_t wait_mark(hipStream_t main, hipStream_t side) {
+  if (side == main) return hipSuccess;
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidValue;
+  std::lock_guard<std::mutex> g(g_mu);
+  Side* S = find_side(g_dev[dev], side);
+  if (S == nullptr) return hipErrorInvalidValue;
+  return hipStreamWaitEvent(main, S->mark, 0);
 }
 
 }  // namespace twell

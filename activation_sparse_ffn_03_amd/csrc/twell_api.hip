@@ -446,6 +446,12 @@ twell_status twell_ffn_bwd(const twell_dims* dims, twell_dtype dtype, const twel
   a.ws.col_ptr = reinterpret_cast<int32_t*>(base + L.col_ptr);
   a.ws.blk_cnt = reinterpret_cast<int32_t*>(base + L.blk_cnt);
   a.ws.grp_off = reinterpret_cast<int32_t*>(base + L.grp_off);
+  a.ws.egrp = reinterpret_cast<int32_t*>(base + L.egrp);
+  if (twell::bwd_dense_mfma(s)) {
+    a.ws.dza = reinterpret_cast<float*>(base + L.dza);
+    a.ws.dadg = reinterpret_cast<uint16_t*>(base + L.dadg);
+    a.ws.dxpart = reinterpret_cast<float*>(base + L.dxpart);
+  }
   return hip_status(twell::launch_ffn_bwd(a, (hipStream_t)stream), "twell_ffn_bwd");
 }
 

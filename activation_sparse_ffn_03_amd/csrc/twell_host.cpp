@@ -130,6 +130,12 @@ BwdLayout bwd_layout(const Shape& s) {
   L.col_ptr = take(((size_t)s.F + 1) * 4);
   L.blk_cnt = take((size_t)s.nrb * s.F * 4);
   L.grp_off = take((size_t)s.dense_cap * s.G * 4);
+  L.egrp = take(((size_t)(s.F + 511) / 512 + 1) * s.N * 4);
+  const bool dm = bwd_dense_mfma(s);
+  const size_t dc = (size_t)s.dense_cap;
+  L.dza = take(dm ? 2 * dc * s.F * 4 : 0);
+  L.dadg = take(dm ? 4 * dc * dense_z_stride(s.F) * 2 : 0);
+  L.dxpart = take(dm ? dc * s.G * s.D * 4 : 0);
   L.total = off;
   return L;
 }

@@ -28,13 +28,18 @@ struct Shape {
 
 // Offsets (bytes from the workspace base) of every backward workspace array.
 struct BwdLayout {
-  size_t row_ptr, dense_pos, pair_col, coef, csc_pair, csc_row, col_ptr, blk_cnt, grp_off, total;
+  size_t row_ptr, dense_pos, pair_col, coef, csc_pair, csc_row, col_ptr, blk_cnt, grp_off, egrp;
+  size_t dza, dadg, dxpart;  // 0 bytes (offset == next) unless bwd_dense_mfma(s)
+  size_t total;
 };
 
 // Validate dims/dtype; on failure returns the status and sets *why.
 twell_status check_shape(const twell_dims* dims, int dtype, Shape* out, std::string* why);
 void compute_sizes(const Shape& s, twell_sizes* out);
 BwdLayout bwd_layout(const Shape& s);
+// The backward's dense-backup rows take the skinny MFMA products (bf16,
+// d_model a multiple of 128, a dense capacity).
+inline bool bwd_dense_mfma(const Shape& s) { return s.esz == 2 && s.D % 128 == 0 && s.dense_cap > 0; }
 // Passes over d_model of the up projection. W_up's columns are dealt to the 8
 // XCDs (F/8 rows of W_up each); when such a block is larger than the XCD's
 // 4 MB L2, d_model is cut into up_passes power-of-two ranges (each a whole

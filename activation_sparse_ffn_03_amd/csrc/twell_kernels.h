@@ -115,6 +115,11 @@ hipError_t launch_forward(const GateArgs& g, const FwdArgs& f, hipStream_t s, bo
 // creation failure); join_side makes `main` wait for the work enqueued on it.
 hipError_t fork_side(hipStream_t main, hipStream_t* side);
 hipError_t join_side(hipStream_t main, hipStream_t side);
+// A join in two steps: mark_side marks the work enqueued on `side` so far;
+// wait_mark makes `main` wait for that mark (not for what `side` took on
+// after it). No-ops when side == main.
+hipError_t mark_side(hipStream_t main, hipStream_t side);
+hipError_t wait_mark(hipStream_t main, hipStream_t side);
 
 // out[rows[o]] = sum_g part[o][g] for o < min(*n_rows, cap), part [cap][G][D].
 hipError_t launch_dense_reduce(const float* part, const int32_t* rows, const int32_t* n_rows, int cap, int G,
@@ -156,6 +161,11 @@ struct BwdWorkspace {
   int32_t* col_ptr;    // [F+1]
   int32_t* blk_cnt;    // [n_rb][F]
   int32_t* grp_off;    // [dense_cap][G]
+  int32_t* egrp;       // [ceil(F / 512) + 1][N] ELL position of each row's first entry per 512-column group
+  // dense-backup rows on the matrix cores (bf16, d_model a multiple of 128; else null):
+  float* dza;          // [2][dense_cap][F] dz, then a, of every unit of the dense rows
+  uint16_t* dadg;      // [4][dense_cap][dense_z_stride(F)] da high, da low, dg high, dg low (bf16)
+  float* dxpart;       // [dense_cap][G][D] partial dx of the d_ff chunks
 };
 
 struct BwdArgs {
@@ -184,5 +194,15 @@ struct BwdArgs {
 };
 
 hipError_t launch_ffn_bwd(const BwdArgs& a, hipStream_t s);
+// dz records of the ELL rows with weight-row reuse through LDS
+// (bwd_blocked.hip): the per-row group positions, then the blocked product.
+int dz_groups(int F);
+bool dz_blocked_applies(const BwdArgs& a);
+hipError_t launch_dz_blocked(const BwdArgs& a, hipStream_t s);
+// Dense-backup rows as skinny MFMA products (bwd_dense.hip): dz and a, then
+// their records and da / dg; then dx of those rows (bwd_dx skips them).
+bool bwd_dense_mfma_applies(const BwdArgs& a);
+hipError_t launch_bwd_dense_dz(const BwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_dense_dx(const BwdArgs& a, hipStream_t s);
 
 }  // namespace twell

@@ -225,6 +225,12 @@ hipError_t launch_ffn_bwd(const BwdArgs& a, hipStream_t) {
   extent(a.ws.col_ptr, (F + 1) * 4, "ws.col_ptr");
   extent(a.ws.blk_cnt, nrb * F * 4, "ws.blk_cnt");
   extent(a.ws.grp_off, dc * G * 4, "ws.grp_off");
+  extent(a.ws.egrp, ((F + 511) / 512 + 1) * N * 4, "ws.egrp");
+  if (a.ws.dza != nullptr) {
+    extent(a.ws.dza, 2 * dc * F * 4, "ws.dza");
+    extent(a.ws.dadg, 4 * dc * dense_z_stride((int)F) * 2, "ws.dadg");
+    extent(a.ws.dxpart, dc * G * D * 4, "ws.dxpart");
+  }
   ++g_launches;
   return hipSuccess;
 }

@@ -260,6 +260,8 @@ def _check_backward(w, pl, grads, tol=1e-4):
     dict(N=700, D=2048, F=640, K=12, dense_cap=700),
     dict(N=512, D=512, F=1300, K=40, tile_n=16),   # 82 tiles: the router's tile batches of 64
     dict(N=384, D=2048, F=8448, K=120, dense_cap=384),  # a_save from two d_model passes of the up projection
+    dict(N=600, D=384, F=1100, K=8, dense_cap=600),    # hundreds of dense rows: MFMA passes of 64 rows,
+                                                       # ragged last d_ff chunk, 3 tiles of 128 columns
 ])
 def test_route_and_backward(case):
     case = dict(case)
