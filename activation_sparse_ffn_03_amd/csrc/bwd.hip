@@ -13,7 +13,8 @@
 //
 // Pipeline (all deterministic, no floating-point atomics):
 //   dense_groups  per dense row: active count per column chunk -> offsets
-//   row_scan      CSR offsets of every row's entries (one workgroup)
+//   row_scan      CSR offsets of every row's entries (one workgroup, rows
+//                 held in registers)
 //   bwd_dz_ell    wave per ELL row and column part: dz, da, dg, z; writes
 //                 each entry's column and (z, da, dg) in CSR order (bf16
 //                 batches take the blocked form of bwd_blocked.hip instead)
@@ -73,9 +74,77 @@ __device__ void block_exclusive_scan(int32_t* part, int tid) {
   }
 }
 
+// Exclusive sum over the 1024 threads of the block of v (wave scans, then the
+// 16 wave totals through LDS); *total gets the block's sum.
+__device__ __forceinline__ int32_t block_excl_1024(int32_t v, int32_t* wsum, int32_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int32_t x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  int32_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) {
+    const int32_t t = wsum[w];
+    before += w < wave ? t : 0;
+    all += t;
+  }
+  __syncthreads();
+  *total = all;
+  return before + x - v;
+}
+
 // Effective entry count of a row: row_nnz for ELL rows, the dense row's own
-// count for dense rows inside the capacity, 0 for dense rows beyond it.
+// count for dense rows inside the capacity, 0 for dense rows beyond it. One
+// workgroup; thread t owns rows [t*C, t*C + C), held in registers, so all of
+// a thread's loads are issued together.
+template <int C>
 __global__ __launch_bounds__(1024) void row_scan(BwdArgs a, const int32_t* dense_nnz) {
+  __shared__ int32_t wsum[16];
+  const int tid = threadIdx.x;
+  const int64_t N = a.N;
+  const int64_t b = (int64_t)tid * C;
+  const int nd = min(*a.n_dense, a.dense_cap);
+  bool dn[C];
+  int32_t nz[C];
+  int32_t cnt = 0;
+#pragma unroll
+  for (int k = 0; k < C; ++k) {
+    const int64_t i = b + k;
+    dn[k] = i < N && a.is_dense[i] != 0;
+    nz[k] = i < N ? min(a.row_nnz[i], a.row_cap) : 0;
+    cnt += dn[k];
+  }
+  int32_t tot;
+  int32_t dpos = block_excl_1024(cnt, wsum, &tot);
+  int32_t eff[C], dp[C];
+  int32_t s = 0;
+#pragma unroll
+  for (int k = 0; k < C; ++k) {
+    dp[k] = dn[k] ? dpos++ : -1;
+    eff[k] = dn[k] ? (dp[k] < nd ? dense_nnz[dp[k]] : 0) : nz[k];
+    s += eff[k];
+  }
+  int32_t run = block_excl_1024(s, wsum, &tot);
+#pragma unroll
+  for (int k = 0; k < C; ++k) {
+    const int64_t i = b + k;
+    if (i < N) {
+      a.ws.dense_pos[i] = dp[k];
+      a.ws.row_ptr[i] = run;
+    }
+    run += eff[k];
+  }
+  if (tid == 1023) a.ws.row_ptr[N] = tot;
+}
+
+// The same for any N (beyond 32768 rows): thread t walks rows
+// [t*chunk, (t+1)*chunk) three times.
+__global__ __launch_bounds__(1024) void row_scan_any(BwdArgs a, const int32_t* dense_nnz) {
   __shared__ int32_t part[1024];
   const int tid = threadIdx.x;
   const int64_t N = a.N;
@@ -525,6 +594,14 @@ hipError_t launch_dw(const BwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Rows per thread of row_scan: the smallest power of two covering N / 1024
+// (64 and more would spill: those N take row_scan_any).
+int row_scan_rows(int64_t N) {
+  int c = 1;
+  while ((int64_t)c * 1024 < N && c < 64) c *= 2;
+  return c;
+}
+
 template <typename TS>
 hipError_t launch_t(const BwdArgs& a, hipStream_t s) {
   constexpr int E = ChunkElems<TS>::E;
@@ -539,7 +616,15 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t s) {
   if (a.dense_cap > 0) {
     TWELL_LAUNCH("dense_groups", dense_groups<TS>, dim3((a.dense_cap + 3) / 4), blk, 0, s, a, G, dense_nnz);
   }
-  TWELL_LAUNCH("row_scan", row_scan, 1, 1024, 0, s, a, dense_nnz);
+  switch (row_scan_rows(a.N)) {
+    case 1: TWELL_LAUNCH("row_scan", row_scan<1>, 1, 1024, 0, s, a, dense_nnz); break;
+    case 2: TWELL_LAUNCH("row_scan", row_scan<2>, 1, 1024, 0, s, a, dense_nnz); break;
+    case 4: TWELL_LAUNCH("row_scan", row_scan<4>, 1, 1024, 0, s, a, dense_nnz); break;
+    case 8: TWELL_LAUNCH("row_scan", row_scan<8>, 1, 1024, 0, s, a, dense_nnz); break;
+    case 16: TWELL_LAUNCH("row_scan", row_scan<16>, 1, 1024, 0, s, a, dense_nnz); break;
+    case 32: TWELL_LAUNCH("row_scan", row_scan<32>, 1, 1024, 0, s, a, dense_nnz); break;
+    default: TWELL_LAUNCH("row_scan", row_scan_any, 1, 1024, 0, s, a, dense_nnz); break;
+  }
 
   // dz records: ELL rows by column part (main stream), dense rows by column
   // chunk (side stream: disjoint record ranges)

@@ -42,6 +42,8 @@ __device__ __forceinline__ int wave_excl_scan(int v) {
   return x - v;
 }
 
+constexpr int kRouteBatch = 4;
+
 // One wave per row. Pass 1: row_nnz and the dense decision from the tile
 // counts (64 tiles per load). Pass 2 (ELL rows): lane l takes tile jb+l of a
 // 64-tile batch; iteration s copies slot s of every lane's tile to ELL
@@ -72,13 +74,31 @@ __global__ __launch_bounds__(1024) void route_rows(RouteArgs a) {
     const int cnt = jl < a.n_tiles ? (int)a.counts[(size_t)jl * N + i] : 0;  // <= S: the row did not overflow
     const int start = base + wave_excl_scan(cnt);
     const int maxc = wave_max_i(cnt);
-    for (int sl = 0; sl < maxc; ++sl) {
-      if (sl < cnt) {
-        const size_t src = ((size_t)jl * a.slots + sl) * N + i;
-        const size_t dst = (size_t)(start + sl) * N + i;
-        ev[dst] = vals[src];
-        a.ell_cols[dst] = jl * a.tile_n + a.cols[src];
-        a.ell_a[dst] = a.a_save[src];
+    // kRouteBatch slots at a time: every load of the batch is issued before
+    // its stores, so a lane has 3 * kRouteBatch loads in flight
+    for (int sl0 = 0; sl0 < maxc; sl0 += kRouteBatch) {
+      TS v[kRouteBatch];
+      uint16_t c[kRouteBatch];
+      float av[kRouteBatch];
+#pragma unroll
+      for (int u = 0; u < kRouteBatch; ++u) {
+        const int sl = sl0 + u;
+        if (sl < cnt) {
+          const size_t src = ((size_t)jl * a.slots + sl) * N + i;
+          v[u] = vals[src];
+          c[u] = a.cols[src];
+          av[u] = a.a_save[src];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kRouteBatch; ++u) {
+        const int sl = sl0 + u;
+        if (sl < cnt) {
+          const size_t dst = (size_t)(start + sl) * N + i;
+          ev[dst] = v[u];
+          a.ell_cols[dst] = jl * a.tile_n + c[u];
+          a.ell_a[dst] = av[u];
+        }
       }
     }
     base = __builtin_amdgcn_readlane(start + cnt, 63);  // start already includes base
