@@ -45,6 +45,7 @@ namespace twell {
 namespace blk {
 
 constexpr int kGroupCols = 512;  // columns of a group at most
+constexpr int kCus = 256;        // compute units of an MI355X: the blocked form needs this many workgroups
 
 // Super-tile of the workgroup order: token blocks x column groups that one
 // XCD runs at a time (32 workgroups, one per CU of the XCD).

@@ -91,8 +91,9 @@ __global__ __launch_bounds__(DzBlk::NT, 1) void bwd_dz_blocked(BwdArgs a, int n_
 int dz_groups(int F) { return (F + kGroupCols - 1) / kGroupCols; }
 
 bool dz_blocked_applies(const BwdArgs& a) {
+  const int64_t pairs = ((a.N + DzBlk::T - 1) / DzBlk::T) * dz_groups(a.F);
   return a.is_bf16 && a.N > 64 && a.D % 32 == 0 && a.row_cap < 1024 && dz_groups(a.F) <= kMaxGroups &&
-         a.ws.egrp != nullptr;
+         a.ws.egrp != nullptr && pairs >= blk::kCus;
 }
 
 hipError_t launch_dz_blocked(const BwdArgs& a, hipStream_t s) {

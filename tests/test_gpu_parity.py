@@ -173,6 +173,8 @@ def test_ovf_rows_match_epilogue_values():
     ("c2", dict(N=96, D=128, F=300, density=0.75), dict(slots=128)),  # more than 64 slots in use per tile
     ("c4", dict(N=520, D=384, F=1100), dict(slots=2, ovf_cap=520)),  # hundreds of overflow rows: MFMA
                                                           # passes of 64 rows, ragged last d_ff chunk
+    ("c2", dict(N=8000, D=192, F=8100), {}),             # 16 x 16 blocks of 512 tokens x 4 tiles: the blocked
+                                                          # up projection, ragged last token block and tile
     ("c2", dict(N=300, D=2048, F=8448), {}),             # W_up block per XCD > 4 MB: two d_model passes
     ("c1", dict(N=200, D=1024, F=8448), {}),             # the same in fp32
 ])
@@ -260,6 +262,7 @@ def _check_backward(w, pl, grads, tol=1e-4):
     dict(N=700, D=2048, F=640, K=12, dense_cap=700),
     dict(N=512, D=512, F=1300, K=40, tile_n=16),   # 82 tiles: the router's tile batches of 64
     dict(N=384, D=2048, F=8448, K=120, dense_cap=384),  # a_save from two d_model passes of the up projection
+    dict(N=8000, D=192, F=8100, K=400, dense_cap=1024),  # 16 x 16 blocks: the blocked dz of the ELL rows
     dict(N=600, D=384, F=1100, K=8, dense_cap=600),    # hundreds of dense rows: MFMA passes of 64 rows,
                                                        # ragged last d_ff chunk, 3 tiles of 128 columns
 ])
