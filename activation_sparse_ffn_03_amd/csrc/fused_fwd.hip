@@ -497,7 +497,7 @@ hipError_t launch_forward(const GateArgs& g, const FwdArgs& f, hipStream_t s, bo
     return err != hipSuccess ? err : launch_ffn_fwd(f, s);
   }
   hipStream_t side = s;
-  hipError_t err = launch_gate_pack_split(g, s, true, &side);
+  hipError_t err = launch_gate_pack_split(g, s, true, &side, f.is_bf16 && up_blocked_applies(f));
   if (side == s) return err != hipSuccess ? err : launch_ffn_fwd(f, s);  // nothing was forked
   if (err == hipSuccess && f.ovf_cap > 0)
     err = f.is_bf16 ? launch_overflow_rows<uint16_t>(f, side) : launch_overflow_rows<float>(f, side);

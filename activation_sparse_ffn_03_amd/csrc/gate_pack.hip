@@ -941,10 +941,11 @@ bool gate_ovf_rows_heavy(const GateArgs& a) {
 
 hipError_t launch_gate_pack(const GateArgs& a, hipStream_t s) {
   hipStream_t so = s;
-  return launch_gate_pack_split(a, s, false, &so);
+  return launch_gate_pack_split(a, s, false, &so, true);
 }
 
-hipError_t launch_gate_pack_split(const GateArgs& a, hipStream_t s, bool fork, hipStream_t* ovf_stream) {
+hipError_t launch_gate_pack_split(const GateArgs& a, hipStream_t s, bool fork, hipStream_t* ovf_stream,
+                                  bool list_on_main) {
   *ovf_stream = s;
   Epi e{};
   e.N = a.N;
@@ -1020,16 +1021,21 @@ hipError_t launch_gate_pack_split(const GateArgs& a, hipStream_t s, bool fork, h
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || no_ovf) return err;
 
-  // 2. overflow rows from the true counts: the flags and the list on `s`
-  // (two short launches; on a side stream they would wait for CUs behind the
-  // up projection, which holds all of a CU's LDS), then the dense rows on `so`
-  // (the side stream when asked to fork)
-  TWELL_LAUNCH("ovf_flags", ovf_flags, dim3((a.N + 63) / 64), 64, 0, s, a.counts, a.N, a.n_tiles, a.slots,
-               a.ovf_flag);
-  err = launch_compact(a.ovf_flag, a.N, a.ovf_rows, a.ovf_cap, a.n_ovf, a.status, 1u /*TWELL_DEV_OVF_CAPACITY*/, s);
-  if (err != hipSuccess || a.ovf_cap == 0) return err;
+  // 2. overflow rows from the true counts: the flags, the list and the dense
+  // rows on `so` (the side stream when asked to fork). With list_on_main the
+  // flags and the list stay on `s` (two short launches that on a side stream
+  // would wait for CUs behind a blocked up projection, which holds all of a
+  // CU's LDS).
   hipStream_t so = s;
-  if (fork) {
+  if (fork && !list_on_main) {
+    if ((err = fork_side(s, &so)) != hipSuccess) return err;
+    *ovf_stream = so;
+  }
+  TWELL_LAUNCH("ovf_flags", ovf_flags, dim3((a.N + 63) / 64), 64, 0, so, a.counts, a.N, a.n_tiles, a.slots,
+               a.ovf_flag);
+  err = launch_compact(a.ovf_flag, a.N, a.ovf_rows, a.ovf_cap, a.n_ovf, a.status, 1u /*TWELL_DEV_OVF_CAPACITY*/, so);
+  if (err != hipSuccess || a.ovf_cap == 0) return err;
+  if (fork && list_on_main) {
     if ((err = fork_side(s, &so)) != hipSuccess) return err;
     *ovf_stream = so;
   }

@@ -44,12 +44,14 @@ struct GateArgs {
 };
 
 hipError_t launch_gate_pack(const GateArgs& a, hipStream_t s);
-// The same launches, with the overflow rows' dense activations enqueued on
-// the side stream when `fork` is set (the pack, the flags and the overflow
-// list stay on `s`). *ovf_stream is the stream that ends the overflow branch:
-// `s` when nothing was forked (no overflow steps, or fork unset), else the
-// side stream, which the caller must join back into `s`.
-hipError_t launch_gate_pack_split(const GateArgs& a, hipStream_t s, bool fork, hipStream_t* ovf_stream);
+// The same launches, with the overflow steps enqueued on the side stream
+// when `fork` is set: the overflow rows' dense activations, and also the
+// flags and the overflow list unless list_on_main (the pack always stays on
+// `s`). *ovf_stream is the stream that ends the overflow branch: `s` when
+// nothing was forked (no overflow steps, or fork unset), else the side stream,
+// which the caller must join back into `s`.
+hipError_t launch_gate_pack_split(const GateArgs& a, hipStream_t s, bool fork, hipStream_t* ovf_stream,
+                                  bool list_on_main);
 // True when the overflow rows' gate rows take the 128x128 register-staged
 // GEMM (bf16, d_model > 2048 and not a multiple of 32, large batch): a long
 // launch that, run beside the up projection, costs it more occupancy than it

@@ -148,7 +148,7 @@ hipError_t launch_gate_pack(const GateArgs& a, hipStream_t) {
   ++g_launches;
   return hipSuccess;
 }
-hipError_t launch_gate_pack_split(const GateArgs& a, hipStream_t s, bool, hipStream_t* o) {
+hipError_t launch_gate_pack_split(const GateArgs& a, hipStream_t s, bool, hipStream_t* o, bool) {
   *o = s;
   return launch_gate_pack(a, s);
 }
