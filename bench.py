@@ -119,7 +119,7 @@ def kernel_work(name, w, st, train):
     if name == "ffn_down_kernel":  # W_down once; cols + z read; y written (fp32)
         byt = F * D * e + nnz * (2 + 4) + n_t * N * 2 + N * D * 4
         return {"flops": 2.0 * D * nnz, "bytes": byt, "bound": "hbm", "gathered": nnz * D * e}
-    if name == "bwd_dz_ell":   # dy, W_down once; row-ELL read; (col, z, da, dg) records written
+    if name in ("bwd_dz_ell", "bwd_dz_blocked"):   # dy, W_down once; row-ELL read; (col, z, da, dg) records written
         byt = N * D * e + F * D * e + nnz_ell * (e + 8) + nnz_ell * 20
         return {"flops": 2.0 * D * nnz_ell, "bytes": byt, "bound": "hbm", "gathered": nnz_ell * D * e}
     if name == "bwd_dx":       # W_up once; records read; dx written (fp32)
@@ -245,9 +245,10 @@ KERNEL_SOURCES = {
     "pack_from_g": ["gate_pack.hip", "twell_device.h"],
     "quantize_e4m3": ["quant.hip", "twell_device.h"],
     "ffn_up_kernel": ["fused_fwd.hip", "row_ops.h", "twell_device.h"],
-    "ffn_up_blocked": ["up_blocked.hip", "row_ops.h", "twell_device.h"],
+    "ffn_up_blocked": ["up_blocked.hip", "blocked_sddmm.h", "row_ops.h", "twell_device.h"],
     "ffn_down_kernel": ["fused_fwd.hip", "row_ops.h", "twell_device.h"],
     "bwd_dz_ell": ["bwd.hip", "row_ops.h", "twell_device.h"],
+    "bwd_dz_blocked": ["bwd_blocked.hip", "blocked_sddmm.h", "twell_device.h"],
     "bwd_dx": ["bwd.hip", "row_ops.h", "twell_device.h"],
     "bwd_dx_gate": ["bwd.hip", "row_ops.h", "twell_device.h"],
     "bwd_dw_down": ["bwd.hip", "row_ops.h", "twell_device.h"],
