@@ -8,17 +8,19 @@
 //
 // Kernels
 //   gate_mfma_dma    TwELL pack path: 256x384 output tile per 8-wave
-//                    workgroup (128x384 per 4-wave workgroup for FP8 grids of
-//                    several waves), v_mfma_f32_16x16x32_bf16, K-steps of 32
-//                    loaded straight into a 2- or 3-stage LDS ring by
-//                    global_load_lds; XCD-aware tile order; the epilogue
+//                    workgroup when the grid is one wave of tiles, 256x256
+//                    on deeper grids (128x384 per 4-wave workgroup for FP8
+//                    grids of several waves), v_mfma_f32_16x16x32_bf16,
+//                    K-steps of 32 loaded straight into a 2- to 4-stage LDS
+//                    ring by global_load_lds; XCD-aware tile order; the epilogue
 //                    stages the fp32 tile in LDS one 128-column group at a
 //                    time and packs it. With FP8 = true the operands are E4M3
 //                    codes (64 k per 64-byte LDS row, one
 //                    v_mfma_f32_32x32x64_f8f6f4 per 32x32 fragment pair and
 //                    stage) and the epilogue applies the row and column scales.
 //   gate_mfma_bf16   register-staged variant (128x128, K-steps of 64), used to
-//                    recompute the overflow rows with identical arithmetic.
+//                    recompute the overflow rows with identical arithmetic
+//                    where gate_rows_skinny (dense_rows.hip) does not apply.
 //   gate_simt_f32    64x128 fp32 tile, plain FMA (fp32 storage only).
 //   gate_gemv_small  small batches (N <= 64, bf16): g as a GEMV over all CUs
 //                    into a caller's buffer, then packed by pack_from_g.
@@ -660,20 +662,25 @@ __global__ __launch_bounds__(C::NT, C::OCC) void gate_mfma_dma(const void* __res
 
 // Tile configurations of the bf16 gate GEMM. All accumulate each output
 // element over K in the same order (32-wide MFMA steps, ascending K), so they
-// produce bit-identical g. The TwELL pack uses the LDS-DMA kernel with a
-// 256x384 tile: eight waves of 128x96 (two per SIMD), one workgroup per CU,
-// the pack epilogue in 256-row passes with every wave busy. Its operand ring
-// has three stages (GatePack) when the grid is several waves of tiles deep,
-// two (GatePackOne) when every tile fits in one wave of workgroups (measured
-// on the 4096 x 5632 x 2048 gate: 92 us with two stages, 95 with three, 101
-// for the earlier 128x384 tile of four waves at two workgroups per CU; on the
-// 16384 x 11008 x 4096 gate 1.25 ms with three stages, 1.29 with two). The
-// overflow rows use the register-staged kernel (a few rows, gathered): 64x128
-// tiles for d_model <= 2048 (half the padding rows of a 128-row tile), 128x128
-// above (with a long K the better operand reuse of the larger wave tiles wins;
-// measured 46 -> 35 us at d_model 2048 and 80 -> 109 us at 4096 for 64-row
-// tiles).
-using GatePack = DmaCfg<256, 384, 2, 4, 3, 1>;
+// produce bit-identical g. The TwELL pack uses the LDS-DMA kernel, eight
+// waves (two per SIMD), one workgroup per CU, the pack epilogue in 256-row
+// passes with every wave busy. When every tile fits in one wave of
+// workgroups the tile is 256x384 (waves of 128x96) with a two-stage ring
+// (GatePackOne; measured on the 4096 x 5632 x 2048 gate: 92 us with two
+// stages, 95 with three, 101 for the earlier 128x384 tile of four waves at two
+// workgroups per CU). On deeper grids it is 256x256 (waves of 128x64) with a
+// four-stage ring (GatePack): the smaller accumulator set leaves registers
+// for more fragments, and the grid's last wave of tiles is finer (measured,
+// us: 16384 x 11008 x 4096 gate 1278-1300 against 1305-1325 for 256x384 with
+// three stages, 1311-1351 with three stages and 1376-1382 with two;
+// 8192 x 14336 x 4096 823-827 against 813-826; 8192 x 8192 x 2048 256-257
+// against 266-281). The overflow rows use the register-staged kernel (a few
+// rows, gathered) where gate_rows_skinny (dense_rows.hip) does not apply:
+// 64x128 tiles for d_model <= 2048 (half the padding rows of a 128-row tile),
+// 128x128 above (with a long K the better operand reuse of the larger wave
+// tiles wins; measured 46 -> 35 us at d_model 2048 and 80 -> 109 us at 4096
+// for 64-row tiles).
+using GatePack = DmaCfg<256, 256, 2, 4, 4, 1>;
 using GatePackOne = DmaCfg<256, 384, 2, 4, 2, 1>;
 // FP8 operands on grids of several waves keep the 128x384 tile of four waves
 // at two workgroups per CU (measured on the 16384 x 11008 x 4096 gate: 0.70 ms
@@ -681,8 +688,8 @@ using GatePackOne = DmaCfg<256, 384, 2, 4, 2, 1>;
 // 2048 gate, one wave of tiles, the two-stage 256x384 tile takes 55 us against
 // 57 us with three stages and 59 us for the 128x384 tile).
 using GatePackFp8 = DmaCfg<128, 384, 1, 4, 2, 2>;
-static_assert(GatePack::BM == GatePackOne::BM && GatePack::BN == GatePackOne::BN, "same tile grid");
-constexpr int kCus = 256;  // compute units of an MI355X: workgroups of one wave of GatePack tiles
+static_assert(GatePackFp8::BN == GatePackOne::BN, "the FP8 configurations share the column grid");
+constexpr int kCus = 256;  // compute units of an MI355X: workgroups of one wave of tiles
 using GateRowsS = MfmaCfg<64, 128, 1, 4>;
 using GateRowsL = MfmaCfg<128, 128, 2, 2>;
 
@@ -991,7 +998,8 @@ hipError_t launch_gate_pack_split(const GateArgs& a, hipStream_t s, bool fork, h
   // 1. GEMM (or given g) + TwELL pack epilogue
   e.mode = MODE_PACK;
   if (a.fp8 && g_in == nullptr) {
-    const int mbc = (int)((a.N + GatePack::BM - 1) / GatePack::BM), nbc = (a.F + GatePack::BN - 1) / GatePack::BN;
+    const int mbc = (int)((a.N + GatePackOne::BM - 1) / GatePackOne::BM),
+              nbc = (a.F + GatePackOne::BN - 1) / GatePackOne::BN;
     if ((int64_t)mbc * nbc <= kCus) {
       TWELL_LAUNCH("gate_mfma_fp8", (gate_mfma_dma<GatePackOne, MODE_PACK, true>), dim3(mbc * nbc), GatePackOne::NT,
                    0, s, a.x, a.w, a.D, mbc, nbc, e);
@@ -1007,13 +1015,16 @@ hipError_t launch_gate_pack_split(const GateArgs& a, hipStream_t s, bool fork, h
     else
       TWELL_LAUNCH("pack_from_g", (pack_from_g<float, MODE_PACK>), dim3(mb * ncb), 256, 0, s, g_in, ncb, e);
   } else if (a.is_bf16) {
-    const int mbc = (int)((a.N + GatePack::BM - 1) / GatePack::BM), nbc = (a.F + GatePack::BN - 1) / GatePack::BN;
-    if ((int64_t)mbc * nbc <= kCus)
+    const int mbc = (int)((a.N + GatePackOne::BM - 1) / GatePackOne::BM),
+              nbc = (a.F + GatePackOne::BN - 1) / GatePackOne::BN;
+    if ((int64_t)mbc * nbc <= kCus) {
       TWELL_LAUNCH("gate_mfma_bf16", (gate_mfma_dma<GatePackOne, MODE_PACK>), dim3(mbc * nbc), GatePackOne::NT, 0, s,
                    (const uint16_t*)a.x, (const uint16_t*)a.w, a.D, mbc, nbc, e);
-    else
-      TWELL_LAUNCH("gate_mfma_bf16", (gate_mfma_dma<GatePack, MODE_PACK>), dim3(mbc * nbc), GatePack::NT, 0, s,
-                 (const uint16_t*)a.x, (const uint16_t*)a.w, a.D, mbc, nbc, e);
+    } else {
+      const int mbd = (int)((a.N + GatePack::BM - 1) / GatePack::BM), nbd = (a.F + GatePack::BN - 1) / GatePack::BN;
+      TWELL_LAUNCH("gate_mfma_bf16", (gate_mfma_dma<GatePack, MODE_PACK>), dim3(mbd * nbd), GatePack::NT, 0, s,
+                   (const uint16_t*)a.x, (const uint16_t*)a.w, a.D, mbd, nbd, e);
+    }
   } else {
     const int64_t mb = (a.N + SBM - 1) / SBM;
     TWELL_LAUNCH("gate_simt_f32", gate_simt_f32<MODE_PACK>, dim3(mb * ncb), 256, 0, s, (const float*)a.x, (const float*)a.w, a.D, ncb, e);
