@@ -23,8 +23,9 @@
 //                 a multiple of 128 take the skinny MFMA products of
 //                 bwd_dense.hip instead, which also give those rows' dx)
 //   bwd_dx        wave per row: dx from the records
-//   csc_*         stable counting sort of the entries by column (row blocks
-//                 processed row by row, so each column lists rows ascending)
+//   csc_*         stable counting sort of the entries by column (per block of
+//                 32 rows a bit mask per column, so each column lists its rows
+//                 ascending and every record is placed independently)
 //   bwd_dw        wave per (column, D-part): the three weight-gradient rows
 #include "row_ops.h"
 #include "twell_kernels.h"
@@ -377,89 +378,117 @@ __global__ __launch_bounds__(256) void bwd_dx(BwdArgs a, int G8, int64_t rblocks
 
 // --------------------------------------------------------------- column transpose
 
-// Per block of RB rows: how many of its entries fall in each column. Counters
-// are 16-bit halves of 32-bit LDS words (a column gets at most RB per block).
-__global__ __launch_bounds__(256) void csc_hist(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ pair_col,
-                                                int64_t N, int F, int32_t* __restrict__ blk_cnt) {
-  extern __shared__ uint32_t cnt[];
-  const int nw = (F + 1) / 2;
-  for (int q = threadIdx.x; q < nw; q += blockDim.x) cnt[q] = 0;
+// Stable counting sort of the records by column, in blocks of RB = 32 rows.
+// For every block and column, bit r of mask[b][c] says whether row b*32 + r
+// has an entry in column c; it is built with LDS atomicOr, which gives the
+// same bits in any order, so everything below is deterministic. A record of
+// row i in column c then goes to
+//   col_ptr[c] + rel[b][c] + popcount(mask[b][c] & (bits below i's)),
+// where rel[b][c] counts the column's entries in earlier blocks: rows ascend
+// within every column, with every record placed independently.
+constexpr int kMaxTransposeF = 32768;  // d_ff the LDS masks cover (the backward's limit)
+
+// Wave w of the block takes rows r0 + w, r0 + w + 4, ...; lane l entries l,
+// l + 64, ... of the row. `body` gets the record index, its column and the
+// row's bit in the block.
+template <typename Body>
+__device__ __forceinline__ void csc_block_rows(const int32_t* __restrict__ row_ptr,
+                                               const int32_t* __restrict__ pair_col, int64_t r0, int64_t r1,
+                                               Body&& body) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int64_t i = r0 + wave; i < r1; i += 4) {
+    const int32_t e = row_ptr[i + 1];
+    for (int32_t p = row_ptr[i] + lane; p < e; p += 64) body(p, pair_col[p], (int)(i - r0));
+  }
+}
+
+// FMAX: the largest d_ff of the instantiation (its LDS is FMAX words, so
+// smaller d_ff leave room for other workgroups on the CU).
+template <int FMAX>
+__global__ __launch_bounds__(256) void csc_mask(const int32_t* __restrict__ row_ptr,
+                                                const int32_t* __restrict__ pair_col, int64_t N, int F,
+                                                uint32_t* __restrict__ masks) {
+  __shared__ uint32_t m[FMAX];
+  for (int q = threadIdx.x; q < F; q += 256) m[q] = 0u;
   __syncthreads();
   const int64_t r0 = (int64_t)blockIdx.x * RB, r1 = min(N, r0 + RB);
-  for (int32_t p = row_ptr[r0] + threadIdx.x; p < row_ptr[r1]; p += blockDim.x) {
-    const int c = pair_col[p];
-    atomicAdd(&cnt[c >> 1], 1u << ((c & 1) * 16));
-  }
+  csc_block_rows(row_ptr, pair_col, r0, r1, [&](int32_t, int c, int r) { atomicOr(&m[c], 1u << r); });
   __syncthreads();
-  int32_t* out = blk_cnt + (size_t)blockIdx.x * F;
-  for (int c = threadIdx.x; c < F; c += blockDim.x) out[c] = (cnt[c >> 1] >> ((c & 1) * 16)) & 0xffffu;
+  uint32_t* out = masks + (size_t)blockIdx.x * F;
+  for (int q = threadIdx.x; q < F; q += 256) out[q] = m[q];
 }
 
-__global__ __launch_bounds__(256) void csc_coltotal(const int32_t* __restrict__ blk_cnt, int nrb, int F,
-                                                    int32_t* __restrict__ col_ptr) {
-  const int c = blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= F) return;
+// Per column: rel[b][c] = entries of column c in blocks before b, and the
+// column's total into col_ptr[c]. A workgroup takes 64 columns; its 16 waves
+// each sum a sixteenth of the blocks (popcounts kept in registers, 8 loads in
+// flight), then add the sixteenths before theirs.
+constexpr int kColpreWaves = 16;
+__global__ __launch_bounds__(64 * kColpreWaves) void csc_colpre(const uint32_t* __restrict__ masks, int nrb, int F,
+                                                                int32_t* __restrict__ rel,
+                                                                int32_t* __restrict__ col_ptr) {
+  __shared__ int32_t part[kColpreWaves][64];
+  const int lane = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int c = blockIdx.x * 64 + lane;
+  const int b0 = (int)((int64_t)nrb * q / kColpreWaves), b1 = (int)((int64_t)nrb * (q + 1) / kColpreWaves);
   int32_t s = 0;
-#pragma unroll 8
-  for (int b = 0; b < nrb; ++b) s += blk_cnt[(size_t)b * F + c];
-  col_ptr[c] = s;
-}
-
-__global__ __launch_bounds__(1024) void csc_colscan(int32_t* col_ptr, int F) {
-  __shared__ int32_t part[1024];
-  const int tid = threadIdx.x;
-  const int chunk = (F + 1023) / 1024;
-  const int b = min(F, tid * chunk), en = min(F, b + chunk);
-  int32_t s = 0;
-  for (int c = b; c < en; ++c) s += col_ptr[c];
-  part[tid] = s;
-  __syncthreads();
-  block_exclusive_scan(part, tid);
-  int32_t run = part[tid] - s;
-  for (int c = b; c < en; ++c) {
-    const int32_t v = col_ptr[c];
-    col_ptr[c] = run;
-    run += v;
-  }
-  if (tid == 1023) col_ptr[F] = part[1023];
-}
-
-__global__ __launch_bounds__(256) void csc_offsets(int32_t* __restrict__ blk_cnt, const int32_t* __restrict__ col_ptr,
-                                                   int nrb, int F) {
-  const int c = blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= F) return;
-  int32_t run = col_ptr[c];
-  for (int b = 0; b < nrb; ++b) {
-    const int32_t v = blk_cnt[(size_t)b * F + c];
-    blk_cnt[(size_t)b * F + c] = run;
-    run += v;
-  }
-}
-
-// One wave per row block walks its rows in order; the entries of one row have
-// distinct columns, so their ranks come from one atomic each without any
-// ordering ambiguity, and each column receives its rows in ascending order.
-__global__ __launch_bounds__(64) void csc_fill(const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ pair_col,
-                                               const int32_t* __restrict__ blk_off, int64_t N, int F,
-                                               int32_t* __restrict__ csc_pair, int32_t* __restrict__ csc_row) {
-  extern __shared__ uint32_t cnt[];
-  const int nw = (F + 1) / 2;
-  for (int q = threadIdx.x; q < nw; q += 64) cnt[q] = 0;
-  __syncthreads();
-  const int64_t r0 = (int64_t)blockIdx.x * RB, r1 = min(N, r0 + RB);
-  const int32_t* off = blk_off + (size_t)blockIdx.x * F;
-  for (int64_t r = r0; r < r1; ++r) {
-    const int32_t e = row_ptr[r + 1];
-    for (int32_t p = row_ptr[r] + threadIdx.x; p < e; p += 64) {
-      const int c = pair_col[p];
-      const int sh = (c & 1) * 16;
-      const uint32_t old = atomicAdd(&cnt[c >> 1], 1u << sh);
-      const int32_t pos = off[c] + (int32_t)((old >> sh) & 0xffffu);
-      csc_pair[pos] = p;
-      csc_row[pos] = (int32_t)r;
+  if (c < F) {
+    int b = b0;
+    for (; b + 8 <= b1; b += 8) {
+      uint32_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = masks[(size_t)(b + u) * F + c];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += __popc(v[u]);
     }
-    __syncthreads();
+    for (; b < b1; ++b) s += __popc(masks[(size_t)b * F + c]);
   }
+  part[q][lane] = s;
+  __syncthreads();
+  int32_t run = 0;
+  for (int k = 0; k < q; ++k) run += part[k][lane];
+  if (c >= F) return;
+  for (int b = b0; b < b1; ++b) {
+    rel[(size_t)b * F + c] = run;
+    run += __popc(masks[(size_t)b * F + c]);
+  }
+  if (q == kColpreWaves - 1) col_ptr[c] = run;
+}
+
+// col_ptr[0..F) -> exclusive offsets, col_ptr[F] = total (one workgroup,
+// C consecutive columns per thread).
+template <int C>
+__global__ __launch_bounds__(1024) void csc_colscan(int32_t* col_ptr, int F) {
+  __shared__ int32_t wsum[16];
+  const int b = threadIdx.x * C;
+  int32_t v[C];
+  int32_t s = 0;
+#pragma unroll
+  for (int k = 0; k < C; ++k) {
+    v[k] = b + k < F ? col_ptr[b + k] : 0;
+    s += v[k];
+  }
+  int32_t tot;
+  int32_t run = block_excl_1024(s, wsum, &tot);
+#pragma unroll
+  for (int k = 0; k < C; ++k) {
+    if (b + k < F) col_ptr[b + k] = run;
+    run += v[k];
+  }
+  if (threadIdx.x == 0) col_ptr[F] = tot;
+}
+
+__global__ __launch_bounds__(256) void csc_fill(const int32_t* __restrict__ row_ptr,
+                                                const int32_t* __restrict__ pair_col,
+                                                const uint32_t* __restrict__ masks, const int32_t* __restrict__ rel,
+                                                const int32_t* __restrict__ col_ptr, int64_t N, int F,
+                                                int32_t* __restrict__ csc_pair, int32_t* __restrict__ csc_row) {
+  const int64_t r0 = (int64_t)blockIdx.x * RB, r1 = min(N, r0 + RB);
+  const size_t bo = (size_t)blockIdx.x * F;
+  csc_block_rows(row_ptr, pair_col, r0, r1, [&](int32_t p, int c, int r) {
+    const int32_t pos = col_ptr[c] + rel[bo + c] + __popc(masks[bo + c] & ((1u << r) - 1u));
+    csc_pair[pos] = p;
+    csc_row[pos] = (int32_t)(r0 + r);
+  });
 }
 
 // --------------------------------------------------------------- weight gradients
@@ -538,13 +567,24 @@ __global__ __launch_bounds__(256) void bwd_dw(BwdArgs a, int G8, int64_t cblocks
 
 // Column transpose of the records (stable: rows ascend within a column).
 hipError_t launch_csc(const BwdArgs& a, hipStream_t s, int nrb) {
-  const size_t lds = (size_t)((a.F + 1) / 2) * 4;
-  TWELL_LAUNCH("csc_hist", csc_hist, dim3(nrb), 256, lds, s, a.ws.row_ptr, a.ws.pair_col, a.N, a.F, a.ws.blk_cnt);
-  TWELL_LAUNCH("csc_coltotal", csc_coltotal, dim3((a.F + 255) / 256), 256, 0, s, a.ws.blk_cnt, nrb, a.F, a.ws.col_ptr);
-  TWELL_LAUNCH("csc_colscan", csc_colscan, 1, 1024, 0, s, a.ws.col_ptr, a.F);
-  TWELL_LAUNCH("csc_offsets", csc_offsets, dim3((a.F + 255) / 256), 256, 0, s, a.ws.blk_cnt, a.ws.col_ptr, nrb, a.F);
-  TWELL_LAUNCH("csc_fill", csc_fill, dim3(nrb), 64, lds, s, a.ws.row_ptr, a.ws.pair_col, a.ws.blk_cnt, a.N, a.F,
-               a.ws.csc_pair, a.ws.csc_row);
+  if (a.F > kMaxTransposeF) return hipErrorInvalidValue;
+  uint32_t* masks = reinterpret_cast<uint32_t*>(a.ws.blk_cnt);
+  int32_t* rel = a.ws.blk_cnt + (size_t)nrb * a.F;
+  if (a.F <= 8192)
+    TWELL_LAUNCH("csc_mask", csc_mask<8192>, dim3(nrb), 256, 0, s, a.ws.row_ptr, a.ws.pair_col, a.N, a.F, masks);
+  else if (a.F <= 16384)
+    TWELL_LAUNCH("csc_mask", csc_mask<16384>, dim3(nrb), 256, 0, s, a.ws.row_ptr, a.ws.pair_col, a.N, a.F, masks);
+  else
+    TWELL_LAUNCH("csc_mask", csc_mask<kMaxTransposeF>, dim3(nrb), 256, 0, s, a.ws.row_ptr, a.ws.pair_col, a.N, a.F,
+                 masks);
+  TWELL_LAUNCH("csc_colpre", csc_colpre, dim3((a.F + 63) / 64), 64 * kColpreWaves, 0, s, masks, nrb, a.F, rel,
+               a.ws.col_ptr);
+  if (a.F <= 8192)
+    TWELL_LAUNCH("csc_colscan", csc_colscan<8>, 1, 1024, 0, s, a.ws.col_ptr, a.F);
+  else
+    TWELL_LAUNCH("csc_colscan", csc_colscan<32>, 1, 1024, 0, s, a.ws.col_ptr, a.F);
+  TWELL_LAUNCH("csc_fill", csc_fill, dim3(nrb), 256, 0, s, a.ws.row_ptr, a.ws.pair_col, masks, rel, a.ws.col_ptr,
+               a.N, a.F, a.ws.csc_pair, a.ws.csc_row);
   return hipGetLastError();
 }
 

@@ -402,7 +402,7 @@ twell_status twell_ffn_bwd(const twell_dims* dims, twell_dtype dtype, const twel
   TWELL_CHECK_PTR(dw_gate_t, (size_t)s.F * s.D * 4, "dw_gate_t");
   TWELL_CHECK_PTR(dw_up_t, (size_t)s.F * s.D * 4, "dw_up_t");
   TWELL_CHECK_PTR(dw_down, (size_t)s.F * s.D * 4, "dw_down");
-  if (s.F > 32768)  // the column transpose keeps 16-bit counters for every column in LDS
+  if (s.F > 32768)  // the column transpose keeps a 32-bit row mask for every column in LDS
     return fail(TWELL_ERR_UNSUPPORTED, "twell_ffn_bwd supports d_ff <= 32768");
   if (!(l1_lambda == l1_lambda) || l1_lambda - l1_lambda != 0.f)
     return fail(TWELL_ERR_INVALID_ARG, "l1_lambda must be finite");

@@ -7,7 +7,7 @@ namespace twell {
 
 namespace {
 constexpr int kChunk = 512;  // must match kDenseChunk of the kernels
-constexpr int kRows = 64;    // must match kTransposeRows of the kernels
+constexpr int kRows = 32;    // must match kTransposeRows of the kernels
 
 size_t align_up(size_t v) { return (v + kWsAlign - 1) / kWsAlign * kWsAlign; }
 }  // namespace
@@ -128,7 +128,7 @@ BwdLayout bwd_layout(const Shape& s) {
   L.csc_pair = take(nnz * 4);
   L.csc_row = take(nnz * 4);
   L.col_ptr = take(((size_t)s.F + 1) * 4);
-  L.blk_cnt = take((size_t)s.nrb * s.F * 4);
+  L.blk_cnt = take((size_t)2 * s.nrb * s.F * 4);
   L.grp_off = take((size_t)s.dense_cap * s.G * 4);
   L.egrp = take(((size_t)(s.F + 511) / 512 + 1) * s.N * 4);
   const bool dm = bwd_dense_mfma(s);

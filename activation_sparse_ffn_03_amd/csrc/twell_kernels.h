@@ -10,8 +10,9 @@ namespace twell {
 // Width of the column chunks that dense (overflow / backup) rows are split
 // into so that one long row is spread over many waves.
 constexpr int kDenseChunk = 512;
-// Rows per block of the deterministic column transpose.
-constexpr int kTransposeRows = 64;
+// Rows per block of the deterministic column transpose (one bit of a 32-bit
+// mask each).
+constexpr int kTransposeRows = 32;
 
 // Ascending list of the rows whose flag is set (single-workgroup
 // deterministic scan). Writes rows[0:min(count,cap)], *n_out = count and
@@ -161,7 +162,7 @@ struct BwdWorkspace {
   int32_t* csc_pair;   // [nnz_max]
   int32_t* csc_row;    // [nnz_max]
   int32_t* col_ptr;    // [F+1]
-  int32_t* blk_cnt;    // [n_rb][F]
+  int32_t* blk_cnt;    // [2][n_rb][F]: per row block and column the row mask, then the column's earlier count
   int32_t* grp_off;    // [dense_cap][G]
   int32_t* egrp;       // [ceil(F / 512) + 1][N] ELL position of each row's first entry per 512-column group
   // dense-backup rows on the matrix cores (bf16, d_model a multiple of 128; else null):

@@ -223,7 +223,7 @@ hipError_t launch_ffn_bwd(const BwdArgs& a, hipStream_t) {
   extent(a.ws.csc_pair, nnz * 4, "ws.csc_pair");
   extent(a.ws.csc_row, nnz * 4, "ws.csc_row");
   extent(a.ws.col_ptr, (F + 1) * 4, "ws.col_ptr");
-  extent(a.ws.blk_cnt, nrb * F * 4, "ws.blk_cnt");
+  extent(a.ws.blk_cnt, 2 * nrb * F * 4, "ws.blk_cnt");
   extent(a.ws.grp_off, dc * G * 4, "ws.grp_off");
   extent(a.ws.egrp, ((F + 511) / 512 + 1) * N * 4, "ws.egrp");
   if (a.ws.dza != nullptr) {
