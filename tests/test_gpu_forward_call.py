@@ -35,6 +35,8 @@ def _same(a, b, what):
     ("c2", dict(N=33, D=512, F=700), dict(tile_n=64, slots=64), True),  # narrower tiles, F ragged
     ("c4", dict(N=300, D=512, F=2048), dict(slots=8, ovf_cap=16), False),  # overflow beyond capacity
     ("c5", dict(N=500, D=256, F=1024), dict(slots=8), False),          # training: a_save as well
+    ("c5", dict(N=8000, D=256, F=8100), dict(slots=8), False),         # 16 x 16 blocks: blocked up projection,
+                                                                         # flags and list before the fork, a_save
 ])
 def test_combined_call_matches_separate_calls(name, kw, extra, small):
     w = make_inputs(name, **kw)

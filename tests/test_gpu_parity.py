@@ -233,6 +233,23 @@ def test_forward_deterministic():
     assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
 
 
+def test_blocked_paths_deterministic():
+    """16 x 16 blocks of 512 tokens x 512 columns: the blocked up projection
+    and the blocked dz, the overflow and dense-backup rows on the matrix cores
+    and the split side-stream joins, run twice, agree bit for bit."""
+    w = _train_case(N=8000, D=256, F=8100, K=400)
+    pl = Pipeline(w, dense_cap=1024, slots=8, ovf_cap=1024)
+    y1 = pl.forward().clone()
+    a = [v.clone() for v in pl.backward()]
+    assert int(pl.ffn.pack.status.item()) == 0 and int(pl.ffn.hyb.status.item()) == 0
+    assert int(pl.ffn.pack.n_ovf.item()) > 64 and int(pl.ffn.hyb.n_dense.item()) > 64
+    y2 = pl.forward().clone()
+    b = [v.clone() for v in pl.backward()]
+    assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+    for u, v in zip(a, b):
+        assert torch.equal(u.view(torch.int32), v.view(torch.int32))
+
+
 # ------------------------------------------------------------------ training: routing + backward
 
 def _train_case(N=1536, D=256, F=1024, K=24, seed=0, **kw):
