@@ -175,6 +175,11 @@ def test_ovf_rows_match_epilogue_values():
                                                           # passes of 64 rows, ragged last d_ff chunk
     ("c2", dict(N=8000, D=192, F=8100), {}),             # 16 x 16 blocks of 512 tokens x 4 tiles: the blocked
                                                           # up projection, ragged last token block and tile
+    ("c2", dict(N=8008, D=1024, F=8100), {}),            # blocked up projection at d_model 1024, ragged
+                                                          # last token block and tile
+    ("c4", dict(N=8008, D=1024, F=8100), dict(slots=8)),  # the same with lognormal rows and overflow rows
+    ("c3", dict(N=8008, D=1024, F=8100, density=0.05), dict(slots=16)),  # 5 % density: several passes of
+                                                          # the blocked up projection's entry list
     ("c2", dict(N=300, D=2048, F=8448), {}),             # W_up block per XCD > 4 MB: two d_model passes
     ("c1", dict(N=200, D=1024, F=8448), {}),             # the same in fp32
 ])
@@ -229,6 +234,17 @@ def test_forward_deterministic():
     y1 = pl.forward().clone()
     assert int(pl.ffn.pack.status.item()) == 0
     assert int(pl.ffn.pack.n_ovf.item()) > 0
+    y2 = pl.forward().clone()
+    assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+
+
+def test_skewed_blocked_forward_deterministic():
+    """Lognormal rows with overflow rows through the blocked up projection and
+    the MFMA overflow-row products: the same y bit for bit."""
+    w = make_inputs("c4", N=8008, D=1024, F=8100)
+    pl = Pipeline(w, slots=8)
+    y1 = pl.forward().clone()
+    assert int(pl.ffn.pack.status.item()) == 0
     y2 = pl.forward().clone()
     assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
 
