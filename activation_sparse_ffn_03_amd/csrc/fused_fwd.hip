@@ -238,6 +238,10 @@ __global__ __launch_bounds__(256) void ffn_down_kernel(FwdArgs a, int G8, int64_
   int p;
   int64_t rb;
   slice_block(blockIdx.x, G8, tblocks, p, rb);
+  if (a.rb_order) {  // heaviest blocks first (the whole batch in one launch)
+    rb = a.rb_order[rb];
+    if ((uint64_t)rb >= (uint64_t)tblocks) return;
+  }
   const int64_t i = i0 + rb * 4 + (threadIdx.x >> 6);
   if (i >= i1) return;
   const int D = a.D;
@@ -395,9 +399,13 @@ hipError_t launch_sparse_rows(const FwdArgs& a, hipStream_t s, int64_t chunk) {
     const int64_t tblocks = (i1 - i0 + 3) / 4;
     const dim3 gup((unsigned)(tblocks * parts * a.up_nq));
     const bool small = i1 - i0 <= kSmallRows;
+    FwdArgs b = a;  // the down launch's arguments: natural block order unless set below
+    b.rb_order = nullptr;
     if (sizeof(TS) == 2 && chunk == a.N && up_blocked_applies(a)) {
-      // large batches: token blocks x tile groups through LDS (up_blocked.hip)
+      // large batches: token blocks x tile groups through LDS (up_blocked.hip),
+      // which also orders the down projection's blocks
       if ((err = launch_up_blocked(a, s)) != hipSuccess) return err;
+      if (down_order_applies(a)) b.rb_order = a.rb_order;
     } else {
 #define TWELL_UP(MM)                                                                                          \
   case MM:                                                                                                    \
@@ -420,9 +428,9 @@ hipError_t launch_sparse_rows(const FwdArgs& a, hipStream_t s, int64_t chunk) {
     const dim3 gdn((unsigned)(tblocks * P));
 #define TWELL_DOWN(E, R)                                                                                    \
   if (small)                                                                                                \
-    TWELL_LAUNCH("ffn_down_kernel", (ffn_down_kernel<TS, E, R, true>), gdn, blk, 0, s, a, G8, tblocks, i0, i1); \
+    TWELL_LAUNCH("ffn_down_kernel", (ffn_down_kernel<TS, E, R, true>), gdn, blk, 0, s, b, G8, tblocks, i0, i1); \
   else                                                                                                      \
-    TWELL_LAUNCH("ffn_down_kernel", (ffn_down_kernel<TS, E, R, false>), gdn, blk, 0, s, a, G8, tblocks, i0, i1)
+    TWELL_LAUNCH("ffn_down_kernel", (ffn_down_kernel<TS, E, R, false>), gdn, blk, 0, s, b, G8, tblocks, i0, i1)
     if constexpr (sizeof(TS) == 2) {
       TWELL_SLICED_CASES(8, TWELL_DOWN)
     } else {

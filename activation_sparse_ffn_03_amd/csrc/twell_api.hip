@@ -286,6 +286,9 @@ static twell_status fwd_prepare(const twell::Shape& s, const twell_sizes& z, twe
     a.part = reinterpret_cast<float*>(base + L.part);
     a.zov = reinterpret_cast<uint16_t*>(base + L.zov);
     a.gbase = reinterpret_cast<int32_t*>(base + L.gbase);
+    a.rb_order = reinterpret_cast<int32_t*>(base + L.rb_order);
+    a.rb_code = reinterpret_cast<int32_t*>(base + L.rb_code);
+    a.rb_hist = reinterpret_cast<int32_t*>(base + L.rb_hist);
   }
   *out = a;
   return TWELL_OK;

@@ -106,7 +106,11 @@ FwdLayout fwd_layout(const Shape& s) {
   L.zov = L.part + align_up((size_t)s.ovf_cap * s.G * s.D * 4);
   L.gbase = L.zov + (s.esz == 2 ? align_up((size_t)2 * s.ovf_cap * dense_z_stride(s.F) * 2) : 0);
   const size_t groups = (size_t)(s.n_tiles + kUpGroupTiles - 1) / kUpGroupTiles;
-  L.total = L.gbase + groups * (size_t)s.N * 4;
+  const size_t nrb4 = ((size_t)s.N + 3) / 4, nwg = ((size_t)s.N + 255) / 256;
+  L.rb_order = L.gbase + align_up(groups * (size_t)s.N * 4);
+  L.rb_code = L.rb_order + align_up(nrb4 * 4);
+  L.rb_hist = L.rb_code + align_up(nrb4 * 4);
+  L.total = L.rb_hist + nwg * 16 * 4;
   return L;
 }
 

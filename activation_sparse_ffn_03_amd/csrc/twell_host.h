@@ -53,9 +53,11 @@ int up_passes(const Shape& s);
 // partials; then, for bf16 storage, the overflow rows' z = h*a as bf16 high
 // and low parts ([2][ovf_cap][dense_z_stride(F)] uint16); then the list
 // position of each kUpGroupTiles-tile group's first entry
-// ([ceil(n_t / kUpGroupTiles)][N] int32).
+// ([ceil(n_t / kUpGroupTiles)][N] int32); then the down projection's order of
+// 4-row blocks ([ceil(N/4)] int32), each block's class code ([ceil(N/4)]
+// int32) and the per-workgroup class counts ([ceil(N/256)][16] int32).
 struct FwdLayout {
-  size_t offs, zlist, upart, uslot, part, zov, gbase, total;
+  size_t offs, zlist, upart, uslot, part, zov, gbase, rb_order, rb_code, rb_hist, total;
 };
 // Row stride (elements) of the overflow rows' z: d_ff rounded up to 32, so
 // every 32-column block of a row lies inside it and rows stay 64-byte aligned.

@@ -88,6 +88,11 @@ struct FwdArgs {
   float* part;    // [ovf_cap][G][D] fp32 partial outputs of dense-row chunks (workspace)
   uint16_t* zov;  // bf16: [2][ovf_cap][dense_z_stride(F)] high / low bf16 parts of the overflow rows' z (workspace)
   int32_t* gbase; // [ceil(n_t / kUpGroupTiles)][N]: list position of each tile group's first entry (workspace)
+  // order of the down projection's 4-row blocks, heaviest first (large bf16
+  // batches; null: natural order) and what up_rows leaves for it (workspace)
+  int32_t* rb_order;  // [ceil(N / 4)]
+  int32_t* rb_code;   // [ceil(N / 4)]: weight class << 16 | rank among its workgroup's blocks of that class
+  int32_t* rb_hist;   // [ceil(N / 256)][16]: blocks of each class per up_rows workgroup
 };
 
 hipError_t launch_ffn_fwd(const FwdArgs& a, hipStream_t s);
@@ -95,6 +100,9 @@ hipError_t launch_ffn_fwd(const FwdArgs& a, hipStream_t s);
 // (up_blocked.hip): list lengths and group positions, then z and a_save.
 bool up_blocked_applies(const FwdArgs& a);
 hipError_t launch_up_blocked(const FwdArgs& a, hipStream_t s);
+// launch_up_blocked also orders the down projection's 4-row blocks (a.rb_order,
+// heaviest first) when this holds.
+bool down_order_applies(const FwdArgs& a);
 // Overflow rows of bf16 layers as two skinny MFMA products (dense_rows.hip):
 // z = h * (X_o . W_up^T), then z . W_down in d_ff chunks and dense_reduce.
 bool dense_mfma_applies(const FwdArgs& a);

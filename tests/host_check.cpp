@@ -128,6 +128,9 @@ static void fwd_extents(const FwdArgs& a) {
   extent(a.offs, N * 4, "ws.offs");
   extent(a.gbase, (nt + kUpGroupTiles - 1) / kUpGroupTiles * N * 4, "ws.gbase");
   extent(a.zlist, N * L * 8, "ws.zlist");
+  extent(a.rb_order, (N + 3) / 4 * 4, "ws.rb_order");
+  extent(a.rb_code, (N + 3) / 4 * 4, "ws.rb_code");
+  extent(a.rb_hist, (N + 255) / 256 * 16 * 4, "ws.rb_hist");
   CHECK(a.up_nq >= 1 && D % (size_t)a.up_nq == 0, "up_nq %d does not divide d_model", a.up_nq);
   if (a.up_nq > 1) {
     extent(a.upart, (size_t)a.up_nq * N * L * 4, "ws.upart");
