@@ -14,9 +14,9 @@
 //
 // up_rows, a small pass before, gives every token its list length (-1 for an
 // overflow row, which the dense-row path handles) and the list position of
-// each tile group's first entry; down_order turns its per-block weight
-// classes into the down projection's block order (heaviest first, so the
-// longest lists of a skewed batch do not start last and make the tail).
+// each tile group's first entry, and with order_blocks the down projection's
+// heaviest-first order of 4-row blocks (block_order.h).
+#include "block_order.h"
 #include "blocked_sddmm.h"
 #include "row_ops.h"
 #include "twell_host.h"
@@ -29,16 +29,12 @@ namespace {
 constexpr int kTG = kUpGroupTiles;
 
 // Thread per token: list length (offs, -1 for an overflow row) and the list
-// position of every kTG-tile group's first entry (gbase). With rb_code set,
-// also the down projection's weight class of each 4-row block (the bit length
-// of its longest list, overflow rows counting 0) with its rank among the
-// workgroup's blocks of that class, and the workgroup's count per class.
-constexpr int kClasses = 16;
-
+// position of every kTG-tile group's first entry (gbase); with rb_code set,
+// also the down projection's block classes (block_order.h; overflow rows
+// weigh nothing, the dense-row path takes them).
 __global__ __launch_bounds__(256) void up_rows(const uint16_t* __restrict__ counts, int64_t N, int n_tiles, int slots,
                                                int32_t* __restrict__ offs, int32_t* __restrict__ gbase,
                                                int32_t* __restrict__ rb_code, int32_t* __restrict__ rb_hist) {
-  __shared__ int cls[64];
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   int len = 0;
   if (i < N) {
@@ -54,91 +50,7 @@ __global__ __launch_bounds__(256) void up_rows(const uint16_t* __restrict__ coun
     offs[i] = ovf ? -1 : run;
     len = ovf ? 0 : run;
   }
-  if (rb_code == nullptr) return;  // uniform: no barrier below is reached
-  len = max(len, __shfl_xor(len, 1, 64));
-  len = max(len, __shfl_xor(len, 2, 64));
-  if ((threadIdx.x & 3) == 0) cls[threadIdx.x >> 2] = min(len == 0 ? 0 : 32 - __clz(len), kClasses - 1);
-  __syncthreads();
-  const int64_t n_rb = (N + 3) / 4;
-  const int t = threadIdx.x;
-  if (t < 64 && (int64_t)blockIdx.x * 64 + t < n_rb) {
-    const int c = cls[t];
-    int r = 0;
-    for (int u = 0; u < t; ++u) r += cls[u] == c;
-    rb_code[(size_t)blockIdx.x * 64 + t] = (c << 16) | r;
-  }
-  if (t < kClasses) {
-    int n = 0;
-    for (int u = 0; u < 64 && (int64_t)blockIdx.x * 64 + u < n_rb; ++u) n += cls[u] == t;
-    rb_hist[(size_t)blockIdx.x * kClasses + t] = n;
-  }
-}
-
-// One workgroup: the down projection's order of 4-row blocks, heavier classes
-// first, within a class by up_rows workgroup, then by rank (deterministic).
-// Thread w < n_wg scans the class counts of up_rows workgroup w into LDS
-// offsets; then every thread places blocks t, t + 1024, ...
-constexpr int kOrderWgs = 1024;  // up_rows workgroups one ordering workgroup handles
-
-__global__ __launch_bounds__(1024) void down_order(int64_t N, const int32_t* __restrict__ rb_code,
-                                                   const int32_t* __restrict__ rb_hist, int32_t* __restrict__ rb_order) {
-  __shared__ int wtot[16][kClasses];
-  __shared__ int base[kClasses];
-  __shared__ int woff[kOrderWgs][kClasses];
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int64_t n_rb = (N + 3) / 4;
-  const int n_wg = (int)((N + 255) / 256);
-  int h[kClasses], x[kClasses];
-#pragma unroll
-  for (int c = 0; c < kClasses; ++c) {
-    h[c] = t < n_wg ? rb_hist[(size_t)t * kClasses + c] : 0;
-    x[c] = h[c];
-  }
-  // inclusive scan over the threads, per class: within the wave, then over waves
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1)
-#pragma unroll
-    for (int c = 0; c < kClasses; ++c) {
-      const int y = __shfl_up(x[c], off, 64);
-      if (lane >= off) x[c] += y;
-    }
-  if (lane == 63)
-#pragma unroll
-    for (int c = 0; c < kClasses; ++c) wtot[wave][c] = x[c];
-  __syncthreads();
-  if (t < kClasses) {  // blocks of heavier classes come first
-    int tot = 0;
-    for (int c2 = kClasses - 1; c2 > t; --c2)
-      for (int w = 0; w < 16; ++w) tot += wtot[w][c2];
-    base[t] = tot;
-  }
-  __syncthreads();
-  if (t < n_wg) {
-#pragma unroll
-    for (int c = 0; c < kClasses; ++c) {
-      int before = 0;
-      for (int w = 0; w < wave; ++w) before += wtot[w][c];
-      woff[t][c] = base[c] + before + x[c] - h[c];
-    }
-  }
-  __syncthreads();
-  constexpr int U = 4;  // blocks whose codes are loaded together
-  for (int64_t rb0 = t; rb0 < n_rb; rb0 += (int64_t)U * 1024) {
-    int code[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t rb = rb0 + (int64_t)u * 1024;
-      code[u] = rb < n_rb ? rb_code[rb] : 0;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t rb = rb0 + (int64_t)u * 1024;
-      if (rb < n_rb) {
-        const int64_t dst = (int64_t)woff[rb / 64][code[u] >> 16] + (code[u] & 0xffff);
-        if (dst < n_rb) rb_order[dst] = (int32_t)rb;  // a permutation: every position written once
-      }
-    }
-  }
+  if (rb_code != nullptr) blkord::block_classes(len, N, rb_code, rb_hist);  // uniform branch
 }
 
 // The forward's pattern: the packed TwELL entries of the non-overflow rows,
@@ -191,7 +103,7 @@ bool up_blocked_applies(const FwdArgs& a) {
 // The ordering kernel has one thread per up_rows workgroup.
 bool down_order_applies(const FwdArgs& a) {
   return up_blocked_applies(a) && a.rb_order != nullptr && a.rb_code != nullptr && a.rb_hist != nullptr &&
-         (a.N + 255) / 256 <= kOrderWgs;
+         blkord::order_fits(a.N);
 }
 
 hipError_t launch_up_blocked(const FwdArgs& a, hipStream_t s) {
@@ -202,7 +114,7 @@ hipError_t launch_up_blocked(const FwdArgs& a, hipStream_t s) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (order) {
-    TWELL_LAUNCH("down_order", down_order, 1, 1024, 0, s, a.N, a.rb_code, a.rb_hist, a.rb_order);
+    TWELL_LAUNCH("order_blocks", blkord::order_blocks, 1, 1024, 0, s, a.N, a.rb_code, a.rb_hist, a.rb_order);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
   const int n_groups = (a.n_tiles + kTG - 1) / kTG;
