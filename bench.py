@@ -246,7 +246,7 @@ KERNEL_SOURCES = {
     "quantize_e4m3": ["quant.hip", "twell_device.h"],
     "ffn_up_kernel": ["fused_fwd.hip", "row_ops.h", "twell_device.h"],
     "ffn_up_blocked": ["up_blocked.hip", "blocked_sddmm.h", "row_ops.h", "twell_device.h"],
-    "ffn_down_kernel": ["fused_fwd.hip", "row_ops.h", "twell_device.h"],
+    "ffn_down_kernel": ["fused_fwd.hip", "block_order.h", "row_ops.h", "twell_device.h"],
     "bwd_dz_ell": ["bwd.hip", "row_ops.h", "twell_device.h"],
     "bwd_dz_blocked": ["bwd_blocked.hip", "blocked_sddmm.h", "twell_device.h"],
     "bwd_dx": ["bwd.hip", "row_ops.h", "twell_device.h"],
