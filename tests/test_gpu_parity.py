@@ -175,6 +175,8 @@ def test_ovf_rows_match_epilogue_values():
                                                           # passes of 64 rows, ragged last d_ff chunk
     ("c2", dict(N=8000, D=192, F=8100), {}),             # 16 x 16 blocks of 512 tokens x 4 tiles: the blocked
                                                           # up projection, ragged last token block and tile
+    ("c4", dict(N=8002, D=192, F=8100), dict(slots=8)),  # lognormal rows in heaviest-first 4-row blocks,
+                                                          # the last block half full
     ("c2", dict(N=8008, D=1024, F=8100), {}),            # blocked up projection at d_model 1024, ragged
                                                           # last token block and tile
     ("c4", dict(N=8008, D=1024, F=8100), dict(slots=8)),  # the same with lognormal rows and overflow rows
