@@ -21,7 +21,10 @@ def dev(a, dtype: str):
 
 
 def f64(t: torch.Tensor) -> np.ndarray:
-    return t.detach().float().cpu().numpy().astype(np.float64)
+    # Unused TwELL slots and ELL positions keep whatever the buffer held (any
+    # bit pattern, NaNs included); callers compare valid entries only.
+    with np.errstate(invalid="ignore"):
+        return t.detach().float().cpu().numpy().astype(np.float64)
 
 
 def u16(t: torch.Tensor) -> np.ndarray:
