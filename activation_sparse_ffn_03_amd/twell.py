@@ -418,15 +418,16 @@ class TwellFFN:
         return self.y
 
     def capture_supported(self) -> bool:
-        """False on the one forward path whose graph capture is not cleared:
-        bf16 gate GEMM (not FP8, not the small-batch GEMV) with d_model above
-        2048 and rows that can overflow. There the overflow rows' gate rows
-        run as a separate GEMM before the up / down projection and the
-        overflow rows' products on the library's side stream; one process
-        that captured and replayed that forward (8192 x 4096 x 14336, skewed
-        density, overflow rows present) printed its results and then aborted
-        at exit in glibc (free(): invalid pointer) with no GPU fault, and the
-        cause has not been found. Eager calls of the same path are unaffected."""
+        """False on the one class of forwards whose graph capture is not
+        cleared: bf16 gate GEMM (not FP8, not the small-batch GEMV) with
+        d_model above 2048 and rows that can overflow. One process that
+        captured and replayed such a forward (8192 x 4096 x 14336, skewed
+        density, overflow rows present; its overflow gate rows then ran as a
+        separate GEMM before the up / down projection, its overflow products
+        on the library's side stream) printed its results and then aborted at
+        exit in glibc (free(): invalid pointer) with no GPU fault. The cause
+        has not been found, so capture stays refused on the whole class.
+        Eager calls are unaffected."""
         d = self.dims
         small = self.ws_gate is not None
         can_overflow = d.slots < d.tile_n and d.ovf_cap > 0
