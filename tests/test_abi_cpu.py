@@ -119,6 +119,45 @@ def test_new_calls_validate_before_touching_the_device():
     assert L.twell_gate_pack_fp8(ctypes.byref(d), fake, fake, fake, None, fake, ctypes.byref(p), None, None) == 1
 
 
+def test_zero_tokens_is_a_no_op_on_every_entry_point():
+    """N == 0 (twell.h, dims): every call validates its arguments and returns
+    TWELL_OK without enqueueing anything, so it needs no device (the pointers
+    here are never dereferenced). Workspaces are still checked against
+    twell_query_sizes, which for N == 0 asks for nothing in the forward."""
+    L = tw.lib()
+    fake = ctypes.c_void_p(0x100000)
+    d = tw.make_dims(0, 256, 1000, 128, 16, 64, 8, 8)
+    z = tw.query_sizes(d, tw.BF16)
+    assert z["ws_fwd"] == 0 and z["ws_gate"] == 0 and z["a_save"] == 0
+    p = tw.Pack(*([fake] * len(tw.Pack._fields_)))
+    h = tw.Hybrid(*([fake] * len(tw.Hybrid._fields_)))
+    B = ctypes.byref
+    calls = {
+        "gate_pack": lambda: L.twell_gate_pack(B(d), 0, fake, fake, fake, B(p), None, None),
+        "gate_pack_ws": lambda: L.twell_gate_pack_ws(B(d), 0, fake, fake, fake, B(p), None, None, 0, None),
+        "pack_preact": lambda: L.twell_pack_preact(B(d), 0, fake, fake, B(p), None),
+        "quantize_e4m3": lambda: L.twell_quantize_e4m3(0, 8, 0, fake, fake, fake, None),
+        "gate_pack_fp8": lambda: L.twell_gate_pack_fp8(B(d), fake, fake, fake, fake, fake, B(p), None, None),
+        "gate_pack_fp8_ws": lambda: L.twell_gate_pack_fp8_ws(B(d), fake, fake, fake, fake, fake, B(p), None, None,
+                                                             0, None),
+        "ffn_fwd": lambda: L.twell_ffn_fwd(B(d), 0, B(p), fake, fake, fake, fake, None, None, 0, None),
+        "ffn_forward": lambda: L.twell_ffn_forward(B(d), 0, fake, fake, fake, B(p), fake, fake, fake, None, None, 0,
+                                                   None, 0, None),
+        "ffn_forward_fp8": lambda: L.twell_ffn_forward_fp8(B(d), fake, fake, fake, fake, fake, B(p), fake, fake, fake,
+                                                           fake, None, None, 0, None, 0, None),
+        "ffn_forward_noalloc": lambda: L.twell_ffn_forward_noalloc(B(d), 0, fake, fake, fake, B(p), fake, fake, fake,
+                                                                   None, None),
+        "route_hybrid": lambda: L.twell_route_hybrid(B(d), 0, B(p), fake, B(h), None),
+        "ffn_bwd": lambda: L.twell_ffn_bwd(B(d), 0, B(h), fake, fake, fake, fake, fake, ctypes.c_float(1e-4), fake,
+                                           fake, fake, fake, fake, z["ws_bwd"], None),
+    }
+    for name, call in calls.items():
+        assert call() == 0, (name, L.twell_last_error())
+    # the backward's workspace is checked even with no tokens
+    assert L.twell_ffn_bwd(B(d), 0, B(h), fake, fake, fake, fake, fake, ctypes.c_float(1e-4), fake, fake, fake, fake,
+                           fake, z["ws_bwd"] - 1, None) == 3
+
+
 # ---------------------------------------------------------------- header <-> binding marshalling
 
 _C_SCALARS = {"int64_t": ctypes.c_int64, "int32_t": ctypes.c_int32, "int": ctypes.c_int, "twell_dtype": ctypes.c_int,
