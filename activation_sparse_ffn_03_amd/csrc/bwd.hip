@@ -653,6 +653,18 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t s) {
   const dim3 blk(256);
   hipError_t err;
 
+  // The dense-backup rows' dz and a (matrix cores) need only the dense-row
+  // list, so they start on the side stream first, beside the row offsets and
+  // the ELL rows' dz; their records follow once the offsets exist.
+  hipStream_t side = s;
+  const bool dense_mfma = sizeof(TS) == 2 && bwd_dense_mfma_applies(a);
+  if (a.dense_cap > 0 && dense_mfma) {
+    if ((err = fork_side(s, &side)) != hipSuccess) return err;
+    if ((err = launch_bwd_dense_nt(a, side)) != hipSuccess) {
+      (void)join_side(s, side);
+      return err;
+    }
+  }
   if (a.dense_cap > 0) {
     TWELL_LAUNCH("dense_groups", dense_groups<TS>, dim3((a.dense_cap + 3) / 4), blk, 0, s, a, G, dense_nnz);
   }
@@ -667,14 +679,20 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t s) {
   }
 
   // dz records: ELL rows by column part (main stream), dense rows by column
-  // chunk (side stream: disjoint record ranges)
-  hipStream_t side = s;
-  const bool dense_mfma = sizeof(TS) == 2 && bwd_dense_mfma_applies(a);
+  // chunk (side stream: disjoint record ranges), past the row offsets
   if (a.dense_cap > 0) {
-    if ((err = fork_side(s, &side)) != hipSuccess) return err;
+    hipStream_t side2 = s;
+    if ((err = fork_side(s, &side2)) != hipSuccess) {
+      (void)join_side(s, side);
+      return err;
+    }
+    if (side2 != side) {  // not the stream of the first fork: finish that branch first
+      if ((err = join_side(s, side)) != hipSuccess) return err;
+      side = side2;
+    }
     const dim3 gdd((unsigned)(((int64_t)a.dense_cap * G + 3) / 4));
     if (dense_mfma) {
-      err = launch_bwd_dense_dz(a, side);
+      err = launch_bwd_dense_records(a, side);
       if (err != hipSuccess) {
         (void)join_side(s, side);
         return err;

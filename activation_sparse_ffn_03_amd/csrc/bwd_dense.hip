@@ -13,7 +13,8 @@
 // three skinny products that stream each weight once per 64 rows (the same
 // MFMA forms as the forward's overflow rows, skinny_mfma.h):
 //   dense_bwd_nt     a wave per 16 columns: DZ and A over all of d_model
-//                    (fp32, [dense_cap][F] each)
+//                    (fp32, [dense_cap][F] each); it needs only the dense-row
+//                    list, so it can start before the row offsets exist
 //   dense_records    wave per (row, 512-column chunk): the records of the
 //                    active units (column and (z, da, dg)) in CSR order, for
 //                    the weight gradients, and DA, DG as bf16 high / low parts
@@ -129,11 +130,13 @@ bool bwd_dense_mfma_applies(const BwdArgs& a) {
   return a.is_bf16 && a.D % kDownCols == 0 && a.D % 32 == 0 && a.dense_cap > 0 && a.ws.dza != nullptr;
 }
 
-hipError_t launch_bwd_dense_dz(const BwdArgs& a, hipStream_t s) {
-  const int G = (a.F + kDenseChunk - 1) / kDenseChunk;
+hipError_t launch_bwd_dense_nt(const BwdArgs& a, hipStream_t s) {
   TWELL_LAUNCH("dense_bwd_nt", dense_bwd_nt, dim3(skinny_blocks(a.F, kSkinnyUW)), 64 * kSkinnyWaves, 0, s, a);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dense_records(const BwdArgs& a, hipStream_t s) {
+  const int G = (a.F + kDenseChunk - 1) / kDenseChunk;
   const int64_t want = ((int64_t)a.dense_cap * G + 3) / 4;
   TWELL_LAUNCH("dense_records", dense_records, dim3((unsigned)(want < kRecordsGrid ? want : kRecordsGrid)), 256, 0,
                s, a, G, dense_z_stride(a.F));

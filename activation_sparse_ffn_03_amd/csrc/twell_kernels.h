@@ -213,7 +213,8 @@ hipError_t launch_dz_blocked(const BwdArgs& a, hipStream_t s);
 // Dense-backup rows as skinny MFMA products (bwd_dense.hip): dz and a, then
 // their records and da / dg; then dx of those rows (bwd_dx skips them).
 bool bwd_dense_mfma_applies(const BwdArgs& a);
-hipError_t launch_bwd_dense_dz(const BwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_dense_nt(const BwdArgs& a, hipStream_t s);       // dz, a (needs the dense-row list)
+hipError_t launch_bwd_dense_records(const BwdArgs& a, hipStream_t s);  // records, da, dg (needs row_ptr)
 hipError_t launch_bwd_dense_dx(const BwdArgs& a, hipStream_t s);
 
 }  // namespace twell
