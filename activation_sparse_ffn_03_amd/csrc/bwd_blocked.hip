@@ -24,14 +24,15 @@ namespace {
 constexpr int kGroupCols = blk::kGroupCols;
 constexpr int kMaxGroups = 64;  // d_ff up to 32768
 
-// Wave per row (lane = ELL position): egrp[g][i] = ELL position of the first
+// Wave per row (lane = ELL position), each XCD a contiguous run of rows (the
+// [.][N] arrays' lines stay in one L2): egrp[g][i] = ELL position of the first
 // entry of row i with column >= g * 512, for g = 0 .. n_groups (0 everywhere
 // for dense rows). Entry k writes the groups after its predecessor's up to
 // its own; the first position past the row's end writes the rest, so every
 // egrp value is written exactly once.
 __global__ __launch_bounds__(256) void ell_groups(BwdArgs a, int n_groups) {
   const int lane = threadIdx.x & 63;
-  const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t i = xcd_run_block(blockIdx.x, gridDim.x) * 4 + (threadIdx.x >> 6);
   const int64_t N = a.N;
   if (i >= N) return;
   const int n = a.is_dense[i] ? 0 : min(a.row_nnz[i], a.row_cap);

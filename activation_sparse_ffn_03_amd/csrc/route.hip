@@ -12,8 +12,11 @@
 //
 // Kernels
 //   route_rows     wave per row, 16 rows per workgroup (their TwELL slot
-//                  loads share cache lines): row_nnz, is_dense, and the ELL entries of
-//                  ELL rows (vals, global cols, saved a).
+//                  loads share cache lines), each XCD a contiguous run of
+//                  row blocks (a 128-byte line of a [.][N] array spans 64
+//                  or 32 rows; split over XCDs, every L2 fetched it):
+//                  row_nnz, is_dense, and the ELL entries of ELL rows (vals,
+//                  global cols, saved a).
 //   launch_compact ascending dense-row list + capacity status.
 //   route_dense_h  thread per (dense row, column): dense activation rows,
 //                  rebuilt from TwELL slots or copied from the overflow rows.
@@ -52,7 +55,7 @@ constexpr int kRouteBatch = 4;
 template <typename TS>
 __global__ __launch_bounds__(1024) void route_rows(RouteArgs a) {
   const int lane = threadIdx.x & 63;
-  const int64_t i = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 6);
+  const int64_t i = xcd_run_block(blockIdx.x, gridDim.x) * 16 + (threadIdx.x >> 6);
   if (i >= a.N) return;
   const int64_t N = a.N;
   int nnz = 0;

@@ -92,6 +92,14 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Block index of workgroup b of nb such that the workgroups of each XCD (b
+// runs on XCD b % 8) take one contiguous run of blocks.
+__device__ __forceinline__ int64_t xcd_run_block(int64_t b, int64_t nb) {
+  const int x = (int)(b % 8);
+  const int64_t q = nb / 8, r = nb % 8;
+  return x * q + (x < r ? x : r) + b / 8;
+}
+
 // Storage types: raw bf16 bits or fp32.
 template <typename T> struct Store;
 template <> struct Store<uint16_t> {
