@@ -41,7 +41,7 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void dense_bwd_nt(BwdArgs a) {
   (void)skinny_columns<kSkinnyUW>(wu, a.D, a.F, c0, ru);
   const int n = min(*a.n_dense, a.dense_cap);
   const size_t plane = (size_t)a.dense_cap * a.F;
-  for (int m0 = 0; m0 < n; m0 += kRowsPerPass) {
+  for (int m0 = blockIdx.z * kRowsPerPass; m0 < n; m0 += gridDim.z * kRowsPerPass) {
 #pragma unroll
     for (int which = 0; which < 2; ++which) {
       f32x4_t acc[NF][kSkinnyUW];
@@ -131,7 +131,8 @@ bool bwd_dense_mfma_applies(const BwdArgs& a) {
 }
 
 hipError_t launch_bwd_dense_nt(const BwdArgs& a, hipStream_t s) {
-  TWELL_LAUNCH("dense_bwd_nt", dense_bwd_nt, dim3(skinny_blocks(a.F, kSkinnyUW)), 64 * kSkinnyWaves, 0, s, a);
+  TWELL_LAUNCH("dense_bwd_nt", dense_bwd_nt, dim3(skinny_blocks(a.F, kSkinnyUW), 1, kPassSplit), 64 * kSkinnyWaves, 0,
+               s, a);
   return hipGetLastError();
 }
 

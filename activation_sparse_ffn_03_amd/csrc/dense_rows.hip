@@ -70,7 +70,7 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void gate_rows_skinny(const uint
   const uint16_t* wrow[UW];
   if (!skinny_columns<UW>(w, D, F, c0, wrow)) return;
   const int n = min(*n_ptr, cap);
-  for (int m0 = 0; m0 < n; m0 += kRowsPerPass) {
+  for (int m0 = blockIdx.z * kRowsPerPass; m0 < n; m0 += gridDim.z * kRowsPerPass) {
     f32x4_t acc[NF][UW];
     skinny_nt<UW, B>(x, rows, n, m0, wrow, D, acc);
     // 16x16 MFMA result: lane l holds rows 4*(l>>4)+r of column l&15
@@ -106,7 +106,7 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void dense_up_mfma(const uint16_
   const uint16_t* wrow[UW];
   if (!skinny_columns<UW>(w, D, F, c0, wrow)) return;
   const int n = min(*n_ptr, cap);
-  for (int m0 = 0; m0 < n; m0 += kRowsPerPass) {
+  for (int m0 = blockIdx.z * kRowsPerPass; m0 < n; m0 += gridDim.z * kRowsPerPass) {
     f32x4_t acc[NF][UW];
     skinny_nt<UW, B>(x, rows, n, m0, wrow, D, acc);
 #pragma unroll
@@ -151,7 +151,8 @@ bool gate_rows_skinny_applies(int D) { return D % 32 == 0; }
 hipError_t launch_gate_rows_skinny(const uint16_t* x, const uint16_t* w, int D, int F, const int32_t* rows,
                                    const int32_t* n_ovf, int cap, const float* t, uint16_t* ovf_h, hipStream_t s) {
   if (!gate_rows_skinny_applies(D)) return hipErrorInvalidValue;
-  TWELL_LAUNCH("gate_rows_skinny", (gate_rows_skinny<kSkinnyUW, kSkinnyB>), dim3(skinny_blocks(F, kSkinnyUW)),
+  TWELL_LAUNCH("gate_rows_skinny", (gate_rows_skinny<kSkinnyUW, kSkinnyB>),
+               dim3(skinny_blocks(F, kSkinnyUW), 1, kPassSplit),
                64 * kSkinnyWaves, 0, s, x, w, D, F, rows, n_ovf, cap, t, ovf_h);
   return hipGetLastError();
 }
@@ -163,7 +164,8 @@ hipError_t launch_dense_mfma(const FwdArgs& a, hipStream_t s) {
   uint16_t* zhi = a.zov;
   uint16_t* zlo = a.zov + (size_t)a.ovf_cap * Fz;
   const uint16_t* x = reinterpret_cast<const uint16_t*>(a.x);
-  TWELL_LAUNCH("dense_up_mfma", (dense_up_mfma<kSkinnyUW, kSkinnyB>), dim3(skinny_blocks(a.F, kSkinnyUW)),
+  TWELL_LAUNCH("dense_up_mfma", (dense_up_mfma<kSkinnyUW, kSkinnyB>),
+               dim3(skinny_blocks(a.F, kSkinnyUW), 1, kPassSplit),
                64 * kSkinnyWaves, 0, s, x, a.ovf_rows, a.n_ovf, a.ovf_cap, reinterpret_cast<const uint16_t*>(a.w_up),
                reinterpret_cast<const uint16_t*>(a.ovf_h), a.D, a.F, Fz, zhi, zlo);
   hipError_t err = hipGetLastError();

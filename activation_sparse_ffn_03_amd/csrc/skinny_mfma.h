@@ -14,6 +14,11 @@ constexpr int NF = kRowsPerPass / 16;
 constexpr int kSkinnyWaves = 4;   // waves per workgroup of the skinny NT kernels (independent)
 constexpr int kSkinnyUW = 1;      // 16-column groups per wave
 constexpr int kSkinnyB = 2;       // 32-element steps per batch of loads
+// Passes of kRowsPerPass rows go to kPassSplit workgroups per column group
+// (grid z; pass p to workgroup p % kPassSplit), so that above 64 rows the
+// passes stream their weights at the same time: a pass is bound by the
+// latency of its loads (one wave per SIMD), not by bandwidth.
+constexpr int kPassSplit = 2;
 
 // One wave: acc[f][u] = rows m0 + 16f + (0..15) (gathered through `rows`, zero
 // past n) times columns c0 + 16u + (0..15) of w, over all of d_model in
@@ -141,7 +146,7 @@ __device__ __forceinline__ void skinny_nn(const NnOperands<NP>& p, int n, int D,
   const int kq = 8 * (lane >> 4);                   // this lane's 8 rows of a 32-row block
   const int c_lo = g * kDenseChunk, c_hi = min(F, c_lo + kDenseChunk);
   const u32x4_t zero{0u, 0u, 0u, 0u};
-  for (int m0 = 0; m0 < n; m0 += kRowsPerPass) {
+  for (int m0 = blockIdx.z * kRowsPerPass; m0 < n; m0 += gridDim.z * kRowsPerPass) {
     size_t ro[NF];
     bool aok[NF];
 #pragma unroll
@@ -205,9 +210,10 @@ __device__ __forceinline__ void skinny_nn(const NnOperands<NP>& p, int n, int D,
 }
 
 // (workgroups of 4 waves over the 128-column tiles of d_model) x d_ff chunks
+// x the row-pass split
 inline dim3 skinny_nn_grid(int D, int G) {
   const int dtiles = D / kDownCols;
-  return dim3((unsigned)((dtiles + kDownWaves - 1) / kDownWaves), (unsigned)G);
+  return dim3((unsigned)((dtiles + kDownWaves - 1) / kDownWaves), (unsigned)G, (unsigned)kPassSplit);
 }
 
 }  // namespace skinny
