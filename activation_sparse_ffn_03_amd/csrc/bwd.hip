@@ -27,6 +27,7 @@
 //                 32 rows a bit mask per column, so each column lists its rows
 //                 ascending and every record is placed independently)
 //   bwd_dw        wave per (column, D-part): the three weight-gradient rows
+#include "block_scan.h"
 #include "row_ops.h"
 #include "twell_kernels.h"
 #include "twell_trace.h"
@@ -73,30 +74,6 @@ __device__ void block_exclusive_scan(int32_t* part, int tid) {
     part[tid] += v;
     __syncthreads();
   }
-}
-
-// Exclusive sum over the 1024 threads of the block of v (wave scans, then the
-// 16 wave totals through LDS); *total gets the block's sum.
-__device__ __forceinline__ int32_t block_excl_1024(int32_t v, int32_t* wsum, int32_t* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int32_t x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int32_t y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
-  if (lane == 63) wsum[wave] = x;
-  __syncthreads();
-  int32_t before = 0, all = 0;
-#pragma unroll
-  for (int w = 0; w < 16; ++w) {
-    const int32_t t = wsum[w];
-    before += w < wave ? t : 0;
-    all += t;
-  }
-  __syncthreads();
-  *total = all;
-  return before + x - v;
 }
 
 // Effective entry count of a row: row_nnz for ELL rows, the dense row's own
