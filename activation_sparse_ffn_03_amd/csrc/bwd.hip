@@ -28,6 +28,7 @@
 //                 ascending and every record is placed independently)
 //   bwd_dw        wave per (column, D-part): the three weight-gradient rows
 #include "block_scan.h"
+#include "ell_groups.h"
 #include "row_ops.h"
 #include "twell_kernels.h"
 #include "twell_trace.h"
@@ -81,7 +82,7 @@ __device__ void block_exclusive_scan(int32_t* part, int tid) {
 // workgroup; thread t owns rows [t*C, t*C + C), held in registers, so all of
 // a thread's loads are issued together.
 template <int C>
-__global__ __launch_bounds__(1024) void row_scan(BwdArgs a, const int32_t* dense_nnz) {
+__device__ __forceinline__ void row_scan_block(const BwdArgs& a, const int32_t* dense_nnz) {
   __shared__ int32_t wsum[16];
   const int tid = threadIdx.x;
   const int64_t N = a.N;
@@ -118,6 +119,25 @@ __global__ __launch_bounds__(1024) void row_scan(BwdArgs a, const int32_t* dense
     run += eff[k];
   }
   if (tid == 1023) a.ws.row_ptr[N] = tot;
+}
+
+template <int C>
+__global__ __launch_bounds__(1024) void row_scan(BwdArgs a, const int32_t* dense_nnz) {
+  row_scan_block<C>(a, dense_nnz);
+}
+
+// The row offsets (workgroup 0) and the blocked dz's per-row group positions
+// (the other workgroups, a wave per row, each XCD a contiguous run of rows)
+// in one launch: the two are independent, and the single-workgroup scan is
+// bound by the latency of its loads, so the group pass runs in its shadow.
+template <int C>
+__global__ __launch_bounds__(1024) void row_scan_groups(BwdArgs a, const int32_t* dense_nnz, int n_groups) {
+  if (blockIdx.x == 0) {
+    row_scan_block<C>(a, dense_nnz);
+    return;
+  }
+  const int64_t i = xcd_run_block(blockIdx.x - 1, gridDim.x - 1) * 16 + (threadIdx.x >> 6);
+  if (i < a.N) ell_groups_row(a, n_groups, i);
 }
 
 // The same for any N (beyond 32768 rows): thread t walks rows
@@ -645,14 +665,32 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t s) {
   if (a.dense_cap > 0) {
     TWELL_LAUNCH("dense_groups", dense_groups<TS>, dim3((a.dense_cap + 3) / 4), blk, 0, s, a, G, dense_nnz);
   }
-  switch (row_scan_rows(a.N)) {
-    case 1: TWELL_LAUNCH("row_scan", row_scan<1>, 1, 1024, 0, s, a, dense_nnz); break;
-    case 2: TWELL_LAUNCH("row_scan", row_scan<2>, 1, 1024, 0, s, a, dense_nnz); break;
-    case 4: TWELL_LAUNCH("row_scan", row_scan<4>, 1, 1024, 0, s, a, dense_nnz); break;
-    case 8: TWELL_LAUNCH("row_scan", row_scan<8>, 1, 1024, 0, s, a, dense_nnz); break;
-    case 16: TWELL_LAUNCH("row_scan", row_scan<16>, 1, 1024, 0, s, a, dense_nnz); break;
-    case 32: TWELL_LAUNCH("row_scan", row_scan<32>, 1, 1024, 0, s, a, dense_nnz); break;
-    default: TWELL_LAUNCH("row_scan", row_scan_any, 1, 1024, 0, s, a, dense_nnz); break;
+  // with the blocked dz, its per-row group positions ride along with the row
+  // offsets (one launch: 1 + one workgroup per 16 rows)
+  const bool dz_blocked = sizeof(TS) == 2 && dz_blocked_applies(a);
+  const int rs = row_scan_rows(a.N);
+  const bool fused = dz_blocked && rs <= 32;
+  if (fused) {
+    const int ng = dz_groups(a.F);
+    const dim3 gg((unsigned)(1 + (a.N + 15) / 16));
+    switch (rs) {
+      case 1: TWELL_LAUNCH("row_scan_groups", row_scan_groups<1>, gg, 1024, 0, s, a, dense_nnz, ng); break;
+      case 2: TWELL_LAUNCH("row_scan_groups", row_scan_groups<2>, gg, 1024, 0, s, a, dense_nnz, ng); break;
+      case 4: TWELL_LAUNCH("row_scan_groups", row_scan_groups<4>, gg, 1024, 0, s, a, dense_nnz, ng); break;
+      case 8: TWELL_LAUNCH("row_scan_groups", row_scan_groups<8>, gg, 1024, 0, s, a, dense_nnz, ng); break;
+      case 16: TWELL_LAUNCH("row_scan_groups", row_scan_groups<16>, gg, 1024, 0, s, a, dense_nnz, ng); break;
+      default: TWELL_LAUNCH("row_scan_groups", row_scan_groups<32>, gg, 1024, 0, s, a, dense_nnz, ng); break;
+    }
+  } else {
+    switch (rs) {
+      case 1: TWELL_LAUNCH("row_scan", row_scan<1>, 1, 1024, 0, s, a, dense_nnz); break;
+      case 2: TWELL_LAUNCH("row_scan", row_scan<2>, 1, 1024, 0, s, a, dense_nnz); break;
+      case 4: TWELL_LAUNCH("row_scan", row_scan<4>, 1, 1024, 0, s, a, dense_nnz); break;
+      case 8: TWELL_LAUNCH("row_scan", row_scan<8>, 1, 1024, 0, s, a, dense_nnz); break;
+      case 16: TWELL_LAUNCH("row_scan", row_scan<16>, 1, 1024, 0, s, a, dense_nnz); break;
+      case 32: TWELL_LAUNCH("row_scan", row_scan<32>, 1, 1024, 0, s, a, dense_nnz); break;
+      default: TWELL_LAUNCH("row_scan", row_scan_any, 1, 1024, 0, s, a, dense_nnz); break;
+    }
   }
 
   // dz records: ELL rows by column part (main stream), dense rows by column
@@ -691,8 +729,8 @@ hipError_t launch_t(const BwdArgs& a, hipStream_t s) {
   }
   const int parts = 8;
   const dim3 gdz((unsigned)(((a.N + 3) / 4) * parts));
-  if (sizeof(TS) == 2 && dz_blocked_applies(a)) {
-    err = launch_dz_blocked(a, s);
+  if (dz_blocked) {
+    err = launch_dz_blocked(a, s, fused);
   } else {
   switch (M) {
     case 1: TWELL_LAUNCH("bwd_dz_ell", (bwd_dz_ell<TS, 1>), gdz, blk, 0, s, a, parts); break;

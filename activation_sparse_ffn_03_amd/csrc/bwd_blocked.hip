@@ -14,6 +14,7 @@
 // position, as bwd_dz_ell does: column and (z, da, dg) = (h*a, dz*h,
 // dz*a + lambda).
 #include "blocked_sddmm.h"
+#include "ell_groups.h"
 #include "twell_host.h"
 #include "twell_kernels.h"
 #include "twell_trace.h"
@@ -24,31 +25,11 @@ namespace {
 constexpr int kGroupCols = blk::kGroupCols;
 constexpr int kMaxGroups = 64;  // d_ff up to 32768
 
-// Wave per row (lane = ELL position), each XCD a contiguous run of rows (the
-// [.][N] arrays' lines stay in one L2): egrp[g][i] = ELL position of the first
-// entry of row i with column >= g * 512, for g = 0 .. n_groups (0 everywhere
-// for dense rows). Entry k writes the groups after its predecessor's up to
-// its own; the first position past the row's end writes the rest, so every
-// egrp value is written exactly once.
+// Wave per row, 4 rows per workgroup, each XCD a contiguous run of rows (the
+// [.][N] arrays' lines stay in one L2).
 __global__ __launch_bounds__(256) void ell_groups(BwdArgs a, int n_groups) {
-  const int lane = threadIdx.x & 63;
   const int64_t i = xcd_run_block(blockIdx.x, gridDim.x) * 4 + (threadIdx.x >> 6);
-  const int64_t N = a.N;
-  if (i >= N) return;
-  const int n = a.is_dense[i] ? 0 : min(a.row_nnz[i], a.row_cap);
-  int32_t* eg = a.ws.egrp + i;  // row g at eg[g * N]
-  int prev_last = -1;           // group of position kb - 1
-  for (int kb = 0; kb <= n; kb += 64) {
-    const int k = kb + lane;
-    // group of position k; positions at or past the end count as group n_groups
-    const int cur = k < n ? (int)min((unsigned)a.ell_cols[(size_t)k * N + i] / kGroupCols, (unsigned)n_groups - 1)
-                          : n_groups;
-    int prev = __shfl_up(cur, 1, 64);
-    if (lane == 0) prev = prev_last;
-    if (k <= n)
-      for (int g = prev + 1; g <= cur; ++g) eg[(size_t)g * N] = k;
-    prev_last = __shfl(cur, 63, 64);
-  }
+  if (i < a.N) ell_groups_row(a, n_groups, i);
 }
 
 // The backward's pattern: the ELL entries of the ELL rows; records at
@@ -97,12 +78,14 @@ bool dz_blocked_applies(const BwdArgs& a) {
          a.ws.egrp != nullptr && pairs >= blk::kCus;
 }
 
-hipError_t launch_dz_blocked(const BwdArgs& a, hipStream_t s) {
+hipError_t launch_dz_blocked(const BwdArgs& a, hipStream_t s, bool groups_done) {
   if (!dz_blocked_applies(a)) return hipErrorInvalidValue;
   const int n_groups = dz_groups(a.F);
-  TWELL_LAUNCH("ell_groups", ell_groups, dim3((unsigned)((a.N + 3) / 4)), 256, 0, s, a, n_groups);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  if (!groups_done) {
+    TWELL_LAUNCH("ell_groups", ell_groups, dim3((unsigned)((a.N + 3) / 4)), 256, 0, s, a, n_groups);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
   const int64_t ntb = (a.N + DzBlk::T - 1) / DzBlk::T;
   TWELL_LAUNCH("bwd_dz_blocked", bwd_dz_blocked, dim3((unsigned)blk::grid_blocks(ntb, n_groups)), DzBlk::NT, 0, s, a,
                n_groups, ntb);

@@ -206,10 +206,11 @@ struct BwdArgs {
 
 hipError_t launch_ffn_bwd(const BwdArgs& a, hipStream_t s);
 // dz records of the ELL rows with weight-row reuse through LDS
-// (bwd_blocked.hip): the per-row group positions, then the blocked product.
+// (bwd_blocked.hip): the per-row group positions (unless groups_done: the
+// caller's row-offset launch wrote them), then the blocked product.
 int dz_groups(int F);
 bool dz_blocked_applies(const BwdArgs& a);
-hipError_t launch_dz_blocked(const BwdArgs& a, hipStream_t s);
+hipError_t launch_dz_blocked(const BwdArgs& a, hipStream_t s, bool groups_done);
 // Dense-backup rows as skinny MFMA products (bwd_dense.hip): dz and a, then
 // their records and da / dg; then dx of those rows (bwd_dx skips them).
 bool bwd_dense_mfma_applies(const BwdArgs& a);
