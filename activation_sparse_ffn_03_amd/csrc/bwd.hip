@@ -14,7 +14,9 @@
 // Pipeline (all deterministic, no floating-point atomics):
 //   dense_groups  per dense row: active count per column chunk -> offsets
 //   row_scan      CSR offsets of every row's entries (one workgroup, rows
-//                 held in registers)
+//                 held in registers); with the blocked dz, row_scan_groups
+//                 runs it in workgroup 0 and the dz's per-row group
+//                 positions (ell_groups.h) in the others
 //   bwd_dz_ell    wave per ELL row and column part: dz, da, dg, z; writes
 //                 each entry's column and (z, da, dg) in CSR order (bf16
 //                 batches take the blocked form of bwd_blocked.hip instead)
