@@ -49,6 +49,36 @@ __global__ __launch_bounds__(256) void dense_groups(BwdArgs a, int G, int32_t* d
   if (o >= a.dense_cap || o >= *a.n_dense) return;
   const TS* h = reinterpret_cast<const TS*>(a.dense_h) + (size_t)o * a.F;
   int run = 0;
+  if constexpr (sizeof(TS) == 2) {
+    if ((a.F & 7) == 0 && (reinterpret_cast<uintptr_t>(a.dense_h) & 15) == 0) {
+      // a 512-column chunk is one 16-byte load per lane (lane l: columns
+      // 8l .. 8l+7), eight chunks in flight; a bf16 h is active iff its bits
+      // are in [1, 0x7fff] (positive, not zero)
+      const uint4* hv = reinterpret_cast<const uint4*>(h);
+      const int nv = a.F / 8;
+      for (int g0 = 0; g0 < G; g0 += 8) {
+        uint4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int q = (g0 + u) * 64 + lane;
+          v[u] = q < nv ? hv[q] : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (g0 + u >= G) break;
+          if (lane == 0) a.ws.grp_off[(size_t)o * G + g0 + u] = run;
+          int cnt = 0;
+          const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            cnt += ((w[e] & 0xffffu) - 1u < 0x7fffu) + ((w[e] >> 16) - 1u < 0x7fffu);
+          run += (int)wave_sum_dpp((float)cnt);  // exact: at most 512
+        }
+      }
+      if (lane == 0) dense_nnz[o] = run;
+      return;
+    }
+  }
 #pragma unroll 2
   for (int g = 0; g < G; ++g) {
     if (lane == 0) a.ws.grp_off[(size_t)o * G + g] = run;
