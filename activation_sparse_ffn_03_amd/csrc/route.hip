@@ -18,8 +18,10 @@
 //                  row_nnz, is_dense, and the ELL entries of ELL rows (vals,
 //                  global cols, saved a).
 //   launch_compact ascending dense-row list + capacity status.
-//   route_dense_h  thread per (dense row, column): dense activation rows,
-//                  rebuilt from TwELL slots or copied from the overflow rows.
+//   route_dense_h  dense activation rows, rebuilt from TwELL slots or copied
+//                  from the overflow rows: for bf16 rows up to 32768 columns
+//                  a workgroup per row building it in LDS, else a thread per
+//                  (dense row, column).
 #include "twell_device.h"
 #include "twell_kernels.h"
 #include "twell_trace.h"
@@ -142,6 +144,48 @@ __global__ __launch_bounds__(256) void route_dense_h(RouteArgs a) {
   out[c] = h;
 }
 
+// The same, a workgroup per dense row for bf16 rows up to 32768 columns: the
+// row is built in LDS (zeroed, then every TwELL slot of the row's tiles
+// scattered to its column, at most one slot per column) and written out
+// coalesced, so each slot is read once instead of once per column of its
+// tile; an overflowed row is copied from its overflow row.
+constexpr int kDenseHLdsCols = 32768;
+__global__ __launch_bounds__(1024) void route_dense_h_lds(RouteArgs a) {
+  extern __shared__ uint16_t hrow[];  // [F]
+  const int o = blockIdx.x;
+  if (o >= a.dense_cap || o >= *a.n_dense) return;  // uniform: no barrier skipped within a workgroup
+  const int64_t N = a.N;
+  const int F = a.F, tid = threadIdx.x;
+  const int64_t i = a.dense_rows[o];
+  uint16_t* out = reinterpret_cast<uint16_t*>(a.dense_h) + (size_t)o * F;
+  if (a.ovf_flag[i]) {
+    const int n = min(*a.n_ovf, a.ovf_cap);
+    int lo = 0, hi = n;  // first position with ovf_rows[pos] >= i
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (a.ovf_rows[mid] < i) lo = mid + 1; else hi = mid;
+    }
+    const bool found = lo < n && a.ovf_rows[lo] == i;
+    const uint16_t* src = reinterpret_cast<const uint16_t*>(a.ovf_h) + (size_t)(found ? lo : 0) * F;
+    for (int c = tid; c < F; c += 1024) out[c] = found ? src[c] : uint16_t(0);
+    return;
+  }
+  for (int c = tid; c < F; c += 1024) hrow[c] = 0;
+  __syncthreads();
+  const uint16_t* vals = reinterpret_cast<const uint16_t*>(a.vals);
+  const int items = a.n_tiles * a.slots;  // (tile, slot) pairs of the row
+  for (int q = tid; q < items; q += 1024) {
+    const int j = q / a.slots, sl = q - j * a.slots;
+    if (sl < min((int)a.counts[(size_t)j * N + i], a.slots)) {
+      const size_t src = ((size_t)j * a.slots + sl) * N + i;
+      const int c = j * a.tile_n + a.cols[src];
+      if (c < F) hrow[c] = vals[src];
+    }
+  }
+  __syncthreads();
+  for (int c = tid; c < F; c += 1024) out[c] = hrow[c];
+}
+
 template <typename TS>
 hipError_t launch_t(const RouteArgs& a, hipStream_t s) {
   TWELL_LAUNCH("route_rows", route_rows<TS>, dim3((unsigned)((a.N + 15) / 16)), 1024, 0, s, a);
@@ -149,7 +193,11 @@ hipError_t launch_t(const RouteArgs& a, hipStream_t s) {
   if (err != hipSuccess) return err;
   err = launch_compact(a.is_dense, a.N, a.dense_rows, a.dense_cap, a.n_dense, a.status, 2u /*TWELL_DEV_DENSE_CAPACITY*/, s);
   if (err != hipSuccess || a.dense_cap == 0) return err;
-  TWELL_LAUNCH("route_dense_h", route_dense_h<TS>, dim3((unsigned)(((a.F + 255) / 256) * (int64_t)a.dense_cap)), 256, 0, s, a);
+  if (sizeof(TS) == 2 && a.F <= kDenseHLdsCols)
+    TWELL_LAUNCH("route_dense_h", route_dense_h_lds, dim3((unsigned)a.dense_cap), 1024, (size_t)a.F * 2, s, a);
+  else
+    TWELL_LAUNCH("route_dense_h", route_dense_h<TS>, dim3((unsigned)(((a.F + 255) / 256) * (int64_t)a.dense_cap)), 256,
+                 0, s, a);
   return hipGetLastError();
 }
 
